@@ -1,0 +1,29 @@
+"""CPU oracle for the dual-flow decode step -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously correct fp64 implementation of what the decode path
+computes, written from the pages' description of the Dual-Flow Transformer
+(Sintesi Tecnica: Dual-Flow Transformers, sections "Architettura Core",
+"Meccanismi Chiave" and "Costi di Inferenza vs. Addestramento").
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg
+may import this package. It shares no code with the HIP library: no kernels,
+headers, helpers or tables. Its inputs are numpy arrays (bf16 given as uint16
+bit patterns); every value is widened exactly to fp64 before any arithmetic.
+
+Functions and their pins (tests/test_oracle_*.py):
+  numerics.round_bf16       -- torch's bf16 cast on fp32-exact inputs; hand-derived
+                               bit patterns for ties, double-rounding cases, overflow
+  attention.decode_attention -- scalar brute force (attention.brute_force), torch
+                               SDPA per flow, Q2 = Q1 identities, one-token cache,
+                               closed forms, LSE partition merge, paging invariance
+  linear.grouped_linear      -- torch.nn.functional.linear per flow, flow independence
+  linear.rmsnorm             -- torch.nn.functional.rms_norm
+  linear.swiglu_couple       -- torch.nn.functional.silu; b = -1 / b = 0 identities
+  cache.kv_append            -- hand-computed slot addresses, bit patterns
+  layer.dual_flow_layer      -- textbook pre-norm decoder layer in torch.nn.functional
+                               (primary flow), aux = primary identities, cache diff
+The placement of the b and c coupling vectors is a reading of the pages (they
+name the levels, not the formula); it is pinned only by the identities above:
+"parity unpinned" beyond this reading.
+"""
+from . import numerics, attention, linear, cache, layer  # noqa: F401
