@@ -1,0 +1,280 @@
+"""Benchmark of the dual-flow decode step on one MI355X.
+
+python bench.py [--steps K] [--warmup W] [--workload layer|attn-b16|attn-ragged|attn-long|attn-fp32]
+
+A step of the default workload is one full dual-flow decode layer (both flows, batch
+32, context 8192, hidden 4096, 32/8 heads x 128, SwiGLU 14336, paged bf16 cache of
+16-token blocks): RMSNorm, grouped Wqkv, primary K/V append, dual-query attention,
+grouped Wo + residual, RMSNorm, grouped gate/up, SwiGLU + b coupling, grouped down +
+c coupling + residual. Inputs are seeded synthetic tensors already resident in HBM.
+Prints one JSON line; `value` is decode steps/s (one layer step = one generated
+position for all 32 sequences of both flows).
+
+Also measured in the same run: the dominant kernel (the dual-query attention call)
+timed with HIP events on the stream it runs on, its algorithmic HBM bytes, and the
+CPU oracle timed on the host cores (a reported baseline, not a target).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="layer",
+                   choices=["layer", "attn-b16", "attn-ragged", "attn-long", "attn-fp32"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--splits", type=int, default=0, help="attention context splits (0 = plan)")
+    p.add_argument("--kernel-reps", type=int, default=20)
+    return p.parse_args()
+
+
+def dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def attn_bytes(case_like, ctx, F, q_bytes):
+    """Algorithmic HBM bytes of one dual-query attention call: every attended K and V
+    row once, the query rows (q1, q2), the coupling vector, the outputs and LSE, the
+    context lengths and the block-table entries that are read."""
+    import numpy as np
+    Hkv, D, Hq, B = case_like["Hkv"], case_like["D"], case_like["Hq"], case_like["B"]
+    el = case_like["kv_el"]
+    tot = int(np.sum(ctx))
+    kv = 2 * tot * Hkv * D * el
+    q = F * B * Hq * D * q_bytes
+    a = D * 4
+    out = F * B * Hq * D * 4 + F * B * Hq * 4
+    table = int(np.sum(-(-np.asarray(ctx) // case_like["bs"]))) * 4 if case_like["paged"] else 0
+    return kv + q + a + out + B * 4 + table
+
+
+def timed(fn, reps, stream):
+    """Average duration (ms) of fn() over reps launches, HIP events on `stream`."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        fn()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(reps):
+            fn()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def source_sha(name):
+    path = os.path.join(ROOT, "dual_flow_shared_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_file, workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(kernel_file):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import dfx_inputs as gen
+    import dual_flow_shared_amd as dfx
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    extra = {}
+
+    if args.workload == "layer":
+        c = gen.config_layer()
+        B, F, H = c.batch, 2, c.hidden
+        kv = dfx.KVCache(dev(c.cache.k_pool), dev(c.cache.v_pool), dev(c.cache.block_table))
+        w = dfx.LayerWeights(dev(c.g_attn), dev(c.w_qkv), dev(c.w_o), dev(c.g_mlp), dev(c.w_gate_up),
+                             dev(c.w_down), c.num_q_heads, c.num_kv_heads, c.head_dim, c.eps,
+                             dev(c.a), dev(c.b), dev(c.c))
+        ctx_np = c.cache.context_lens + 1
+        ctx = dev(ctx_np)
+        max_ctx = int(ctx_np.max())
+        x0 = dev(c.x.copy())
+        x = x0.clone()
+        ws = dfx.Workspace()
+
+        def step():
+            dfx.dual_flow_decode_layer(x, w, kv, ctx, max_ctx, workspace=ws)
+
+        # dominant kernel: the attention call of the layer, on the same cache, queries taken
+        # from a Wqkv-shaped fp32 buffer (row stride 6144) as inside the layer
+        Nqkv = (c.num_q_heads + 2 * c.num_kv_heads) * c.head_dim
+        qkv = torch.randn(F, B, Nqkv, device="cuda", dtype=torch.float32)
+        q1 = qkv[0, :, : c.num_q_heads * c.head_dim].view(B, c.num_q_heads, c.head_dim)
+        q2 = qkv[1, :, : c.num_q_heads * c.head_dim].view(B, c.num_q_heads, c.head_dim)
+        a = dev(c.a)
+        aws = dfx.Workspace()
+        shape = dict(Hkv=c.num_kv_heads, D=c.head_dim, Hq=c.num_q_heads, B=B, kv_el=2, bs=16, paged=True)
+        weights_bytes = 2 * (c.w_qkv.size + c.w_o.size + c.w_gate_up.size + c.w_down.size)
+        step_bytes = (weights_bytes + attn_bytes(shape, ctx_np, F, 4)
+                      + 2 * B * c.num_kv_heads * c.head_dim * 2      # appended K/V rows
+                      + 2 * F * B * H * 4                            # residual rows in and out
+                      + 4 * (2 * H + c.head_dim + c.intermediate + H))  # gains, a, b, c
+        workload = (f"dual-flow decode layer: batch {B} x context {max_ctx}, hidden {H}, "
+                    f"{c.num_q_heads}/{c.num_kv_heads} heads x {c.head_dim}, SwiGLU {c.intermediate}, "
+                    f"paged bf16 KV (16-token blocks), both flows")
+        cfg = {"workload": workload, "batch": B, "context": max_ctx, "hidden": H,
+               "q_heads": c.num_q_heads, "kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
+               "intermediate": c.intermediate, "flows": F, "kv_block": 16}
+        attn_ctx = (ctx, max_ctx)
+    else:
+        idx = {"attn-fp32": 1, "attn-b16": 2, "attn-ragged": 3, "attn-long": 4}[args.workload]
+        case = gen.config_attention(idx)
+        B, F = case.batch, 2
+        kv = dfx.KVCache(dev(case.k_pool), dev(case.v_pool),
+                         None if case.block_table is None else dev(case.block_table))
+        ctx_np = case.context_lens
+        ctx = dev(ctx_np)
+        max_ctx = int(ctx_np.max())
+        q1, q2, a = dev(case.q1), dev(case.q2), dev(case.a)
+        aws = dfx.Workspace()
+        el = 4 if case.dtype == "f32" else 2
+        shape = dict(Hkv=case.num_kv_heads, D=case.head_dim, Hq=case.num_q_heads, B=B, kv_el=el,
+                     bs=case.block_size, paged=case.paged)
+        step_bytes = attn_bytes(shape, ctx_np, F, el)
+
+        def step():
+            dfx.decode_attn(q1, q2, a, cache=kv, context_lens=ctx, max_context=max_ctx,
+                            num_splits=args.splits, workspace=aws)
+
+        workload = (f"dual-query decode attention: batch {B}, {case.num_q_heads}/{case.num_kv_heads} heads x "
+                    f"{case.head_dim}, context {'ragged' if idx == 3 else max_ctx}, "
+                    f"{'paged' if case.paged else 'contiguous'} {case.dtype} KV")
+        cfg = {"workload": workload, "batch": B, "context_max": max_ctx, "context_sum": int(ctx_np.sum()),
+               "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
+               "flows": F, "dtype": case.dtype}
+        attn_ctx = (ctx, max_ctx)
+
+    # ---- timed steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    steps_per_s = 1000.0 / ms
+
+    # ---- dominant kernel: dual-query attention, events on its stream
+    ctx_t, mc = attn_ctx
+
+    def attn_call(q2_=q2, a_=a):
+        dfx.decode_attn(q1, q2_, a_, cache=kv, context_lens=ctx_t, max_context=mc,
+                        num_splits=args.splits, want_lse=False, workspace=aws)
+
+    attn_ms = timed(attn_call, args.kernel_reps, stream)
+    single_ms = timed(lambda: attn_call(None, None), args.kernel_reps, stream)
+    abytes = attn_bytes(shape, ctx_np, F, 4 if args.workload == "layer" else shape["kv_el"])
+    achieved = abytes / (attn_ms * 1e-3) / 1e9
+    splits, _ = dfx.decode_attn_plan(kv, B, shape["Hq"], F, mc, args.splits)
+    extra.update({"attn_ms": round(attn_ms, 4), "attn_single_flow_ms": round(single_ms, 4),
+                  "dual_single_ratio": round(attn_ms / single_ms, 3), "attn_splits": splits,
+                  "step_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                  "step_bytes": int(step_bytes), "wall_s": round(wall, 3)})
+
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_from_profiles("attn_mfma.hip", args.workload),
+                "kernel": "dfx_decode_attn (attn_mfma_kernel + attn_merge_kernel)",
+                "bytes_per_launch": int(abytes)}
+
+    # ---- CPU oracle on the host cores (reported baseline only)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, locals())
+
+    line = {"metric": "dual-flow decode attn HBM GB/s (% of peak) and decode steps/s at batch x ctx",
+            "value": round(steps_per_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": cfg, "roofline": roofline, "cpu_baseline": cpu, **extra}
+    print(json.dumps(line))
+
+
+def cpu_baseline(workload, env):
+    """Time the oracle (fp64 numpy, as it stands) on a bounded sample of the workload and
+    scale to steps/s of the full workload."""
+    import numpy as np
+    from oracle.attention import decode_attention
+    from oracle.layer import dual_flow_layer
+    if workload == "layer":
+        c = env["c"]
+        kv = c.cache
+        times = []
+        while len(times) < 5 and sum(times) < 10.0:
+            t0 = time.perf_counter()
+            dual_flow_layer(c.x, c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.a, c.b,
+                            c.c, c.eps, kv.k_pool, kv.v_pool, kv.block_table, kv.context_lens,
+                            c.num_q_heads, c.num_kv_heads, c.head_dim)
+            times.append(time.perf_counter() - t0)
+        full = float(np.median(times))
+        sample = (f"the whole layer step (all {c.batch} sequences, both flows), median of "
+                  f"{len(times)} runs, {sum(times):.1f} s in total")
+    else:
+        case = env["case"]
+        seqs = case.batch if case.batch * int(np.max(case.context_lens)) <= 16 * 4096 else 2
+        t0 = time.perf_counter()
+        decode_attention(case.q1, case.q2, case.a, case.a_head_stride, case.k_pool, case.v_pool,
+                         case.block_table, case.context_lens, batches=list(range(seqs)))
+        t = time.perf_counter() - t0
+        share = float(np.sum(case.context_lens[:seqs])) / float(np.sum(case.context_lens))
+        full = t / share
+        sample = (f"oracle attention on {seqs} of {case.batch} sequences ({t:.1f} s), scaled by "
+                  f"their share of the context tokens")
+    return {"value": round(1.0 / full, 4), "unit": "steps/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": sample}
+
+
+if __name__ == "__main__":
+    main()

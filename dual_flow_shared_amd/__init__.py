@@ -1,0 +1,283 @@
+"""dual_flow_shared_amd -- the dual-flow decode step on MI355X (gfx950).
+
+Thin torch-facing binding of libdfx.so (include/dfx.h): it checks shapes and dtypes,
+passes device pointers and the current HIP stream, and returns torch tensors. Every
+step of the path runs in the library's HIP kernels; torch only holds device memory.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from ._abi import (DFX_BF16, DFX_F32, DfxError, KVCacheStruct, LayerWeightsStruct, check, lib)
+
+__all__ = ["DfxError", "KVCache", "LayerWeights", "decode_attn", "decode_attn_plan",
+           "kv_append_primary", "grouped_linear", "rmsnorm", "swiglu_couple",
+           "dual_flow_decode_layer", "layer_workspace_size", "copy_bytes", "fill_bytes",
+           "Workspace", "version"]
+
+
+def version() -> int:
+    return lib().dfx_version()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the HIP library must live on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DFX_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return DFX_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _contig(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+class Workspace:
+    """A zero-filled device byte buffer grown on demand (the library's split-K counters
+    need zero on first use and leave it zero after each call)."""
+
+    def __init__(self, device=None):
+        self.device = torch.device("cuda") if device is None else torch.device(device)
+        self.buf = torch.zeros(0, dtype=torch.uint8, device=self.device)
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(ws: Optional[Workspace], device, purpose: str) -> Workspace:
+    """Default workspaces are kept per device and per purpose: split-K counters of the
+    linear and layer calls must not share memory with attention partials."""
+    if ws is not None:
+        return ws
+    d = torch.device(device)
+    key = (d.index if d.index is not None else torch.cuda.current_device(), purpose)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(torch.device("cuda", key[0]))
+    return _default_ws[key]
+
+
+@dataclass
+class KVCache:
+    """The primary flow's persistent K/V pool [num_blocks][Hkv][block_size][D]
+    (bfloat16 or float32) with an optional int32 block table [batch][max_blocks]."""
+    k: torch.Tensor
+    v: torch.Tensor
+    block_table: Optional[torch.Tensor] = None
+
+    def struct(self) -> KVCacheStruct:
+        k, v = _contig(self.k, "k"), _contig(self.v, "v")
+        if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
+            raise ValueError("k and v must be equal-shaped [blocks][Hkv][block_size][D] tensors")
+        s = KVCacheStruct()
+        s.dtype = _dtype_code(k)
+        s.num_blocks, s.num_kv_heads, s.block_size, s.head_dim = k.shape
+        s.k, s.v = k.data_ptr(), v.data_ptr()
+        if self.block_table is not None:
+            bt = _contig(self.block_table, "block_table")
+            if bt.dtype != torch.int32 or bt.dim() != 2:
+                raise ValueError("block_table must be int32 [batch][max_blocks]")
+            s.block_table, s.max_blocks_per_seq = bt.data_ptr(), bt.shape[1]
+        else:
+            s.block_table, s.max_blocks_per_seq = None, 0
+        s.reserved = 0
+        return s
+
+    @property
+    def capacity(self) -> int:
+        bs = self.k.shape[2]
+        return bs * self.block_table.shape[1] if self.block_table is not None else bs
+
+
+def decode_attn_plan(cache: KVCache, batch: int, num_q_heads: int, n_flows: int, max_context: int,
+                     num_splits: int = 0):
+    s = ctypes.c_int32()
+    n = ctypes.c_size_t()
+    st = cache.struct()
+    check(lib().dfx_decode_attn_plan(ctypes.byref(st), batch, num_q_heads, n_flows, max_context,
+                                     num_splits, ctypes.byref(s), ctypes.byref(n)))
+    return s.value, n.value
+
+
+def decode_attn(q1: torch.Tensor, q2_raw: Optional[torch.Tensor] = None, a: Optional[torch.Tensor] = None,
+                *, cache: KVCache, context_lens: torch.Tensor, max_context: int, num_splits: int = 0,
+                softmax_scale: float = 0.0, want_lse: bool = True, out=None,
+                workspace: Optional[Workspace] = None, stream=None):
+    """Dual-query decode attention (dfx_decode_attn). q1, q2_raw: [B][Hq][D] (rows may be
+    strided: the batch stride is taken from the tensor). a: fp32 [D] or [Hq][D].
+    Returns (o1, o2 or None, lse [F][B][Hq] or None)."""
+    B, Hq, D = q1.shape
+    if q1.stride(2) != 1 or q1.stride(1) != D:
+        raise ValueError("q1 rows must be [Hq][D] contiguous within a sequence")
+    if q2_raw is not None and (q2_raw.shape != q1.shape or q2_raw.stride() != q1.stride()
+                               or q2_raw.dtype != q1.dtype):
+        raise ValueError("q2_raw must match q1 in shape, strides and dtype")
+    F = 1 if q2_raw is None else 2
+    if context_lens.dtype != torch.int32 or context_lens.numel() != B:
+        raise ValueError("context_lens must be int32 [batch]")
+    a_stride = 0
+    if a is not None:
+        if a.dtype != torch.float32:
+            raise TypeError("a must be float32")
+        a = _contig(a, "a")
+        a_stride = 0 if a.numel() == D else D
+        if a.numel() not in (D, Hq * D):
+            raise ValueError("a must be [D] or [Hq][D]")
+    dev = q1.device
+    if out is None:
+        o1 = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+        o2 = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if F == 2 else None
+    else:
+        o1, o2 = out
+    lse = torch.empty(F, B, Hq, dtype=torch.float32, device=dev) if want_lse else None
+    if cache.block_table is not None and cache.block_table.shape[0] < B:
+        raise ValueError("block_table has fewer rows than the batch")
+    st = cache.struct()
+    splits, need = decode_attn_plan(cache, B, Hq, F, max_context, num_splits)
+    ws = _workspace(workspace, dev, "attn").get(need) if need else None
+    check(lib().dfx_decode_attn(ctypes.byref(st), _ptr(context_lens), B, max_context, Hq, _dtype_code(q1),
+                                _ptr(q1), _ptr(q2_raw), q1.stride(0), _ptr(a), a_stride,
+                                float(softmax_scale), _ptr(o1), _ptr(o2), _ptr(lse), num_splits,
+                                _ptr(ws), need, _stream(stream)))
+    return o1, o2, lse
+
+
+def kv_append_primary(cache: KVCache, positions: torch.Tensor, k_new: torch.Tensor,
+                      v_new: torch.Tensor, stream=None) -> None:
+    """Write the primary rows k_new, v_new ([B][Hkv*D], row stride from the tensor) at
+    positions[b] (dfx_kv_append_primary)."""
+    B = positions.numel()
+    if positions.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    if k_new.stride() != v_new.stride() or k_new.dtype != v_new.dtype or k_new.stride(-1) != 1:
+        raise ValueError("k_new and v_new must share dtype and row-major strides")
+    st = cache.struct()
+    check(lib().dfx_kv_append_primary(ctypes.byref(st), B, _ptr(positions), _dtype_code(k_new),
+                                      _ptr(k_new), _ptr(v_new), k_new.stride(0), _stream(stream)))
+
+
+def grouped_linear(x: torch.Tensor, w: torch.Tensor, *, y_dtype=torch.float32,
+                   couple: Optional[torch.Tensor] = None, residual: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None,
+                   stream=None) -> torch.Tensor:
+    """Y[f] = bf16(X[f]) W^T (+ couple, + residual) for x [F][rows][K], w bf16 [N][K]."""
+    F, rows, K = x.shape
+    N = w.shape[0]
+    x, w = _contig(x, "x"), _contig(w, "w")
+    if w.shape[1] != K:
+        raise ValueError("w must be [N][K]")
+    y = out if out is not None else torch.empty(F, rows, N, dtype=y_dtype, device=x.device)
+    n = ctypes.c_size_t()
+    check(lib().dfx_grouped_linear_workspace_size(F, rows, K, N, ctypes.byref(n)))
+    ws = _workspace(workspace, x.device, "linear").get(n.value) if n.value else None
+    check(lib().dfx_grouped_linear(F, rows, K, N, _dtype_code(x), _ptr(x), _ptr(w), _dtype_code(y),
+                                   _ptr(y), _ptr(couple), _ptr(residual), _ptr(ws), n.value,
+                                   _stream(stream)))
+    return y
+
+
+def rmsnorm(x: torch.Tensor, gain: torch.Tensor, eps: float, out=None, stream=None) -> torch.Tensor:
+    x = _contig(x, "x")
+    dim = x.shape[-1]
+    rows = x.numel() // dim
+    y = out if out is not None else torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    check(lib().dfx_rmsnorm(rows, dim, _ptr(x), _ptr(gain), float(eps), _ptr(y), _stream(stream)))
+    return y
+
+
+def swiglu_couple(gate_up: torch.Tensor, b: Optional[torch.Tensor] = None, out=None,
+                  stream=None) -> torch.Tensor:
+    gate_up = _contig(gate_up, "gate_up")
+    F, rows, two_i = gate_up.shape
+    y = out if out is not None else torch.empty(F, rows, two_i // 2, dtype=torch.bfloat16,
+                                                device=gate_up.device)
+    check(lib().dfx_swiglu_couple(F, rows, two_i // 2, _ptr(gate_up), _ptr(b), _ptr(y), _stream(stream)))
+    return y
+
+
+@dataclass
+class LayerWeights:
+    """Device weights of one dual-flow layer (matrices bf16 [out][in], vectors fp32)."""
+    attn_norm_gain: torch.Tensor
+    w_qkv: torch.Tensor
+    w_o: torch.Tensor
+    mlp_norm_gain: torch.Tensor
+    w_gate_up: torch.Tensor
+    w_down: torch.Tensor
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    eps: float = 1e-5
+    couple_a: Optional[torch.Tensor] = None
+    couple_b: Optional[torch.Tensor] = None
+    couple_c: Optional[torch.Tensor] = None
+
+    def struct(self) -> LayerWeightsStruct:
+        s = LayerWeightsStruct()
+        s.hidden = self.w_qkv.shape[1]
+        s.num_q_heads, s.num_kv_heads, s.head_dim = self.num_q_heads, self.num_kv_heads, self.head_dim
+        s.intermediate = self.w_down.shape[1]
+        s.rms_eps = self.eps
+        for name in ("attn_norm_gain", "w_qkv", "w_o", "mlp_norm_gain", "w_gate_up", "w_down",
+                     "couple_a", "couple_b", "couple_c"):
+            t = getattr(self, name)
+            setattr(s, name, None if t is None else _contig(t, name).data_ptr())
+        return s
+
+
+def layer_workspace_size(weights: LayerWeights, cache: KVCache, batch: int, n_flows: int,
+                         max_context: int) -> int:
+    n = ctypes.c_size_t()
+    w, c = weights.struct(), cache.struct()
+    check(lib().dfx_dual_flow_decode_layer_workspace_size(ctypes.byref(w), ctypes.byref(c), batch,
+                                                          n_flows, max_context, ctypes.byref(n)))
+    return n.value
+
+
+def dual_flow_decode_layer(x: torch.Tensor, weights: LayerWeights, cache: KVCache,
+                           context_lens: torch.Tensor, max_context: int,
+                           workspace: Optional[Workspace] = None, stream=None) -> torch.Tensor:
+    """One decode step of one layer, in place on x [F][B][hidden] fp32 (F = 2: both flows)."""
+    F, B, H = x.shape
+    x = _contig(x, "x")
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    w, c = weights.struct(), cache.struct()
+    need = layer_workspace_size(weights, cache, B, F, max_context)
+    ws = _workspace(workspace, x.device, "layer").get(need)
+    check(lib().dfx_dual_flow_decode_layer(ctypes.byref(w), ctypes.byref(c), _ptr(context_lens), B,
+                                           max_context, F, _ptr(x), _ptr(ws), need, _stream(stream)))
+    return x
+
+
+def copy_bytes(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    n = min(dst.numel() * dst.element_size(), src.numel() * src.element_size())
+    check(lib().dfx_copy_bytes(_ptr(dst), _ptr(src), n - n % 16, _stream(stream)))
+
+
+def fill_bytes(dst: torch.Tensor, pattern: int = 0, stream=None) -> None:
+    n = dst.numel() * dst.element_size()
+    check(lib().dfx_fill_bytes(_ptr(dst), n - n % 16, pattern, _stream(stream)))

@@ -1,0 +1,479 @@
+// C ABI of libdfx.so: argument validation (before any HIP call), split planning,
+// workspace carving and kernel dispatch. No device memory is allocated here and
+// nothing synchronizes; every launch goes to the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+using namespace dfx;
+
+namespace {
+
+thread_local char g_err[512];
+
+dfx_status fail(dfx_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dfx_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return DFX_OK;
+  return fail(DFX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kChunkQuantum = 128;  // tokens: 4 waves x 32-token tiles
+constexpr int kMinChunk = 512;
+constexpr int kTargetAttnGroups = 2048;
+constexpr int kTargetGemmGroups = 512;
+// Split-K arrival counters live in a fixed region at the start of a linear workspace, so
+// that a later call with another plan never reads bytes an earlier call used as partials.
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(uint32_t));
+
+dfx_status check_kv(const dfx_kv_cache *kv, int32_t batch) {
+  if (!kv) return fail(DFX_EINVAL, "kv is NULL");
+  if (kv->dtype != DFX_F32 && kv->dtype != DFX_BF16) return fail(DFX_EINVAL, "kv.dtype %d", kv->dtype);
+  if (kv->head_dim != 64 && kv->head_dim != 128)
+    return fail(DFX_EUNSUPPORTED, "head_dim %d (64 or 128 supported)", kv->head_dim);
+  if (kv->num_kv_heads < 1) return fail(DFX_EINVAL, "num_kv_heads %d", kv->num_kv_heads);
+  if (kv->block_size < 1) return fail(DFX_EINVAL, "block_size %d", kv->block_size);
+  if (kv->num_blocks < 1) return fail(DFX_EINVAL, "num_blocks %lld", (long long)kv->num_blocks);
+  if (!kv->k || !kv->v) return fail(DFX_EINVAL, "kv.k / kv.v is NULL");
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(DFX_EINVAL, "kv.k / kv.v not 16-byte aligned");
+  if (kv->reserved != 0) return fail(DFX_EINVAL, "kv.reserved must be 0");
+  if (kv->block_table) {
+    if (!pow2(kv->block_size)) return fail(DFX_EINVAL, "paged block_size %d is not a power of two", kv->block_size);
+    if (kv->max_blocks_per_seq < 1) return fail(DFX_EINVAL, "max_blocks_per_seq %d", kv->max_blocks_per_seq);
+  } else if (kv->num_blocks < batch) {
+    return fail(DFX_EINVAL, "contiguous cache has %lld sequences < batch %d", (long long)kv->num_blocks, batch);
+  }
+  return DFX_OK;
+}
+
+int64_t capacity(const dfx_kv_cache *kv) {
+  return kv->block_table ? (int64_t)kv->max_blocks_per_seq * kv->block_size : kv->block_size;
+}
+
+void attn_plan(int batch, int hkv, int max_ctx, int requested, int *splits, int *chunk) {
+  const int max_s = max_ctx > 0 ? (max_ctx + kChunkQuantum - 1) / kChunkQuantum : 1;
+  int s;
+  if (requested > 0) {
+    s = requested < max_s ? requested : max_s;
+  } else {
+    const int pairs = batch * hkv > 0 ? batch * hkv : 1;
+    s = (kTargetAttnGroups + pairs - 1) / pairs;
+    const int by_min = max_ctx > kMinChunk ? (max_ctx + kMinChunk - 1) / kMinChunk : 1;
+    if (s > by_min) s = by_min;
+    if (s > max_s) s = max_s;
+    if (s < 1) s = 1;
+  }
+  int c = max_ctx > 0 ? (max_ctx + s - 1) / s : kChunkQuantum;
+  c = (c + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
+  *chunk = c;
+  *splits = max_ctx > 0 ? (max_ctx + c - 1) / c : 1;
+}
+
+size_t attn_ws_bytes(int splits, int n_flows, int batch, int hq, int d) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)splits * n_flows * batch * hq;
+  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+}
+
+struct GemmPlan {
+  int nt, ksplit, tiles, groups;
+  size_t counter_bytes, partial_bytes;
+  size_t total() const { return counter_bytes + partial_bytes; }
+};
+
+GemmPlan gemm_plan(int n_flows, int rows, int K, int N) {
+  GemmPlan g{};
+  const int per_group = n_flows * rows < 64 ? n_flows * rows : 64;
+  g.nt = (N % 64 == 0 && per_group > 32) ? 64 : (N % 32 == 0 ? 32 : 16);
+  g.tiles = N / g.nt;
+  const int nks = K / 32;
+  int ks = (kTargetGemmGroups + g.tiles - 1) / g.tiles;
+  const int max_ks = nks / 8 > 1 ? nks / 8 : 1;  // keep >= 8 k-steps (2 per wave) per group
+  if (ks > max_ks) ks = max_ks;
+  if (ks > 8) ks = 8;
+  if (ks < 1) ks = 1;
+  g.ksplit = ks;
+  const int rpg = 64 / n_flows;
+  g.groups = rows > 0 ? (rows + rpg - 1) / rpg : 0;
+  if ((int64_t)g.groups * g.tiles > kMaxCounters) ks = 1;
+  g.ksplit = ks;
+  if (ks > 1) {
+    g.counter_bytes = kCounterBytes;
+    g.partial_bytes = (size_t)ks * g.groups * g.tiles * 64 * g.nt * sizeof(float);
+  }
+  return g;
+}
+
+dfx_status check_linear(int32_t n_flows, int32_t rows, int32_t K, int32_t N) {
+  if (n_flows != 1 && n_flows != 2) return fail(DFX_EINVAL, "n_flows %d (1 or 2)", n_flows);
+  if (rows < 0) return fail(DFX_EINVAL, "rows %d", rows);
+  if (K < 32 || K % 32) return fail(DFX_EUNSUPPORTED, "in_features %d is not a positive multiple of 32", K);
+  if (N < 16 || N % 16) return fail(DFX_EUNSUPPORTED, "out_features %d is not a positive multiple of 16", N);
+  return DFX_OK;
+}
+
+// counters: zero-filled region of >= plan.counter_bytes; partial: >= plan.partial_bytes.
+dfx_status run_linear_parts(int32_t n_flows, int32_t rows, int32_t K, int32_t N, int x_f32,
+                            const void *x, const uint16_t *w, int y_bf16, void *y,
+                            const float *couple, const float *residual, uint32_t *counters,
+                            float *partial, hipStream_t s) {
+  if (rows == 0) return DFX_OK;
+  const GemmPlan g = gemm_plan(n_flows, rows, K, N);
+  GemmArgs a{};
+  a.n_flows = n_flows; a.rows = rows; a.K = K; a.N = N;
+  a.x_f32 = x_f32; a.x = x; a.w = w; a.y_bf16 = y_bf16; a.y = y;
+  a.couple = couple; a.residual = residual; a.ksplit = g.ksplit;
+  a.counters = g.ksplit > 1 ? counters : nullptr;
+  a.partial = g.ksplit > 1 ? partial : nullptr;
+  return hip_status(launch_grouped_linear(a, g.nt, s), "grouped_linear launch");
+}
+
+dfx_status run_linear(int32_t n_flows, int32_t rows, int32_t K, int32_t N, int x_f32, const void *x,
+                      const uint16_t *w, int y_bf16, void *y, const float *couple,
+                      const float *residual, void *ws, size_t ws_bytes, hipStream_t s) {
+  if (rows == 0) return DFX_OK;
+  const GemmPlan g = gemm_plan(n_flows, rows, K, N);
+  if (g.total() > 0 && (!ws || ws_bytes < g.total()))
+    return fail(DFX_EWORKSPACE, "grouped_linear needs %zu workspace bytes, got %zu", g.total(), ws_bytes);
+  return run_linear_parts(n_flows, rows, K, N, x_f32, x, w, y_bf16, y, couple, residual,
+                          (uint32_t *)ws, (float *)((char *)ws + g.counter_bytes), s);
+}
+
+struct AttnCall {
+  const dfx_kv_cache *kv;
+  const int32_t *ctx;
+  int32_t batch, max_context, hq, q_dtype;
+  const void *q1, *q2;
+  int64_t q_bstride;
+  const float *a;
+  int32_t a_stride;
+  float scale;
+  float *o1, *o2, *lse;
+  int32_t splits;
+  void *ws;
+  size_t ws_bytes;
+};
+
+dfx_status validate_attn(const AttnCall &c) {
+  dfx_status st = check_kv(c.kv, c.batch);
+  if (st) return st;
+  const dfx_kv_cache *kv = c.kv;
+  if (c.batch < 0) return fail(DFX_EINVAL, "batch %d", c.batch);
+  if (c.hq < 1 || c.hq % kv->num_kv_heads)
+    return fail(DFX_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", c.hq, kv->num_kv_heads);
+  if (c.q_dtype != DFX_F32 && c.q_dtype != DFX_BF16) return fail(DFX_EINVAL, "q_dtype %d", c.q_dtype);
+  if (c.max_context < 0 || c.max_context > capacity(kv))
+    return fail(DFX_EINVAL, "max_context %d outside [0, capacity %lld]", c.max_context, (long long)capacity(kv));
+  if (c.batch > 0 && !c.ctx) return fail(DFX_EINVAL, "context_lens is NULL");
+  if (c.batch > 0 && kv->block_table == nullptr && kv->num_blocks < c.batch)
+    return fail(DFX_EINVAL, "contiguous cache smaller than batch");
+  if (!c.q1 || !c.o1) return fail(DFX_EINVAL, "q1 / o1 is NULL");
+  if ((c.q2 == nullptr) != (c.o2 == nullptr)) return fail(DFX_EINVAL, "q2_raw and o2 must be both NULL or both set");
+  if (c.a && !c.q2) return fail(DFX_EINVAL, "coupling vector a given without q2_raw");
+  if (c.a_stride != 0 && c.a_stride != kv->head_dim)
+    return fail(DFX_EINVAL, "a_head_stride %d (0 or head_dim)", c.a_stride);
+  const int64_t row = (int64_t)c.hq * kv->head_dim;
+  if (c.q_bstride < 0 || (c.q_bstride != 0 && (c.q_bstride < row || c.q_bstride % 8)))
+    return fail(DFX_EINVAL, "q_batch_stride %lld", (long long)c.q_bstride);
+  if (!aligned16(c.q1) || (c.q2 && !aligned16(c.q2)) || !aligned16(c.o1) || (c.o2 && !aligned16(c.o2)))
+    return fail(DFX_EINVAL, "q / o pointers must be 16-byte aligned");
+  if (c.a && ((uintptr_t)c.a & 3)) return fail(DFX_EINVAL, "a not 4-byte aligned");
+  if (c.splits < 0) return fail(DFX_EINVAL, "num_splits %d", c.splits);
+  const int G = c.hq / kv->num_kv_heads, F = c.q2 ? 2 : 1;
+  if (F * G > 32) return fail(DFX_EUNSUPPORTED, "%d query rows per KV head (at most 32)", F * G);
+  return DFX_OK;
+}
+
+dfx_status run_attn(const AttnCall &c, hipStream_t s) {
+  dfx_status st = validate_attn(c);
+  if (st) return st;
+  const dfx_kv_cache *kv = c.kv;
+  const int F = c.q2 ? 2 : 1, G = c.hq / kv->num_kv_heads;
+  int splits, chunk;
+  attn_plan(c.batch, kv->num_kv_heads, c.max_context, c.splits, &splits, &chunk);
+  const size_t need = attn_ws_bytes(splits, F, c.batch, c.hq, kv->head_dim);
+  if (need && (!c.ws || c.ws_bytes < need))
+    return fail(DFX_EWORKSPACE, "decode_attn needs %zu workspace bytes for %d splits, got %zu", need, splits, c.ws_bytes);
+  if (c.batch == 0) return DFX_OK;
+  AttnArgs a{};
+  a.k = kv->k; a.v = kv->v; a.table = kv->block_table; a.num_blocks = kv->num_blocks;
+  a.max_blocks = kv->max_blocks_per_seq; a.block_size = kv->block_size;
+  a.block_shift = kv->block_table ? (int)__builtin_ctz((unsigned)kv->block_size) : -1;
+  a.num_kv_heads = kv->num_kv_heads; a.head_dim = kv->head_dim; a.group = G;
+  a.num_q_heads = c.hq; a.n_flows = F; a.batch = c.batch; a.ctx = c.ctx; a.max_context = c.max_context;
+  a.q1 = c.q1; a.q2 = c.q2; a.q_bstride = c.q_bstride ? c.q_bstride : (int64_t)c.hq * kv->head_dim;
+  a.q_bf16 = c.q_dtype == DFX_BF16; a.kv_bf16 = kv->dtype == DFX_BF16;
+  a.a = c.a; a.a_hstride = c.a_stride;
+  const float scale = c.scale > 0.f ? c.scale : 1.0f / sqrtf((float)kv->head_dim);
+  a.scale_log2 = scale * kLog2e;
+  a.o1 = c.o1; a.o2 = c.o2; a.lse = c.lse;
+  a.num_splits = splits; a.chunk = chunk;
+  if (splits > 1) {
+    const size_t rows = (size_t)splits * F * c.batch * c.hq;
+    a.part_o = (float *)c.ws;
+    a.part_lse = (float *)((char *)c.ws + round_up(rows * kv->head_dim * sizeof(float), 256));
+  }
+  const bool mfma = a.kv_bf16 && F * G <= 16;
+  hipError_t e = mfma ? launch_attn_mfma(a, s) : launch_attn_valu(a, s);
+  if (e != hipSuccess) return hip_status(e, "decode_attn launch");
+  if (splits > 1) return hip_status(launch_attn_merge(a, s), "decode_attn merge launch");
+  return DFX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dfx_version(void) { return DFX_VERSION; }
+
+const char *dfx_last_error(void) { return g_err; }
+
+#define DFX_BEGIN g_err[0] = 0; try {
+#define DFX_END } catch (...) { return fail(DFX_EINVAL, "internal error"); }
+
+dfx_status dfx_decode_attn_plan(const dfx_kv_cache *kv, int32_t batch, int32_t num_q_heads,
+                                int32_t n_flows, int32_t max_context, int32_t num_splits,
+                                int32_t *splits_out, size_t *workspace_bytes) {
+  DFX_BEGIN
+  dfx_status st = check_kv(kv, batch < 0 ? 0 : batch);
+  if (st) return st;
+  if (batch < 0 || num_q_heads < 1 || (n_flows != 1 && n_flows != 2) || max_context < 0 || num_splits < 0)
+    return fail(DFX_EINVAL, "bad plan arguments");
+  if (max_context > capacity(kv)) return fail(DFX_EINVAL, "max_context above cache capacity");
+  int s, c;
+  attn_plan(batch, kv->num_kv_heads, max_context, num_splits, &s, &c);
+  if (splits_out) *splits_out = s;
+  if (workspace_bytes) *workspace_bytes = attn_ws_bytes(s, n_flows, batch, num_q_heads, kv->head_dim);
+  return DFX_OK;
+  DFX_END
+}
+
+dfx_status dfx_decode_attn(const dfx_kv_cache *kv, const int32_t *context_lens, int32_t batch,
+                           int32_t max_context, int32_t num_q_heads, int32_t q_dtype,
+                           const void *q1, const void *q2_raw, int64_t q_batch_stride,
+                           const float *a, int32_t a_head_stride, float softmax_scale,
+                           float *o1, float *o2, float *lse, int32_t num_splits,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  DFX_BEGIN
+  AttnCall c{kv, context_lens, batch, max_context, num_q_heads, q_dtype, q1, q2_raw, q_batch_stride,
+             a, a_head_stride, softmax_scale, o1, o2, lse, num_splits, workspace, workspace_bytes};
+  return run_attn(c, (hipStream_t)stream);
+  DFX_END
+}
+
+dfx_status dfx_kv_append_primary(const dfx_kv_cache *kv, int32_t batch, const int32_t *positions,
+                                 int32_t src_dtype, const void *k_new, const void *v_new,
+                                 int64_t src_row_stride, void *stream) {
+  DFX_BEGIN
+  dfx_status st = check_kv(kv, batch < 0 ? 0 : batch);
+  if (st) return st;
+  if (batch < 0) return fail(DFX_EINVAL, "batch %d", batch);
+  if (src_dtype != DFX_F32 && src_dtype != DFX_BF16) return fail(DFX_EINVAL, "src_dtype %d", src_dtype);
+  if (batch > 0 && (!positions || !k_new || !v_new)) return fail(DFX_EINVAL, "positions / k_new / v_new is NULL");
+  const int64_t row = (int64_t)kv->num_kv_heads * kv->head_dim;
+  if (src_row_stride < 0 || (src_row_stride != 0 && (src_row_stride < row || src_row_stride % 8)))
+    return fail(DFX_EINVAL, "src_row_stride %lld", (long long)src_row_stride);
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(DFX_EINVAL, "k_new / v_new not 16-byte aligned");
+  if (batch == 0) return DFX_OK;
+  return hip_status(launch_kv_append(*kv, batch, positions, 0, src_dtype == DFX_F32, k_new, v_new,
+                                     src_row_stride ? src_row_stride : row, (hipStream_t)stream),
+                    "kv_append launch");
+  DFX_END
+}
+
+dfx_status dfx_grouped_linear_workspace_size(int32_t n_flows, int32_t rows, int32_t in_features,
+                                             int32_t out_features, size_t *bytes) {
+  DFX_BEGIN
+  dfx_status st = check_linear(n_flows, rows, in_features, out_features);
+  if (st) return st;
+  if (!bytes) return fail(DFX_EINVAL, "bytes is NULL");
+  *bytes = rows > 0 ? gemm_plan(n_flows, rows, in_features, out_features).total() : 0;
+  return DFX_OK;
+  DFX_END
+}
+
+dfx_status dfx_grouped_linear(int32_t n_flows, int32_t rows, int32_t in_features,
+                              int32_t out_features, int32_t x_dtype, const void *x,
+                              const uint16_t *w, int32_t y_dtype, void *y, const float *couple,
+                              const float *residual, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  DFX_BEGIN
+  dfx_status st = check_linear(n_flows, rows, in_features, out_features);
+  if (st) return st;
+  if (x_dtype != DFX_F32 && x_dtype != DFX_BF16) return fail(DFX_EINVAL, "x_dtype %d", x_dtype);
+  if (y_dtype != DFX_F32 && y_dtype != DFX_BF16) return fail(DFX_EINVAL, "y_dtype %d", y_dtype);
+  if (rows > 0 && (!x || !w || !y)) return fail(DFX_EINVAL, "x / w / y is NULL");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (residual && !aligned16(residual)))
+    return fail(DFX_EINVAL, "x / w / y / residual not 16-byte aligned");
+  if (couple && ((uintptr_t)couple & 3)) return fail(DFX_EINVAL, "couple not 4-byte aligned");
+  return run_linear(n_flows, rows, in_features, out_features, x_dtype == DFX_F32, x, w,
+                    y_dtype == DFX_BF16, y, couple, residual, workspace, workspace_bytes,
+                    (hipStream_t)stream);
+  DFX_END
+}
+
+dfx_status dfx_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
+                       uint16_t *y, void *stream) {
+  DFX_BEGIN
+  if (rows < 0 || dim < 4 || dim % 4 || dim > 16384) return fail(DFX_EINVAL, "rows %d dim %d", rows, dim);
+  if (rows > 0 && (!x || !gain || !y)) return fail(DFX_EINVAL, "x / gain / y is NULL");
+  if (!aligned16(x) || !aligned16(gain) || ((uintptr_t)y & 7)) return fail(DFX_EINVAL, "misaligned pointer");
+  if (!(eps >= 0.f)) return fail(DFX_EINVAL, "eps");
+  return hip_status(launch_rmsnorm(rows, dim, x, gain, eps, y, (hipStream_t)stream), "rmsnorm launch");
+  DFX_END
+}
+
+dfx_status dfx_swiglu_couple(int32_t n_flows, int32_t rows, int32_t dim, const float *gate_up,
+                             const float *b, uint16_t *out, void *stream) {
+  DFX_BEGIN
+  if ((n_flows != 1 && n_flows != 2) || rows < 0 || dim < 4 || dim % 4)
+    return fail(DFX_EINVAL, "n_flows %d rows %d dim %d", n_flows, rows, dim);
+  if (rows > 0 && (!gate_up || !out)) return fail(DFX_EINVAL, "gate_up / out is NULL");
+  if (!aligned16(gate_up) || (b && !aligned16(b)) || ((uintptr_t)out & 7)) return fail(DFX_EINVAL, "misaligned pointer");
+  return hip_status(launch_swiglu(n_flows, rows, dim, gate_up, b, out, (hipStream_t)stream), "swiglu launch");
+  DFX_END
+}
+
+// ---- one dual-flow decode layer ---------------------------------------------------
+
+namespace {
+
+struct LayerPlan {
+  size_t h, qkv, o, gu, attn_ws, counters, partials, total;
+  int splits;
+};
+
+dfx_status layer_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_t batch,
+                      int32_t n_flows, int32_t max_context, LayerPlan *pl) {
+  if (!w) return fail(DFX_EINVAL, "weights is NULL");
+  dfx_status st = check_kv(kv, batch < 0 ? 0 : batch);
+  if (st) return st;
+  if (batch < 0 || (n_flows != 1 && n_flows != 2)) return fail(DFX_EINVAL, "batch %d n_flows %d", batch, n_flows);
+  if (kv->dtype != DFX_BF16) return fail(DFX_EUNSUPPORTED, "layer needs a bf16 cache");
+  if (w->head_dim != kv->head_dim || w->num_kv_heads != kv->num_kv_heads)
+    return fail(DFX_EINVAL, "weights and cache disagree on head_dim / num_kv_heads");
+  if (w->num_q_heads < 1 || w->num_q_heads % w->num_kv_heads) return fail(DFX_EINVAL, "num_q_heads %d", w->num_q_heads);
+  if (w->hidden < 32 || w->hidden % 32 || w->hidden > 16384) return fail(DFX_EUNSUPPORTED, "hidden %d", w->hidden);
+  if (w->intermediate < 32 || w->intermediate % 32) return fail(DFX_EUNSUPPORTED, "intermediate %d", w->intermediate);
+  if (!(w->rms_eps >= 0.f)) return fail(DFX_EINVAL, "rms_eps");
+  if (!w->attn_norm_gain || !w->w_qkv || !w->w_o || !w->mlp_norm_gain || !w->w_gate_up || !w->w_down)
+    return fail(DFX_EINVAL, "a weight pointer is NULL");
+  if (max_context < 1 || max_context > capacity(kv)) return fail(DFX_EINVAL, "max_context %d", max_context);
+  const int F = n_flows, B = batch, H = w->hidden, D = w->head_dim, Hq = w->num_q_heads;
+  const int Nqkv = (Hq + 2 * w->num_kv_heads) * D, I = w->intermediate;
+  LayerPlan p{};
+  auto a256 = [](size_t x) { return round_up(x, 256); };
+  p.h = a256((size_t)F * B * (H > I ? H : I) * 2);
+  p.qkv = a256((size_t)F * B * Nqkv * 4);
+  p.o = a256((size_t)F * B * Hq * D * 4);
+  p.gu = a256((size_t)F * B * 2 * I * 4);
+  // (the bf16 MLP intermediate reuses the h buffer)
+  int chunk;
+  attn_plan(B, kv->num_kv_heads, max_context, 0, &p.splits, &chunk);
+  p.attn_ws = a256(attn_ws_bytes(p.splits, F, B, Hq, D));
+  // one counter region (zero between calls) shared by the four projections, which run
+  // one after another on the stream, then one partial region
+  const int shapes[4][2] = {{H, Nqkv}, {Hq * D, H}, {H, 2 * I}, {I, H}};
+  for (auto &sh : shapes) {
+    const GemmPlan g = gemm_plan(F, B, sh[0], sh[1]);
+    p.counters = g.counter_bytes > p.counters ? g.counter_bytes : p.counters;
+    p.partials = g.partial_bytes > p.partials ? g.partial_bytes : p.partials;
+  }
+  p.counters = a256(p.counters);
+  p.partials = a256(p.partials);
+  p.total = p.counters + p.partials + p.h + p.qkv + p.o + p.gu + p.attn_ws;
+  *pl = p;
+  return DFX_OK;
+}
+
+}  // namespace
+
+dfx_status dfx_dual_flow_decode_layer_workspace_size(const dfx_layer_weights *w,
+                                                     const dfx_kv_cache *kv, int32_t batch,
+                                                     int32_t n_flows, int32_t max_context,
+                                                     size_t *bytes) {
+  DFX_BEGIN
+  LayerPlan p;
+  dfx_status st = layer_plan(w, kv, batch, n_flows, max_context, &p);
+  if (st) return st;
+  if (!bytes) return fail(DFX_EINVAL, "bytes is NULL");
+  *bytes = p.total;
+  return DFX_OK;
+  DFX_END
+}
+
+dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv,
+                                      const int32_t *context_lens, int32_t batch,
+                                      int32_t max_context, int32_t n_flows, float *x,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+  DFX_BEGIN
+  LayerPlan p;
+  dfx_status st = layer_plan(w, kv, batch, n_flows, max_context, &p);
+  if (st) return st;
+  if (batch > 0 && (!context_lens || !x)) return fail(DFX_EINVAL, "context_lens / x is NULL");
+  if (!aligned16(x)) return fail(DFX_EINVAL, "x not 16-byte aligned");
+  if (!workspace || workspace_bytes < p.total)
+    return fail(DFX_EWORKSPACE, "layer needs %zu workspace bytes, got %zu", p.total, workspace_bytes);
+  if (batch == 0) return DFX_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int F = n_flows, B = batch, H = w->hidden, D = w->head_dim, Hq = w->num_q_heads;
+  const int Hkv = w->num_kv_heads, Nqkv = (Hq + 2 * Hkv) * D, I = w->intermediate;
+  char *base = (char *)workspace;
+  uint32_t *cnt = (uint32_t *)base;
+  float *part = (float *)(base + p.counters);
+  uint16_t *h = (uint16_t *)(base + p.counters + p.partials);
+  float *qkv = (float *)((char *)h + p.h);
+  float *o = (float *)((char *)qkv + p.qkv);
+  float *gu = (float *)((char *)o + p.o);
+  void *aws = (char *)gu + p.gu;
+  const int rows = F * B;
+  dfx_status r;
+  // attention block
+  if ((r = hip_status(launch_rmsnorm(rows, H, x, w->attn_norm_gain, w->rms_eps, h, s), "rmsnorm launch"))) return r;
+  if ((r = run_linear_parts(F, B, H, Nqkv, 0, h, w->w_qkv, 0, qkv, nullptr, nullptr, cnt, part, s))) return r;
+  if ((r = hip_status(launch_kv_append(*kv, B, context_lens, 1, 1, qkv + Hq * D, qkv + (Hq + Hkv) * D,
+                                       Nqkv, s), "kv_append launch"))) return r;
+  AttnCall c{kv, context_lens, B, max_context, Hq, DFX_F32, qkv, F == 2 ? qkv + (size_t)B * Nqkv : nullptr,
+             Nqkv, F == 2 ? w->couple_a : nullptr, 0, 0.f, o, F == 2 ? o + (size_t)B * Hq * D : nullptr,
+             nullptr, 0, aws, p.attn_ws};
+  if ((r = run_attn(c, s))) return r;
+  if ((r = run_linear_parts(F, B, Hq * D, H, 1, o, w->w_o, 0, x, nullptr, x, cnt, part, s))) return r;
+  // MLP block
+  if ((r = hip_status(launch_rmsnorm(rows, H, x, w->mlp_norm_gain, w->rms_eps, h, s), "rmsnorm launch"))) return r;
+  if ((r = run_linear_parts(F, B, H, 2 * I, 0, h, w->w_gate_up, 0, gu, nullptr, nullptr, cnt, part, s))) return r;
+  if ((r = hip_status(launch_swiglu(F, B, I, gu, F == 2 ? w->couple_b : nullptr, h, s), "swiglu launch"))) return r;
+  return run_linear_parts(F, B, I, H, 0, h, w->w_down, 0, x, F == 2 ? w->couple_c : nullptr, x, cnt, part, s);
+  DFX_END
+}
+
+dfx_status dfx_copy_bytes(void *dst, const void *src, size_t bytes, void *stream) {
+  DFX_BEGIN
+  if (bytes % 16 || !aligned16(dst) || !aligned16(src) || (bytes && (!dst || !src)))
+    return fail(DFX_EINVAL, "copy needs 16-byte aligned pointers and a multiple of 16 bytes");
+  return hip_status(launch_copy(dst, src, bytes, (hipStream_t)stream), "copy launch");
+  DFX_END
+}
+
+dfx_status dfx_fill_bytes(void *dst, size_t bytes, uint32_t pattern, void *stream) {
+  DFX_BEGIN
+  if (bytes % 16 || !aligned16(dst) || (bytes && !dst))
+    return fail(DFX_EINVAL, "fill needs a 16-byte aligned pointer and a multiple of 16 bytes");
+  return hip_status(launch_fill(dst, bytes, pattern, (hipStream_t)stream), "fill launch");
+  DFX_END
+}
+
+}  // extern "C"

@@ -1,0 +1,303 @@
+// Dual-query flash-decoding over a bf16 K/V cache on gfx950 matrix cores.
+//
+// The auxiliary query attends to the primary's keys and values, so one pass over the
+// cache serves both flows (Sintesi Tecnica: Dual-Flow Transformers, "Meccanismi
+// Chiave"). One work-group owns (sequence b, KV head g, context split); its query
+// tile holds every query row that reads KV head g: n_flows x (Hq / Hkv) rows, at most
+// 16 -- both flows and all grouped-query heads share each K/V byte fetched from HBM.
+//
+// Per 32-token tile a wave computes
+//   S^T[tok][row] = K[tok][:] . Q[row][:]       (16x16x32 bf16 MFMA, two 16-token blocks)
+//   O^T[d][row]  += V^T[d][tok] . P^T[tok][row] (one MFMA per 16 head-dim rows)
+// with fp32 accumulation. Q and P are fp32 values; each is split into bf16 hi + lo and
+// multiplied twice, so products carry ~16 significant bits more than one bf16 pass
+// (K and V are exact bf16 already). The softmax is online (running max m, sum l) in the
+// log2 domain; a row's statistics live in the same lane as its O^T column, so the
+// per-tile rescale needs no cross-lane traffic.
+//
+// Lane layouts (64 lanes, n = lane % 16, j = lane / 16):
+//   A operand 16 x 32: lane holds row n, k = 8j .. 8j+7;  B operand 32 x 16: column n,
+//   k = 8j .. 8j+7;  C 16 x 16: column n, rows 4j .. 4j+3.
+// The k order of a contraction is free as long as both operands use it, which fixes the
+// loads: score k-step s uses head-dim chunk c = 4s + j (so one load instruction reads a
+// 64-byte run of 16 token rows); the P.V contraction orders tokens as
+// tau(j, v) = 4j + v (v < 4), 16 + 4j + v - 4 (v >= 4), which is exactly where the
+// score MFMA left them, and its M rows are head-dim d = VEC * m + mb, so one lane loads
+// VEC contiguous elements of 8 token rows (4 full rows per load instruction) and a
+// register transpose yields the V^T operand.
+#include "common.h"
+
+namespace dfx {
+
+__device__ __forceinline__ int64_t kv_row(const AttnArgs &p, int b, int g, int pos) {
+  int64_t blk;
+  int slot;
+  if (p.block_shift >= 0) {
+    const uint32_t e = (uint32_t)p.table[(int64_t)b * p.max_blocks + (pos >> p.block_shift)];
+    blk = (uint64_t)e < (uint64_t)p.num_blocks ? (int64_t)e : p.num_blocks - 1;
+    slot = pos & (p.block_size - 1);
+  } else {
+    blk = b;
+    slot = pos;
+  }
+  return ((blk * p.num_kv_heads + g) * (int64_t)p.block_size + slot) * p.head_dim;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void *base, int64_t off, float *out) {
+  if constexpr (BF16) {
+    const u32x4 w = *(const u32x4 *)((const uint16_t *)base + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = bf16_lo(w[i]);
+      out[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const f32x4 a = *(const f32x4 *)((const float *)base + off);
+    const f32x4 c = *(const f32x4 *)((const float *)base + off + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[i] = a[i];
+      out[4 + i] = c[i];
+    }
+  }
+}
+
+// Writes one finished (row, d) value: final output when there is a single split,
+// otherwise the split's normalized partial and its log2-domain LSE.
+__device__ __forceinline__ void store_result(const AttnArgs &p, int split, int b, int g, int r,
+                                             int d, float M, float L, float O) {
+  const int G = p.group;
+  const int f = r / G, h = g * G + r % G;
+  const int Hq = p.num_q_heads, D = p.head_dim;
+  const float o = L > 0.f ? O / L : 0.f;
+  const float lse2 = L > 0.f ? M + __log2f(L) : -INFINITY;
+  if (p.num_splits == 1) {
+    float *out = f == 0 ? p.o1 : p.o2;
+    out[((int64_t)b * Hq + h) * D + d] = o;
+    if (d == 0 && p.lse) p.lse[((int64_t)f * p.batch + b) * Hq + h] = lse2 * kLn2;
+  } else {
+    const int64_t row = (((int64_t)split * p.n_flows + f) * p.batch + b) * Hq + h;
+    p.part_o[row * D + d] = o;
+    if (d == 0) p.part_lse[row] = lse2;
+  }
+}
+
+template <int D, bool QBF16>
+__global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs p) {
+  constexpr int KS = D / 32;  // k-steps of the score contraction
+  constexpr int VEC = D / 16; // head-dim elements one lane loads per V row; also O^T blocks
+  __shared__ float s_o[4][16][D];
+  __shared__ float s_m[4][16], s_l[4][16];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, j = lane >> 4;
+  const int ctx = min(max(p.ctx[b], 0), p.max_context);
+  const int start = split * p.chunk;
+  if (split > 0 && start >= ctx) return;  // uniform for the whole work-group
+  const int end = min(start + p.chunk, ctx);
+  const int G = p.group, R = p.n_flows * G;
+
+  // ---- query tile: lane holds query row n, head-dim chunks 4s + j; Q2 coupled here.
+  u32x4 qh[KS], ql[KS];
+  {
+    const bool valid = n < R;
+    const int f = valid ? n / G : 0;
+    const int h = g * G + (valid ? n % G : 0);
+    const int64_t qoff = (int64_t)b * p.q_bstride + (int64_t)h * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int d0 = 8 * (4 * s + j);
+      float q[8];
+      load8<QBF16>(p.q1, qoff + d0, q);
+      if (f == 1) {
+        float q2[8];
+        load8<QBF16>(p.q2, qoff + d0, q2);
+        if (p.a) {
+          const float *av = p.a + (int64_t)h * p.a_hstride + d0;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) q[v] = fmaf(av[v], q[v], q2[v]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 8; ++v) q[v] = q2[v];
+        }
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t h0, l0, h1, l1;
+        split_bf16(valid ? q[2 * w] : 0.f, h0, l0);
+        split_bf16(valid ? q[2 * w + 1] : 0.f, h1, l1);
+        qh[s][w] = h0 | (h1 << 16);
+        ql[s][w] = l0 | (l1 << 16);
+      }
+    }
+  }
+
+  const uint16_t *kp = (const uint16_t *)p.k;
+  const uint16_t *vp = (const uint16_t *)p.v;
+  f32x4 oacc[VEC];
+#pragma unroll
+  for (int mb = 0; mb < VEC; ++mb) oacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int t0 = start + 32 * wave; t0 < end; t0 += 128) {
+    // K rows of the two 16-token blocks (A operand rows = tokens t0 + 16 mb + n)
+    u32x4 kf[2][KS];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int64_t base = kv_row(p, b, g, min(t0 + 16 * mb + n, ctx - 1));
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[mb][s] = *(const u32x4 *)(kp + base + 8 * (4 * s + j));
+    }
+    // V: VEC elements (head-dim VEC*n ..) of the 8 token rows tau(j, v)
+    uint32_t vr[8][VEC / 2];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int tok = min(t0 + (v < 4 ? 4 * j + v : 12 + 4 * j + v), ctx - 1);
+      const uint16_t *src = vp + kv_row(p, b, g, tok) + VEC * n;
+      if constexpr (VEC == 8) {
+        const u32x4 x = *(const u32x4 *)src;
+        vr[v][0] = x[0]; vr[v][1] = x[1]; vr[v][2] = x[2]; vr[v][3] = x[3];
+      } else {
+        const u32x2 x = *(const u32x2 *)src;
+        vr[v][0] = x[0]; vr[v][1] = x[1];
+      }
+    }
+
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        sacc[mb] = mfma16x16x32(as_bf16x8(kf[mb][s]), as_bf16x8(qh[s]), sacc[mb]);
+        sacc[mb] = mfma16x16x32(as_bf16x8(kf[mb][s]), as_bf16x8(ql[s]), sacc[mb]);
+      }
+
+    // online softmax over this tile for query row n (lane holds 8 of its 32 tokens)
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 16 * mb + 4 * j + i;
+        const float x = tok < end ? sacc[mb][i] * p.scale_log2 : -INFINITY;
+        sv[4 * mb + i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+    uint32_t phi[8], plo[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const float pv = exp2f(sv[v] - m_new);
+      psum += pv;
+      split_bf16(pv, phi[v], plo[v]);
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    u32x4 pH, pL;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      pH[w] = phi[2 * w] | (phi[2 * w + 1] << 16);
+      pL[w] = plo[2 * w] | (plo[2 * w + 1] << 16);
+    }
+#pragma unroll
+    for (int mb = 0; mb < VEC; ++mb) {
+      oacc[mb] *= alpha;
+      // V^T rows d = VEC*n + mb over tokens tau(j, 0..7): element mb of each loaded row
+      u32x4 af;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x0 = vr[2 * w][mb >> 1], x1 = vr[2 * w + 1][mb >> 1];
+        af[w] = (mb & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+      }
+      oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pH), oacc[mb]);
+      oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pL), oacc[mb]);
+    }
+  }
+
+  // ---- combine the four waves (fixed order), then store output or split partial
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (j == 0) {
+    s_m[wave][n] = m_run;
+    s_l[wave][n] = l_tot;
+  }
+#pragma unroll
+  for (int mb = 0; mb < VEC; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[wave][n][VEC * (4 * j + i) + mb] = oacc[mb][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < R * D; idx += 256) {
+    const int r = idx / D, d = idx % D;
+    float M = fmaxf(fmaxf(s_m[0][r], s_m[1][r]), fmaxf(s_m[2][r], s_m[3][r]));
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float c = exp2f(s_m[w][r] - M);
+        L += c * s_l[w][r];
+        O += c * s_o[w][r][d];
+      }
+    }
+    store_result(p, split, b, g, r, d, M, L, O);
+  }
+}
+
+hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s) {
+  const dim3 grid(a.num_splits, a.num_kv_heads, a.batch), block(256);
+  if (a.head_dim == 128) {
+    if (a.q_bf16) attn_mfma_kernel<128, true><<<grid, block, 0, s>>>(a);
+    else attn_mfma_kernel<128, false><<<grid, block, 0, s>>>(a);
+  } else {
+    if (a.q_bf16) attn_mfma_kernel<64, true><<<grid, block, 0, s>>>(a);
+    else attn_mfma_kernel<64, false><<<grid, block, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+// ---- split merge: O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), lse = M + log2 sum
+template <int D>
+__global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs p) {
+  constexpr int PER = D / 64;
+  const int rows = p.n_flows * p.batch * p.num_q_heads;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int Hq = p.num_q_heads;
+  const int h = row % Hq, b = (row / Hq) % p.batch, f = row / (Hq * p.batch);
+  const int ctx = min(max(p.ctx[b], 0), p.max_context);
+  const int nvalid = min((ctx + p.chunk - 1) / p.chunk, p.num_splits);
+  const int64_t stride = (int64_t)p.n_flows * p.batch * Hq;  // rows per split
+  float M = -INFINITY;
+  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, p.part_lse[s * stride + row]);
+  float L = 0.f, O[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) O[k] = 0.f;
+  for (int s = 0; s < nvalid; ++s) {
+    const float c = exp2f(p.part_lse[s * stride + row] - M);
+    L += c;
+    const float *po = p.part_o + (s * stride + row) * D;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) O[k] += c * po[lane + 64 * k];
+  }
+  float *out = (f == 0 ? p.o1 : p.o2) + ((int64_t)b * Hq + h) * D;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) out[lane + 64 * k] = nvalid ? O[k] / L : 0.f;
+  if (lane == 0 && p.lse)
+    p.lse[((int64_t)f * p.batch + b) * Hq + h] = nvalid ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t s) {
+  const int rows = a.n_flows * a.batch * a.num_q_heads;
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (a.head_dim == 128) attn_merge_kernel<128><<<grid, block, 0, s>>>(a);
+  else attn_merge_kernel<64><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace dfx

@@ -1,0 +1,99 @@
+// Internal helpers shared by the dfx HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dfx.h"
+
+namespace dfx {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- bf16 <-> fp32 on raw bit patterns ----------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN -> quiet NaN with the sign kept.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Splits x into hi + lo, both bf16, with |x - hi - lo| <= 2^-16 |x| (hi is x truncated to
+// bf16, lo is the remainder rounded to nearest even). Two bf16 MFMA passes with hi and lo
+// give products accurate to about fp32's level where a single bf16 pass would lose 8 bits.
+__device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) {
+  uint32_t h = __float_as_uint(x) & 0xffff0000u;
+  hi = h >> 16;
+  lo = f32_to_bf16_rne(x - __uint_as_float(h));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- launch-time parameter blocks --------------------------------------------------
+
+struct AttnArgs {
+  const void *k, *v;
+  const int32_t *table;
+  int64_t num_blocks;
+  int32_t max_blocks, block_size, block_shift;  // block_shift < 0: contiguous layout
+  int32_t num_kv_heads, head_dim, group, num_q_heads, n_flows, batch;
+  const int32_t *ctx;
+  int32_t max_context;
+  const void *q1, *q2;
+  int64_t q_bstride;
+  int32_t q_bf16, kv_bf16;
+  const float *a;
+  int32_t a_hstride;
+  float scale_log2;  // softmax scale * log2(e)
+  float *o1, *o2, *lse;
+  float *part_o, *part_lse;  // [S][F][B][Hq][D], [S][F][B][Hq] (log2 domain)
+  int32_t num_splits, chunk;
+};
+
+struct GemmArgs {
+  int32_t n_flows, rows, K, N;
+  int32_t x_f32;
+  const void *x;
+  const uint16_t *w;
+  int32_t y_bf16;
+  void *y;
+  const float *couple, *residual;
+  int32_t ksplit;      // work-groups along K per feature tile
+  float *partial;      // [ksplit][groups][tiles][64][NT] when ksplit > 1
+  uint32_t *counters;  // [groups][tiles] arrival counters (zero between calls)
+};
+
+// Kernel launchers (defined next to their kernels). They assume validated arguments.
+hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_valu(const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t s);
+hipError_t launch_kv_append(const dfx_kv_cache &kv, int32_t batch, const int32_t *positions,
+                            int32_t pos_minus_one, int32_t src_f32, const void *k_new,
+                            const void *v_new, int64_t src_stride, hipStream_t s);
+hipError_t launch_grouped_linear(const GemmArgs &g, int nt, hipStream_t s);
+hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
+                          uint16_t *y, hipStream_t s);
+hipError_t launch_swiglu(int32_t n_flows, int32_t rows, int32_t dim, const float *gu,
+                         const float *b, uint16_t *out, hipStream_t s);
+hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+hipError_t launch_fill(void *dst, size_t bytes, uint32_t pattern, hipStream_t s);
+
+}  // namespace dfx

@@ -1,0 +1,101 @@
+// Layer glue: RMSNorm (shared gain, bf16 out), SwiGLU with the MLP-intermediate coupling
+// b (bf16 out), and two measurement helpers (plain copy, fill).
+#include "common.h"
+
+namespace dfx {
+
+// One work-group per row; each thread owns dim/256 elements read as float4.
+__global__ void __launch_bounds__(256) rmsnorm_kernel(int32_t dim, const float *x,
+                                                      const float *gain, float eps, uint16_t *y) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const f32x4 *xr = (const f32x4 *)(x + row * dim);
+  const int n4 = dim / 4;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const f32x4 v = xr[i];
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float r = 1.0f / sqrtf(tot / (float)dim + eps);
+  const f32x4 *g4 = (const f32x4 *)gain;
+  u32x2 *yr = (u32x2 *)(y + row * dim);
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const f32x4 v = xr[i], gg = g4[i];
+    yr[i] = u32x2{pack_bf16x2(v[0] * r * gg[0], v[1] * r * gg[1]),
+                  pack_bf16x2(v[2] * r * gg[2], v[3] * r * gg[3])};
+  }
+}
+
+hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
+                          uint16_t *y, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  rmsnorm_kernel<<<rows, 256, 0, s>>>(dim, x, gain, eps, y);
+  return hipGetLastError();
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// One thread per 4 intermediate elements of one row index, covering both flows.
+__global__ void __launch_bounds__(256) swiglu_kernel(int32_t n_flows, int32_t rows, int32_t dim,
+                                                     const float *gu, const float *bvec,
+                                                     uint16_t *out) {
+  const int q = dim / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)rows * q) return;
+  const int64_t r = idx / q;
+  const int i4 = (int)(idx % q) * 4;
+  f32x4 prim;
+  for (int f = 0; f < n_flows; ++f) {
+    const float *row = gu + ((int64_t)f * rows + r) * 2 * dim;
+    const f32x4 g = *(const f32x4 *)(row + i4), u = *(const f32x4 *)(row + dim + i4);
+    f32x4 v{silu(g[0]) * u[0], silu(g[1]) * u[1], silu(g[2]) * u[2], silu(g[3]) * u[3]};
+    if (f == 0) prim = v;
+    else if (bvec) {
+      const f32x4 bb = *(const f32x4 *)(bvec + i4);
+      v = f32x4{fmaf(bb[0], prim[0], v[0]), fmaf(bb[1], prim[1], v[1]),
+                fmaf(bb[2], prim[2], v[2]), fmaf(bb[3], prim[3], v[3])};
+    }
+    *(u32x2 *)(out + ((int64_t)f * rows + r) * dim + i4) =
+        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+}
+
+hipError_t launch_swiglu(int32_t n_flows, int32_t rows, int32_t dim, const float *gu,
+                         const float *b, uint16_t *out, hipStream_t s) {
+  const int64_t t = (int64_t)rows * (dim / 4);
+  if (t == 0) return hipSuccess;
+  swiglu_kernel<<<(unsigned)((t + 255) / 256), 256, 0, s>>>(n_flows, rows, dim, gu, b, out);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) copy_kernel(u32x4 *dst, const u32x4 *src, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = src[i];
+}
+
+__global__ void __launch_bounds__(256) fill_kernel(u32x4 *dst, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = u32x4{v, v, v, v};
+}
+
+hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 16);
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = n / 256 < 4096 ? (n + 255) / 256 : 4096;
+  copy_kernel<<<(unsigned)blocks, 256, 0, s>>>((u32x4 *)dst, (const u32x4 *)src, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(void *dst, size_t bytes, uint32_t pattern, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 16);
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = n / 256 < 4096 ? (n + 255) / 256 : 4096;
+  fill_kernel<<<(unsigned)blocks, 256, 0, s>>>((u32x4 *)dst, n, pattern);
+  return hipGetLastError();
+}
+
+}  // namespace dfx

@@ -1,0 +1,274 @@
+/*
+ * dfx.h -- C ABI of the dual-flow decode library (libdfx.so), MI355X / gfx950.
+ *
+ * The Dual-Flow Transformer runs two residual rows per generated position: a
+ * primary flow, which is a complete causal Transformer and the only writer of
+ * the persistent K/V cache, and an auxiliary flow, which reads the primary's
+ * cache and never writes it (Sintesi Tecnica: Dual-Flow Transformers,
+ * section "Architettura Core"). The auxiliary query Q2 is coupled to the
+ * primary query Q1 through a learned vector a and attends to the primary keys
+ * and values, so one pass over the cache and one pass over the shared weights
+ * serve both flows (same page, section "Meccanismi Chiave"; the cost claim --
+ * no larger cache, no extra unique weights read in decode -- is in section
+ * "Costi di Inferenza vs. Addestramento").
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates no device memory, keeps no per-call state and never
+ *    synchronizes. Every call is asynchronous on `stream` (a hipStream_t;
+ *    NULL = the null stream). Calls on one stream run in issue order.
+ *  - Flow 0 is the primary flow, flow 1 the auxiliary flow. Arrays with a
+ *    flow axis put it first: [n_flows][rows][...], flows back to back.
+ *  - bf16 values are stored as uint16 bit patterns; every bf16 rounding in
+ *    the library is round-to-nearest-even. Accumulation is fp32.
+ *  - Arguments are validated on the host before any HIP call. On failure a
+ *    call returns a non-zero dfx_status, launches nothing and leaves a message
+ *    for dfx_last_error(). A failed launch returns DFX_EHIP. No C++ exception
+ *    crosses this interface.
+ *  - Device-resident indices (context lengths, positions, block-table
+ *    entries) are clamped inside the kernels to the sizes given here, so a
+ *    bad value yields wrong numbers, never an out-of-bounds access.
+ */
+#ifndef DFX_H
+#define DFX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFX_VERSION 100
+
+typedef enum {
+  DFX_OK = 0,
+  DFX_EINVAL = 1,       /* a null pointer, bad size, bad stride or misaligned pointer */
+  DFX_EUNSUPPORTED = 2, /* a valid request outside what the kernels implement */
+  DFX_EWORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_size result */
+  DFX_EHIP = 4          /* a HIP call or kernel launch failed */
+} dfx_status;
+
+typedef enum { DFX_F32 = 0, DFX_BF16 = 1 } dfx_dtype;
+
+/*
+ * The single persistent K/V cache of the primary flow (same page, section
+ * "Architettura Core": only the primary writes it, the auxiliary flow reads it).
+ *
+ * Layout of k and v: [num_blocks][num_kv_heads][block_size][head_dim], elements
+ * of `dtype`, each pointer 16-byte aligned.
+ *  - Paged (block_table != NULL): position p of sequence b, KV head g is
+ *    element row [block_table[b*max_blocks_per_seq + p/block_size]][g][p % block_size].
+ *    block_size must be a power of two; block_table is device int32
+ *    [batch][max_blocks_per_seq].
+ *  - Contiguous (block_table == NULL): sequence b owns block b, block_size is
+ *    the per-sequence capacity (any value >= 1) and num_blocks >= batch.
+ */
+typedef struct dfx_kv_cache {
+  int32_t dtype;              /* dfx_dtype of the pool: DFX_BF16 or DFX_F32 */
+  int32_t num_kv_heads;       /* >= 1 */
+  int32_t head_dim;           /* 64 or 128 */
+  int32_t block_size;         /* tokens per block (paged) or capacity (contiguous) */
+  int64_t num_blocks;         /* blocks in the pool (block ids are clamped to it) */
+  void *k;                    /* device [num_blocks][num_kv_heads][block_size][head_dim] */
+  void *v;                    /* same layout as k */
+  const int32_t *block_table; /* device [batch][max_blocks_per_seq], or NULL (contiguous) */
+  int32_t max_blocks_per_seq; /* row length of block_table (ignored when contiguous) */
+  int32_t reserved;           /* must be 0 */
+} dfx_kv_cache;
+
+/* Library version (DFX_VERSION of the build). */
+int dfx_version(void);
+
+/* Message of the last failing call on this thread ("" if none). The pointer is
+ * valid until the next dfx_* call on the same thread. */
+const char *dfx_last_error(void);
+
+/* Number of context splits dfx_decode_attn will use for these arguments
+ * (num_splits = 0 asks for the automatic plan) and the workspace it needs in
+ * bytes (0 when the plan has a single split). Pure host arithmetic. */
+dfx_status dfx_decode_attn_plan(const dfx_kv_cache *kv, int32_t batch, int32_t num_q_heads,
+                                int32_t n_flows, int32_t max_context, int32_t num_splits,
+                                int32_t *splits_out, size_t *workspace_bytes);
+
+/*
+ * Dual-query decode attention over the primary cache (same page, section
+ * "Meccanismi Chiave": the auxiliary query Q2 is coupled to Q1 through the
+ * learned vector a and attends to the primary K1, V1; the cache is read once
+ * and serves both flows).
+ *
+ * For each sequence b < batch, query head h (KV head g = h / (num_q_heads /
+ * num_kv_heads)) and flow f:
+ *   Q1 = q1[b][h]                       Q2 = q2_raw[b][h] + a_h * Q1 (elementwise)
+ *   s_p = scale * <Q_f, K[b][g][p]>     for 0 <= p < n_b = min(context_lens[b], max_context)
+ *   o_f[b][h] = sum_p softmax(s)_p V[b][g][p],   lse[f][b][h] = log sum_p exp(s_p)
+ * a_h = a[h * a_head_stride + d] (a_head_stride 0: one vector of head_dim for
+ * all heads; head_dim: one vector per head). a == NULL means Q2 = q2_raw.
+ * n_b = 0 gives o = 0 and lse = -inf. Positions >= n_b are never read as data.
+ *
+ *  q1, q2_raw   device [batch][num_q_heads][head_dim] of q_dtype, rows of
+ *               consecutive sequences q_batch_stride elements apart (0 =
+ *               num_q_heads*head_dim; must be a multiple of 8); 16-byte aligned.
+ *               q2_raw == NULL runs the primary flow only (n_flows = 1).
+ *  a            device fp32, NULL, or [head_dim] / [num_q_heads][head_dim].
+ *  softmax_scale  <= 0 selects 1/sqrt(head_dim).
+ *  o1, o2       device fp32 [batch][num_q_heads][head_dim]; o2 NULL iff q2_raw NULL.
+ *  lse          device fp32 [n_flows][batch][num_q_heads] (natural log) or NULL.
+ *  max_context  host upper bound of context_lens (used for split planning and
+ *               clamping; <= the cache capacity).
+ *  num_splits   0 = automatic; otherwise the number of context splits, each
+ *               merged in a fixed order by a log-sum-exp combine (deterministic).
+ *  workspace    device scratch of >= the dfx_decode_attn_plan size (may be NULL
+ *               when that size is 0); owned by the caller, not kept after the call.
+ * The pool is only read. Results for one (b, h, f) do not depend on the other
+ * flow, heads or sequences: o1 is bit-identical with and without q2_raw.
+ */
+dfx_status dfx_decode_attn(const dfx_kv_cache *kv, const int32_t *context_lens, int32_t batch,
+                           int32_t max_context, int32_t num_q_heads, int32_t q_dtype,
+                           const void *q1, const void *q2_raw, int64_t q_batch_stride,
+                           const float *a, int32_t a_head_stride, float softmax_scale,
+                           float *o1, float *o2, float *lse, int32_t num_splits,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Append the primary flow's new key and value rows to the cache (same page,
+ * section "Architettura Core": the primary flow writes the persistent cache,
+ * the auxiliary flow never does -- this call has no flow argument, so no
+ * auxiliary row can reach the cache).
+ *
+ * For each b < batch: row positions[b] of sequence b, every KV head g, gets
+ * k_new[b*src_row_stride + g*head_dim + d] (and v likewise), converted to the
+ * pool dtype (fp32 -> bf16 round to nearest even). positions is device int32
+ * [batch], each clamped to [0, capacity). src_dtype is the element type of
+ * k_new / v_new; src_row_stride (elements, 0 = num_kv_heads*head_dim) lets the
+ * rows come straight from a fused QKV projection output. Re-running the call
+ * rewrites the same bytes (idempotent).
+ */
+dfx_status dfx_kv_append_primary(const dfx_kv_cache *kv, int32_t batch, const int32_t *positions,
+                                 int32_t src_dtype, const void *k_new, const void *v_new,
+                                 int64_t src_row_stride, void *stream);
+
+/*
+ * Grouped shared-weight linear: one pass over W for the rows of every flow
+ * (same page, section "Architettura Core": both flows share the attention,
+ * MLP and output matrices; section "Costi di Inferenza vs. Addestramento":
+ * the flows are grouped so decode reads no extra unique weights).
+ *
+ *   Y[f][r][n] = sum_k bf16(X[f][r][k]) * W[n][k]          (fp32 accumulate)
+ *   if couple && n_flows == 2:  Y[1][r][n] += couple[n] * Y[0][r][n]
+ *   if residual:                Y[f][r][n] += residual[f][r][n]
+ *   y = Y (fp32) or bf16(Y)
+ *
+ *  x        device [n_flows][rows][in_features], x_dtype (fp32 rows are rounded
+ *           to bf16 on load), 16-byte aligned, in_features a multiple of 32.
+ *  w        device bf16 [out_features][in_features], out_features a multiple of 16.
+ *  y        device [n_flows][rows][out_features] of y_dtype; may alias residual
+ *           (in-place residual update), must not overlap x or w.
+ *  couple   device fp32 [out_features] or NULL; residual device fp32 or NULL.
+ *  workspace  device scratch of >= dfx_grouped_linear_workspace_size bytes (may be
+ *           NULL when that is 0). It must be zero-filled before its first use; every
+ *           completed call leaves it ready for the next one (its arrival counters
+ *           back at zero). Calls sharing one workspace must not overlap in time.
+ * The K-reduction order of every output element is fixed by (in_features,
+ * out_features) alone: flow-0 outputs are bit-identical for n_flows 1 and 2
+ * and for any row count.
+ */
+dfx_status dfx_grouped_linear_workspace_size(int32_t n_flows, int32_t rows, int32_t in_features,
+                                             int32_t out_features, size_t *bytes);
+
+dfx_status dfx_grouped_linear(int32_t n_flows, int32_t rows, int32_t in_features,
+                              int32_t out_features, int32_t x_dtype, const void *x,
+                              const uint16_t *w, int32_t y_dtype, void *y, const float *couple,
+                              const float *residual, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
+ * RMSNorm with one gain vector shared by all rows (the flows add no
+ * parameters besides embeddings and coupling vectors: same page, section
+ * "Costi di Inferenza vs. Addestramento"):
+ *   y[r][i] = bf16( x[r][i] / sqrt(mean_j x[r][j]^2 + eps) * gain[i] )
+ *  x device fp32 [rows][dim], gain device fp32 [dim], y device bf16 [rows][dim];
+ *  dim a multiple of 4, at most 16384.
+ */
+dfx_status dfx_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
+                       uint16_t *y, void *stream);
+
+/*
+ * SwiGLU activation with the MLP-intermediate coupling b (same page, section
+ * "Meccanismi Chiave": one-way primary -> auxiliary vectors at the
+ * MLP-intermediate level; the formula is this library's reading):
+ *   inter[f][r][i] = silu(gu[f][r][i]) * gu[f][r][dim + i]
+ *   if b && n_flows == 2:  inter[1][r][i] += b[i] * inter[0][r][i]
+ *   out = bf16(inter)
+ *  gate_up device fp32 [n_flows][rows][2*dim] ([gate | up] per row),
+ *  b device fp32 [dim] or NULL, out device bf16 [n_flows][rows][dim]; dim % 4 == 0.
+ */
+dfx_status dfx_swiglu_couple(int32_t n_flows, int32_t rows, int32_t dim, const float *gate_up,
+                             const float *b, uint16_t *out, void *stream);
+
+/*
+ * Weights of one dual-flow decoder layer. Every matrix is shared by the two
+ * flows; a, b, c are the coupling vectors at the query, MLP-intermediate and
+ * MLP-output levels (same page, sections "Architettura Core" and "Meccanismi
+ * Chiave"). NULL coupling vectors give the minimal two-flow form (separate
+ * rows, shared cache, no coupling; section "Risultati" reports this variant).
+ * All pointers are device pointers; matrices are bf16 row-major [out][in].
+ */
+typedef struct dfx_layer_weights {
+  int32_t hidden;             /* model width; a multiple of 32, at most 16384 */
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;           /* 64 or 128; num_q_heads * head_dim may differ from hidden */
+  int32_t intermediate;       /* MLP width; a multiple of 32 */
+  float rms_eps;
+  const float *attn_norm_gain;     /* [hidden] */
+  const uint16_t *w_qkv;           /* [(num_q_heads + 2*num_kv_heads)*head_dim][hidden]: Q, K, V rows */
+  const uint16_t *w_o;             /* [hidden][num_q_heads*head_dim] */
+  const float *mlp_norm_gain;      /* [hidden] */
+  const uint16_t *w_gate_up;       /* [2*intermediate][hidden]: gate rows, then up rows */
+  const uint16_t *w_down;          /* [hidden][intermediate] */
+  const float *couple_a;           /* [head_dim] (one vector for all heads) or NULL */
+  const float *couple_b;           /* [intermediate] or NULL */
+  const float *couple_c;           /* [hidden] or NULL */
+} dfx_layer_weights;
+
+/* Workspace bytes dfx_dual_flow_decode_layer needs for these sizes. */
+dfx_status dfx_dual_flow_decode_layer_workspace_size(const dfx_layer_weights *w,
+                                                     const dfx_kv_cache *kv, int32_t batch,
+                                                     int32_t n_flows, int32_t max_context,
+                                                     size_t *bytes);
+
+/*
+ * One decode step of one layer for both flows (n_flows = 2) or the primary
+ * alone (n_flows = 1), in place on the fp32 residual rows x [n_flows][batch][hidden]:
+ *   h  = rmsnorm(x, attn_norm_gain)                               (bf16)
+ *   qkv = h W_qkv^T                                               (one weight pass, both flows)
+ *   append K, V columns of the flow-0 rows at position context_lens[b] - 1
+ *   o  = dfx_decode_attn(Q1 = flow-0 Q columns, q2_raw = flow-1 Q columns, a)
+ *   x += o W_o^T                                                  (o rounded to bf16 on load)
+ *   h  = rmsnorm(x, mlp_norm_gain)
+ *   inter = swiglu_couple(h W_gate_up^T, b)
+ *   m  = inter W_down^T;  m[1] += c * m[0];  x += m
+ * context_lens (device int32 [batch]) counts the positions attended in this
+ * step, the new one included (>= 1). The flow-1 K, V columns are computed by
+ * the shared projection and discarded. workspace: >= the size above, zero-filled
+ * before its first use (as for dfx_grouped_linear; calls leave it reusable).
+ */
+dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv,
+                                      const int32_t *context_lens, int32_t batch,
+                                      int32_t max_context, int32_t n_flows, float *x,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Measurement helpers (not part of the method): a plain device copy of
+ * `bytes` (multiple of 16, both pointers 16-byte aligned) used to calibrate
+ * hardware traffic counters, and a write of `bytes` used to evict caches
+ * between timed iterations.
+ */
+dfx_status dfx_copy_bytes(void *dst, const void *src, size_t bytes, void *stream);
+dfx_status dfx_fill_bytes(void *dst, size_t bytes, uint32_t pattern, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFX_H */

@@ -1,0 +1,74 @@
+"""Helpers for GPU tests: move seeded cases to the device, compare with the oracle."""
+import numpy as np
+import torch
+
+import dual_flow_shared_amd as dfx
+
+
+def dev(a, dtype=None):
+    """numpy -> cuda tensor; uint16 arrays become bfloat16 tensors with the same bits."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    t = torch.from_numpy(a).cuda()
+    return t if dtype is None else t.to(dtype)
+
+
+def host_bits(t):
+    """cuda bfloat16 tensor -> numpy uint16 bit patterns."""
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def cache_of(case):
+    return dfx.KVCache(dev(case.k_pool), dev(case.v_pool),
+                       None if case.block_table is None else dev(case.block_table))
+
+
+def run_attn(case, cache=None, q2=True, a=True, num_splits=0, max_context=None, q1=None, q2v=None):
+    cache = cache_of(case) if cache is None else cache
+    ctx = dev(case.context_lens)
+    mc = int(case.context_lens.max()) if max_context is None else max_context
+    q1t = dev(case.q1 if q1 is None else q1)
+    q2t = (dev(case.q2 if q2v is None else q2v) if q2 else None)
+    at = dev(case.a) if (a and q2) else None
+    o1, o2, lse = dfx.decode_attn(q1t, q2t, at, cache=cache, context_lens=ctx, max_context=mc,
+                                  num_splits=num_splits)
+    torch.cuda.synchronize()
+    return (o1.cpu().numpy().astype(np.float64),
+            None if o2 is None else o2.cpu().numpy().astype(np.float64),
+            lse.cpu().numpy().astype(np.float64))
+
+
+def max_err(a, b, rows=None):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    if rows is not None:
+        a, b = a[rows], b[rows]
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def lse_err(a, b):
+    """max |a - b| over finite entries; -inf must match -inf."""
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    inf = np.isneginf(b)
+    assert np.array_equal(np.isneginf(a), inf)
+    return float(np.max(np.abs(a[~inf] - b[~inf]))) if (~inf).any() else 0.0
+
+
+def bf16_decisions_agree(gpu_bits, oracle_fp64, rel=2e-6, scale=None):
+    """bf16 outputs: equal bits, except where the oracle's unrounded value sits within
+    rel * scale of a rounding midpoint (scale: magnitude of the operands that formed the
+    value, default the value itself) -- there the fp32 kernel may take either neighbour.
+    Returns the fraction of exactly equal elements."""
+    from oracle.numerics import bf16_bits, widen
+    want = bf16_bits(oracle_fp64)
+    got = np.asarray(gpu_bits, np.uint16)
+    same = got == want
+    if not same.all():
+        x = np.asarray(oracle_fp64, np.float64)[~same]
+        sc = np.abs(x) if scale is None else np.asarray(scale, np.float64)[~same]
+        g = widen(got[~same])
+        w = widen(want[~same])
+        mid = (g + w) / 2
+        ok = (np.abs(x - mid) <= rel * sc + 1e-30) & (np.abs(g - w) <= np.abs(w) * 2.0 ** -7 + 1e-38)
+        assert ok.all(), f"{(~ok).sum()} bf16 outputs disagree beyond a rounding midpoint"
+    return float(same.mean())

@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+rejects bad arguments on the host before any HIP call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dual_flow_shared_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dfx.h")
+FAKE = 0x10000          # aligned, never dereferenced: every call below fails validation first
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:dfx_status|int|const char \*)\s*(dfx_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = _abi.lib()
+    names = declared()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _abi.SIGNATURES, n
+    assert set(_abi.SIGNATURES) == set(names)
+    assert lib.dfx_version() == 100
+
+
+def kv(dtype=1, heads=8, D=128, bs=16, nb=100, table=FAKE, mb=64):
+    s = _abi.KVCacheStruct()
+    s.dtype, s.num_kv_heads, s.head_dim, s.block_size, s.num_blocks = dtype, heads, D, bs, nb
+    s.k = s.v = FAKE
+    s.block_table, s.max_blocks_per_seq, s.reserved = table, mb, 0
+    return s
+
+
+def attn(k, **over):
+    a = dict(ctx=FAKE, batch=2, maxc=100, hq=32, qdt=1, q1=FAKE, q2=FAKE, qs=0, a=FAKE, ast=0,
+             scale=0.0, o1=FAKE, o2=FAKE, lse=None, splits=0, ws=None, wsb=0)
+    a.update(over)
+    lib = _abi.lib()
+    st = lib.dfx_decode_attn(ctypes.byref(k), a["ctx"], a["batch"], a["maxc"], a["hq"], a["qdt"], a["q1"],
+                             a["q2"], a["qs"], a["a"], a["ast"], a["scale"], a["o1"], a["o2"], a["lse"],
+                             a["splits"], a["ws"], a["wsb"], None)
+    return st, lib.dfx_last_error().decode()
+
+
+@pytest.mark.parametrize("kvover,over,status,needle", [
+    (dict(D=96), {}, 2, "head_dim"),
+    (dict(dtype=7), {}, 1, "dtype"),
+    (dict(bs=24), {}, 1, "power of two"),
+    (dict(heads=0), {}, 1, "num_kv_heads"),
+    ({}, dict(hq=30), 1, "multiple"),
+    ({}, dict(maxc=64 * 16 + 1), 1, "capacity"),
+    ({}, dict(o2=None), 1, "both"),
+    ({}, dict(q2=None, o2=None), 1, "without q2"),
+    ({}, dict(ast=5), 1, "a_head_stride"),
+    ({}, dict(qs=4100), 1, "q_batch_stride"),
+    ({}, dict(q1=FAKE + 4), 1, "aligned"),
+    ({}, dict(ctx=None), 1, "context_lens"),
+    ({}, dict(qdt=5), 1, "q_dtype"),
+    ({}, dict(splits=-1), 1, "num_splits"),
+    ({}, dict(maxc=4096 + 0, splits=4), 1, "capacity"),
+    (dict(mb=1024), dict(maxc=4096, splits=4, ws=None, wsb=0), 3, "workspace"),
+    (dict(heads=1), dict(hq=64), 2, "query rows"),
+])
+def test_attention_rejects(kvover, over, status, needle):
+    st, msg = attn(kv(**kvover), **over)
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_plan_is_host_arithmetic():
+    lib = _abi.lib()
+    s, n = ctypes.c_int32(), ctypes.c_size_t()
+    k = kv(mb=8192, nb=65536)
+    assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 0, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value > 1 and n.value >= s.value * 2 * 8 * 64 * 129 * 4
+    assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 1, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value == 1 and n.value == 0
+    assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 7, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value == 7
+    # the plan does not depend on the number of flows (primary results stay bit-identical)
+    s1 = ctypes.c_int32()
+    lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 1, 131072, 0, ctypes.byref(s1), ctypes.byref(n))
+    lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 0, ctypes.byref(s), ctypes.byref(n))
+    assert s.value == s1.value
+
+
+def test_linear_and_glue_reject():
+    lib = _abi.lib()
+    n = ctypes.c_size_t()
+    assert lib.dfx_grouped_linear_workspace_size(3, 4, 64, 64, ctypes.byref(n)) == 1
+    assert lib.dfx_grouped_linear_workspace_size(2, 4, 48, 64, ctypes.byref(n)) == 2
+    assert lib.dfx_grouped_linear_workspace_size(2, 4, 64, 24, ctypes.byref(n)) == 2
+    assert lib.dfx_grouped_linear_workspace_size(2, 32, 4096, 4096, ctypes.byref(n)) == 0 and n.value > 0
+    st = lib.dfx_grouped_linear(2, 32, 4096, 4096, 1, FAKE, FAKE, 0, FAKE, None, None, None, 0, None)
+    assert st == 3 and "workspace" in lib.dfx_last_error().decode()
+    assert lib.dfx_grouped_linear(2, 4, 64, 64, 9, FAKE, FAKE, 0, FAKE, None, None, None, 0, None) == 1
+    assert lib.dfx_grouped_linear(2, 4, 64, 64, 1, FAKE + 8, FAKE, 0, FAKE, None, None, None, 0, None) == 1
+    assert lib.dfx_rmsnorm(4, 30, FAKE, FAKE, 1e-5, FAKE, None) == 1
+    assert lib.dfx_rmsnorm(4, 64, None, FAKE, 1e-5, FAKE, None) == 1
+    assert lib.dfx_swiglu_couple(3, 4, 64, FAKE, None, FAKE, None) == 1
+    assert lib.dfx_copy_bytes(FAKE, FAKE, 17, None) == 1
+    assert lib.dfx_fill_bytes(FAKE + 4, 32, 0, None) == 1
+    k = kv()
+    assert lib.dfx_kv_append_primary(ctypes.byref(k), 2, FAKE, 0, FAKE, FAKE, 12, None) == 1
+    assert lib.dfx_kv_append_primary(ctypes.byref(k), 2, FAKE, 3, FAKE, FAKE, 0, None) == 1
+
+
+def test_layer_rejects():
+    lib = _abi.lib()
+    w = _abi.LayerWeightsStruct()
+    w.hidden, w.num_q_heads, w.num_kv_heads, w.head_dim, w.intermediate, w.rms_eps = 4096, 32, 8, 128, 14336, 1e-5
+    for f in ("attn_norm_gain", "w_qkv", "w_o", "mlp_norm_gain", "w_gate_up", "w_down"):
+        setattr(w, f, FAKE)
+    k = kv(mb=512, nb=16384)
+    n = ctypes.c_size_t()
+    assert lib.dfx_dual_flow_decode_layer_workspace_size(ctypes.byref(w), ctypes.byref(k), 32, 2, 8192, ctypes.byref(n)) == 0
+    assert n.value > 32 * 2 * 6144 * 4
+    assert lib.dfx_dual_flow_decode_layer(ctypes.byref(w), ctypes.byref(k), FAKE, 32, 8192, 2, FAKE, None, 0, None) == 3
+    w.head_dim = 64
+    assert lib.dfx_dual_flow_decode_layer_workspace_size(ctypes.byref(w), ctypes.byref(k), 32, 2, 8192, ctypes.byref(n)) == 1
+    w.head_dim = 128
+    k32 = kv(dtype=0, mb=512, nb=16384)
+    assert lib.dfx_dual_flow_decode_layer_workspace_size(ctypes.byref(w), ctypes.byref(k32), 32, 2, 8192, ctypes.byref(n)) == 2
