@@ -129,7 +129,7 @@ def main():
         c = gen.config_layer()
         B, F, H = c.batch, 2, c.hidden
         kv = dfx.KVCache(dev(c.cache.k_pool), dev(c.cache.v_pool), dev(c.cache.block_table))
-        w = dfx.LayerWeights(dev(c.g_attn), dev(c.w_qkv), dev(c.w_o), dev(c.g_mlp), dev(c.w_gate_up),
+        w = dfx.LayerWeights.from_row_major(dev(c.g_attn), dev(c.w_qkv), dev(c.w_o), dev(c.g_mlp), dev(c.w_gate_up),
                              dev(c.w_down), c.num_q_heads, c.num_kv_heads, c.head_dim, c.eps,
                              dev(c.a), dev(c.b), dev(c.c))
         ctx_np = c.cache.context_lens + 1

@@ -12,10 +12,11 @@ from typing import Optional
 
 import torch
 
-from ._abi import (DFX_BF16, DFX_F32, DfxError, KVCacheStruct, LayerWeightsStruct, check, lib)
+from ._abi import (DFX_BF16, DFX_F32, DFX_W_PACKED, DFX_W_ROW_MAJOR, DfxError, KVCacheStruct,
+                   LayerWeightsStruct, check, lib)
 
 __all__ = ["DfxError", "KVCache", "LayerWeights", "decode_attn", "decode_attn_plan",
-           "kv_append_primary", "grouped_linear", "rmsnorm", "swiglu_couple",
+           "kv_append_primary", "grouped_linear", "pack_weight", "rmsnorm", "swiglu_couple",
            "dual_flow_decode_layer", "layer_workspace_size", "copy_bytes", "fill_bytes",
            "Workspace", "version"]
 
@@ -179,11 +180,22 @@ def kv_append_primary(cache: KVCache, positions: torch.Tensor, k_new: torch.Tens
                                       _ptr(k_new), _ptr(v_new), k_new.stride(0), _stream(stream)))
 
 
-def grouped_linear(x: torch.Tensor, w: torch.Tensor, *, y_dtype=torch.float32,
+def pack_weight(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """Row-major bf16 W [N][K] -> the same matrix in DFX_W_PACKED fragment order (a new
+    [N][K]-sized tensor; the shape is kept for bookkeeping, the element order is not)."""
+    w = _contig(w, "w")
+    N, K = w.shape
+    out = torch.empty_like(w)
+    check(lib().dfx_pack_weight(N, K, _ptr(w), _ptr(out), _stream(stream)))
+    return out
+
+
+def grouped_linear(x: torch.Tensor, w: torch.Tensor, *, packed: bool = False, y_dtype=torch.float32,
                    couple: Optional[torch.Tensor] = None, residual: Optional[torch.Tensor] = None,
                    out: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None,
                    stream=None) -> torch.Tensor:
-    """Y[f] = bf16(X[f]) W^T (+ couple, + residual) for x [F][rows][K], w bf16 [N][K]."""
+    """Y[f] = bf16(X[f]) W^T (+ couple, + residual) for x [F][rows][K], w bf16 [N][K]
+    (row-major, or packed by pack_weight when ``packed``)."""
     F, rows, K = x.shape
     N = w.shape[0]
     x, w = _contig(x, "x"), _contig(w, "w")
@@ -193,7 +205,8 @@ def grouped_linear(x: torch.Tensor, w: torch.Tensor, *, y_dtype=torch.float32,
     n = ctypes.c_size_t()
     check(lib().dfx_grouped_linear_workspace_size(F, rows, K, N, ctypes.byref(n)))
     ws = _workspace(workspace, x.device, "linear").get(n.value) if n.value else None
-    check(lib().dfx_grouped_linear(F, rows, K, N, _dtype_code(x), _ptr(x), _ptr(w), _dtype_code(y),
+    check(lib().dfx_grouped_linear(F, rows, K, N, _dtype_code(x), _ptr(x), _ptr(w),
+                                   DFX_W_PACKED if packed else DFX_W_ROW_MAJOR, _dtype_code(y),
                                    _ptr(y), _ptr(couple), _ptr(residual), _ptr(ws), n.value,
                                    _stream(stream)))
     return y
@@ -220,7 +233,8 @@ def swiglu_couple(gate_up: torch.Tensor, b: Optional[torch.Tensor] = None, out=N
 
 @dataclass
 class LayerWeights:
-    """Device weights of one dual-flow layer (matrices bf16 [out][in], vectors fp32)."""
+    """Device weights of one dual-flow layer: the four matrices bf16 [out][in] in packed
+    fragment order (see ``LayerWeights.from_row_major``), vectors fp32."""
     attn_norm_gain: torch.Tensor
     w_qkv: torch.Tensor
     w_o: torch.Tensor
@@ -234,6 +248,15 @@ class LayerWeights:
     couple_a: Optional[torch.Tensor] = None
     couple_b: Optional[torch.Tensor] = None
     couple_c: Optional[torch.Tensor] = None
+
+    @classmethod
+    def from_row_major(cls, attn_norm_gain, w_qkv, w_o, mlp_norm_gain, w_gate_up, w_down,
+                       num_q_heads, num_kv_heads, head_dim, eps=1e-5, couple_a=None, couple_b=None,
+                       couple_c=None) -> "LayerWeights":
+        """Pack row-major device matrices once (dfx_pack_weight) and keep the packed copies."""
+        return cls(attn_norm_gain, pack_weight(w_qkv), pack_weight(w_o), mlp_norm_gain,
+                   pack_weight(w_gate_up), pack_weight(w_down), num_q_heads, num_kv_heads,
+                   head_dim, eps, couple_a, couple_b, couple_c)
 
     def struct(self) -> LayerWeightsStruct:
         s = LayerWeightsStruct()

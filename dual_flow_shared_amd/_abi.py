@@ -7,6 +7,7 @@ LIB_PATH = os.path.join(PKG, "libdfx.so")
 
 DFX_OK, DFX_EINVAL, DFX_EUNSUPPORTED, DFX_EWORKSPACE, DFX_EHIP = range(5)
 DFX_F32, DFX_BF16 = 0, 1
+DFX_W_ROW_MAJOR, DFX_W_PACKED = 0, 1
 STATUS_NAMES = {0: "DFX_OK", 1: "DFX_EINVAL", 2: "DFX_EUNSUPPORTED", 3: "DFX_EWORKSPACE", 4: "DFX_EHIP"}
 
 # every function the header declares, with (restype, argtypes)
@@ -46,7 +47,8 @@ SIGNATURES = {
     "dfx_decode_attn": (I32, [KVP, P, I32, I32, I32, I32, P, P, I64, P, I32, F32, P, P, P, I32, P, SZ, P]),
     "dfx_kv_append_primary": (I32, [KVP, I32, P, I32, P, P, I64, P]),
     "dfx_grouped_linear_workspace_size": (I32, [I32, I32, I32, I32, PSZ]),
-    "dfx_grouped_linear": (I32, [I32, I32, I32, I32, I32, P, P, I32, P, P, P, P, SZ, P]),
+    "dfx_grouped_linear": (I32, [I32, I32, I32, I32, I32, P, P, I32, I32, P, P, P, P, SZ, P]),
+    "dfx_pack_weight": (I32, [I32, I32, P, P, P]),
     "dfx_rmsnorm": (I32, [I32, I32, P, P, F32, P, P]),
     "dfx_swiglu_couple": (I32, [I32, I32, I32, P, P, P, P]),
     "dfx_dual_flow_decode_layer_workspace_size": (I32, [LWP, KVP, I32, I32, I32, PSZ]),

@@ -32,13 +32,16 @@ bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kChunkQuantum = 128;  // tokens: 4 waves x 32-token tiles
-constexpr int kMinChunk = 512;
-constexpr int kTargetAttnGroups = 2048;
-constexpr int kTargetGemmGroups = 512;
-// Split-K arrival counters live in a fixed region at the start of a linear workspace, so
-// that a later call with another plan never reads bytes an earlier call used as partials.
-constexpr size_t kCounterBytes = 64 * 1024;
-constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(uint32_t));
+constexpr int kMinChunk = 1024;
+// Launch-shape defaults (compile-time so that alternatives can be measured).
+#ifndef DFX_ATTN_TARGET
+#define DFX_ATTN_TARGET 1024
+#endif
+#ifndef DFX_GEMM_TARGET
+#define DFX_GEMM_TARGET 512
+#endif
+constexpr int kTargetAttnGroups = DFX_ATTN_TARGET;
+constexpr int kTargetGemmGroups = DFX_GEMM_TARGET;
 
 dfx_status check_kv(const dfx_kv_cache *kv, int32_t batch) {
   if (!kv) return fail(DFX_EINVAL, "kv is NULL");
@@ -64,8 +67,16 @@ int64_t capacity(const dfx_kv_cache *kv) {
   return kv->block_table ? (int64_t)kv->max_blocks_per_seq * kv->block_size : kv->block_size;
 }
 
-void attn_plan(int batch, int hkv, int max_ctx, int requested, int *splits, int *chunk) {
+// block_size: paged block size, 0 for a contiguous cache. A paged split must span at
+// most kMaxChunkBlocks - 1 whole blocks (the kernel holds the split's block ids in LDS).
+constexpr int kMaxChunkBlocks = 1024;
+
+void attn_plan(int batch, int hkv, int max_ctx, int requested, int block_size, int *splits,
+               int *chunk) {
   const int max_s = max_ctx > 0 ? (max_ctx + kChunkQuantum - 1) / kChunkQuantum : 1;
+  const int64_t cap = block_size > 0
+      ? ((int64_t)(kMaxChunkBlocks - 1) * block_size) / kChunkQuantum * kChunkQuantum
+      : (int64_t)1 << 30;
   int s;
   if (requested > 0) {
     s = requested < max_s ? requested : max_s;
@@ -77,11 +88,14 @@ void attn_plan(int batch, int hkv, int max_ctx, int requested, int *splits, int 
     if (s > max_s) s = max_s;
     if (s < 1) s = 1;
   }
-  int c = max_ctx > 0 ? (max_ctx + s - 1) / s : kChunkQuantum;
+  int64_t c = max_ctx > 0 ? (max_ctx + s - 1) / s : kChunkQuantum;
   c = (c + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
-  *chunk = c;
-  *splits = max_ctx > 0 ? (max_ctx + c - 1) / c : 1;
+  if (c > cap) c = cap;
+  *chunk = (int)c;
+  *splits = max_ctx > 0 ? (int)((max_ctx + c - 1) / c) : 1;
 }
+
+int paged_bs(const dfx_kv_cache *kv) { return kv->block_table ? kv->block_size : 0; }
 
 size_t attn_ws_bytes(int splits, int n_flows, int batch, int hq, int d) {
   if (splits <= 1) return 0;
@@ -89,32 +103,33 @@ size_t attn_ws_bytes(int splits, int n_flows, int batch, int hq, int d) {
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
 }
 
+// The linear kernel tiles 64 output features per work-group (16 per wave) and may split K
+// over ksplit work-groups, whose fp32 tiles a second kernel sums in split order.
 struct GemmPlan {
-  int nt, ksplit, tiles, groups;
-  size_t counter_bytes, partial_bytes;
-  size_t total() const { return counter_bytes + partial_bytes; }
+  int ksplit, tiles, groups;
+  size_t partial_bytes;
+  size_t total() const { return partial_bytes; }
 };
 
 GemmPlan gemm_plan(int n_flows, int rows, int K, int N) {
   GemmPlan g{};
-  const int per_group = n_flows * rows < 64 ? n_flows * rows : 64;
-  g.nt = (N % 64 == 0 && per_group > 32) ? 64 : (N % 32 == 0 ? 32 : 16);
-  g.tiles = N / g.nt;
+  g.tiles = (N + 63) / 64;
   const int nks = K / 32;
   int ks = (kTargetGemmGroups + g.tiles - 1) / g.tiles;
-  const int max_ks = nks / 8 > 1 ? nks / 8 : 1;  // keep >= 8 k-steps (2 per wave) per group
+  const int max_ks = nks / 16 > 1 ? nks / 16 : 1;  // keep >= 16 k-steps per work-group
   if (ks > max_ks) ks = max_ks;
-  if (ks > 8) ks = 8;
+  if (ks > 16) ks = 16;
   if (ks < 1) ks = 1;
+  if (K % 256 == 0) {
+    // the chunked kernel splits K into whole 256-column chunks: `per` chunks per split
+    const int nch = K / 256;
+    const int per = (nch + ks - 1) / ks;
+    ks = (nch + per - 1) / per;
+  }
   g.ksplit = ks;
   const int rpg = 64 / n_flows;
   g.groups = rows > 0 ? (rows + rpg - 1) / rpg : 0;
-  if ((int64_t)g.groups * g.tiles > kMaxCounters) ks = 1;
-  g.ksplit = ks;
-  if (ks > 1) {
-    g.counter_bytes = kCounterBytes;
-    g.partial_bytes = (size_t)ks * g.groups * g.tiles * 64 * g.nt * sizeof(float);
-  }
+  if (ks > 1) g.partial_bytes = round_up((size_t)ks * g.groups * 64 * N * sizeof(float), 256);
   return g;
 }
 
@@ -126,31 +141,30 @@ dfx_status check_linear(int32_t n_flows, int32_t rows, int32_t K, int32_t N) {
   return DFX_OK;
 }
 
-// counters: zero-filled region of >= plan.counter_bytes; partial: >= plan.partial_bytes.
+// partial: >= plan.partial_bytes of scratch (unused when the plan has one K split).
 dfx_status run_linear_parts(int32_t n_flows, int32_t rows, int32_t K, int32_t N, int x_f32,
-                            const void *x, const uint16_t *w, int y_bf16, void *y,
-                            const float *couple, const float *residual, uint32_t *counters,
-                            float *partial, hipStream_t s) {
+                            const void *x, const uint16_t *w, int w_packed, int y_bf16, void *y,
+                            const float *couple, const float *residual, float *partial,
+                            hipStream_t s) {
   if (rows == 0) return DFX_OK;
   const GemmPlan g = gemm_plan(n_flows, rows, K, N);
   GemmArgs a{};
   a.n_flows = n_flows; a.rows = rows; a.K = K; a.N = N;
-  a.x_f32 = x_f32; a.x = x; a.w = w; a.y_bf16 = y_bf16; a.y = y;
+  a.x_f32 = x_f32; a.x = x; a.w = w; a.w_packed = w_packed; a.y_bf16 = y_bf16; a.y = y;
   a.couple = couple; a.residual = residual; a.ksplit = g.ksplit;
-  a.counters = g.ksplit > 1 ? counters : nullptr;
   a.partial = g.ksplit > 1 ? partial : nullptr;
-  return hip_status(launch_grouped_linear(a, g.nt, s), "grouped_linear launch");
+  return hip_status(launch_grouped_linear(a, s), "grouped_linear launch");
 }
 
 dfx_status run_linear(int32_t n_flows, int32_t rows, int32_t K, int32_t N, int x_f32, const void *x,
-                      const uint16_t *w, int y_bf16, void *y, const float *couple,
+                      const uint16_t *w, int w_packed, int y_bf16, void *y, const float *couple,
                       const float *residual, void *ws, size_t ws_bytes, hipStream_t s) {
   if (rows == 0) return DFX_OK;
   const GemmPlan g = gemm_plan(n_flows, rows, K, N);
   if (g.total() > 0 && (!ws || ws_bytes < g.total()))
     return fail(DFX_EWORKSPACE, "grouped_linear needs %zu workspace bytes, got %zu", g.total(), ws_bytes);
-  return run_linear_parts(n_flows, rows, K, N, x_f32, x, w, y_bf16, y, couple, residual,
-                          (uint32_t *)ws, (float *)((char *)ws + g.counter_bytes), s);
+  return run_linear_parts(n_flows, rows, K, N, x_f32, x, w, w_packed, y_bf16, y, couple,
+                          residual, (float *)ws, s);
 }
 
 struct AttnCall {
@@ -166,6 +180,7 @@ struct AttnCall {
   int32_t splits;
   void *ws;
   size_t ws_bytes;
+  int32_t o_bf16;  // layer-internal: outputs rounded to bf16 (the rows entering W_o)
 };
 
 dfx_status validate_attn(const AttnCall &c) {
@@ -204,7 +219,7 @@ dfx_status run_attn(const AttnCall &c, hipStream_t s) {
   const dfx_kv_cache *kv = c.kv;
   const int F = c.q2 ? 2 : 1, G = c.hq / kv->num_kv_heads;
   int splits, chunk;
-  attn_plan(c.batch, kv->num_kv_heads, c.max_context, c.splits, &splits, &chunk);
+  attn_plan(c.batch, kv->num_kv_heads, c.max_context, c.splits, paged_bs(kv), &splits, &chunk);
   const size_t need = attn_ws_bytes(splits, F, c.batch, c.hq, kv->head_dim);
   if (need && (!c.ws || c.ws_bytes < need))
     return fail(DFX_EWORKSPACE, "decode_attn needs %zu workspace bytes for %d splits, got %zu", need, splits, c.ws_bytes);
@@ -220,14 +235,16 @@ dfx_status run_attn(const AttnCall &c, hipStream_t s) {
   a.a = c.a; a.a_hstride = c.a_stride;
   const float scale = c.scale > 0.f ? c.scale : 1.0f / sqrtf((float)kv->head_dim);
   a.scale_log2 = scale * kLog2e;
-  a.o1 = c.o1; a.o2 = c.o2; a.lse = c.lse;
+  a.o1 = c.o1; a.o2 = c.o2; a.lse = c.lse; a.o_bf16 = c.o_bf16;
   a.num_splits = splits; a.chunk = chunk;
   if (splits > 1) {
     const size_t rows = (size_t)splits * F * c.batch * c.hq;
     a.part_o = (float *)c.ws;
     a.part_lse = (float *)((char *)c.ws + round_up(rows * kv->head_dim * sizeof(float), 256));
   }
-  const bool mfma = a.kv_bf16 && F * G <= 16;
+  // matrix-core path: bf16 cache, at most 16 query rows per KV head, paged blocks of
+  // >= 16 tokens (a 16-token half tile then lies in one block)
+  const bool mfma = a.kv_bf16 && F * G <= 16 && (!kv->block_table || kv->block_size >= 16);
   hipError_t e = mfma ? launch_attn_mfma(a, s) : launch_attn_valu(a, s);
   if (e != hipSuccess) return hip_status(e, "decode_attn launch");
   if (splits > 1) return hip_status(launch_attn_merge(a, s), "decode_attn merge launch");
@@ -255,7 +272,7 @@ dfx_status dfx_decode_attn_plan(const dfx_kv_cache *kv, int32_t batch, int32_t n
     return fail(DFX_EINVAL, "bad plan arguments");
   if (max_context > capacity(kv)) return fail(DFX_EINVAL, "max_context above cache capacity");
   int s, c;
-  attn_plan(batch, kv->num_kv_heads, max_context, num_splits, &s, &c);
+  attn_plan(batch, kv->num_kv_heads, max_context, num_splits, paged_bs(kv), &s, &c);
   if (splits_out) *splits_out = s;
   if (workspace_bytes) *workspace_bytes = attn_ws_bytes(s, n_flows, batch, num_q_heads, kv->head_dim);
   return DFX_OK;
@@ -270,7 +287,7 @@ dfx_status dfx_decode_attn(const dfx_kv_cache *kv, const int32_t *context_lens, 
                            void *workspace, size_t workspace_bytes, void *stream) {
   DFX_BEGIN
   AttnCall c{kv, context_lens, batch, max_context, num_q_heads, q_dtype, q1, q2_raw, q_batch_stride,
-             a, a_head_stride, softmax_scale, o1, o2, lse, num_splits, workspace, workspace_bytes};
+             a, a_head_stride, softmax_scale, o1, o2, lse, num_splits, workspace, workspace_bytes, 0};
   return run_attn(c, (hipStream_t)stream);
   DFX_END
 }
@@ -308,21 +325,36 @@ dfx_status dfx_grouped_linear_workspace_size(int32_t n_flows, int32_t rows, int3
 
 dfx_status dfx_grouped_linear(int32_t n_flows, int32_t rows, int32_t in_features,
                               int32_t out_features, int32_t x_dtype, const void *x,
-                              const uint16_t *w, int32_t y_dtype, void *y, const float *couple,
-                              const float *residual, void *workspace, size_t workspace_bytes,
-                              void *stream) {
+                              const uint16_t *w, int32_t w_layout, int32_t y_dtype, void *y,
+                              const float *couple, const float *residual, void *workspace,
+                              size_t workspace_bytes, void *stream) {
   DFX_BEGIN
   dfx_status st = check_linear(n_flows, rows, in_features, out_features);
   if (st) return st;
   if (x_dtype != DFX_F32 && x_dtype != DFX_BF16) return fail(DFX_EINVAL, "x_dtype %d", x_dtype);
   if (y_dtype != DFX_F32 && y_dtype != DFX_BF16) return fail(DFX_EINVAL, "y_dtype %d", y_dtype);
+  if (w_layout != DFX_W_ROW_MAJOR && w_layout != DFX_W_PACKED) return fail(DFX_EINVAL, "w_layout %d", w_layout);
   if (rows > 0 && (!x || !w || !y)) return fail(DFX_EINVAL, "x / w / y is NULL");
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (residual && !aligned16(residual)))
     return fail(DFX_EINVAL, "x / w / y / residual not 16-byte aligned");
   if (couple && ((uintptr_t)couple & 3)) return fail(DFX_EINVAL, "couple not 4-byte aligned");
   return run_linear(n_flows, rows, in_features, out_features, x_dtype == DFX_F32, x, w,
-                    y_dtype == DFX_BF16, y, couple, residual, workspace, workspace_bytes,
-                    (hipStream_t)stream);
+                    w_layout == DFX_W_PACKED, y_dtype == DFX_BF16, y, couple, residual, workspace,
+                    workspace_bytes, (hipStream_t)stream);
+  DFX_END
+}
+
+dfx_status dfx_pack_weight(int32_t out_features, int32_t in_features, const uint16_t *w,
+                           uint16_t *packed, void *stream) {
+  DFX_BEGIN
+  if (out_features < 16 || out_features % 16 || in_features < 32 || in_features % 32)
+    return fail(DFX_EINVAL, "pack_weight needs N %% 16 == 0 and K %% 32 == 0 (got %d x %d)", out_features, in_features);
+  if (!w || !packed || !aligned16(w) || !aligned16(packed)) return fail(DFX_EINVAL, "w / packed NULL or misaligned");
+  const size_t bytes = (size_t)out_features * in_features * 2;
+  if ((const char *)w < (const char *)packed + bytes && (const char *)packed < (const char *)w + bytes)
+    return fail(DFX_EINVAL, "w and packed overlap");
+  return hip_status(launch_pack_weight(out_features, in_features, w, packed, (hipStream_t)stream),
+                    "pack_weight launch");
   DFX_END
 }
 
@@ -353,7 +385,7 @@ dfx_status dfx_swiglu_couple(int32_t n_flows, int32_t rows, int32_t dim, const f
 namespace {
 
 struct LayerPlan {
-  size_t h, qkv, o, gu, attn_ws, counters, partials, total;
+  size_t h, qkv, o, gu, attn_ws, partials, total;
   int splits;
 };
 
@@ -383,19 +415,16 @@ dfx_status layer_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_
   p.gu = a256((size_t)F * B * 2 * I * 4);
   // (the bf16 MLP intermediate reuses the h buffer)
   int chunk;
-  attn_plan(B, kv->num_kv_heads, max_context, 0, &p.splits, &chunk);
+  attn_plan(B, kv->num_kv_heads, max_context, 0, paged_bs(kv), &p.splits, &chunk);
   p.attn_ws = a256(attn_ws_bytes(p.splits, F, B, Hq, D));
-  // one counter region (zero between calls) shared by the four projections, which run
-  // one after another on the stream, then one partial region
+  // one split-K partial region shared by the four projections (they run in stream order)
   const int shapes[4][2] = {{H, Nqkv}, {Hq * D, H}, {H, 2 * I}, {I, H}};
   for (auto &sh : shapes) {
     const GemmPlan g = gemm_plan(F, B, sh[0], sh[1]);
-    p.counters = g.counter_bytes > p.counters ? g.counter_bytes : p.counters;
     p.partials = g.partial_bytes > p.partials ? g.partial_bytes : p.partials;
   }
-  p.counters = a256(p.counters);
   p.partials = a256(p.partials);
-  p.total = p.counters + p.partials + p.h + p.qkv + p.o + p.gu + p.attn_ws;
+  p.total = p.partials + p.h + p.qkv + p.o + p.gu + p.attn_ws;
   *pl = p;
   return DFX_OK;
 }
@@ -433,9 +462,8 @@ dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_c
   const int F = n_flows, B = batch, H = w->hidden, D = w->head_dim, Hq = w->num_q_heads;
   const int Hkv = w->num_kv_heads, Nqkv = (Hq + 2 * Hkv) * D, I = w->intermediate;
   char *base = (char *)workspace;
-  uint32_t *cnt = (uint32_t *)base;
-  float *part = (float *)(base + p.counters);
-  uint16_t *h = (uint16_t *)(base + p.counters + p.partials);
+  float *part = (float *)base;
+  uint16_t *h = (uint16_t *)(base + p.partials);
   float *qkv = (float *)((char *)h + p.h);
   float *o = (float *)((char *)qkv + p.qkv);
   float *gu = (float *)((char *)o + p.o);
@@ -444,19 +472,21 @@ dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_c
   dfx_status r;
   // attention block
   if ((r = hip_status(launch_rmsnorm(rows, H, x, w->attn_norm_gain, w->rms_eps, h, s), "rmsnorm launch"))) return r;
-  if ((r = run_linear_parts(F, B, H, Nqkv, 0, h, w->w_qkv, 0, qkv, nullptr, nullptr, cnt, part, s))) return r;
+  if ((r = run_linear_parts(F, B, H, Nqkv, 0, h, w->w_qkv, 1, 0, qkv, nullptr, nullptr, part, s))) return r;
   if ((r = hip_status(launch_kv_append(*kv, B, context_lens, 1, 1, qkv + Hq * D, qkv + (Hq + Hkv) * D,
                                        Nqkv, s), "kv_append launch"))) return r;
+  // attention writes its rows already rounded to bf16 (the rows entering W_o)
+  uint16_t *ob = (uint16_t *)o;
   AttnCall c{kv, context_lens, B, max_context, Hq, DFX_F32, qkv, F == 2 ? qkv + (size_t)B * Nqkv : nullptr,
-             Nqkv, F == 2 ? w->couple_a : nullptr, 0, 0.f, o, F == 2 ? o + (size_t)B * Hq * D : nullptr,
-             nullptr, 0, aws, p.attn_ws};
+             Nqkv, F == 2 ? w->couple_a : nullptr, 0, 0.f, (float *)ob,
+             F == 2 ? (float *)(ob + (size_t)B * Hq * D) : nullptr, nullptr, 0, aws, p.attn_ws, 1};
   if ((r = run_attn(c, s))) return r;
-  if ((r = run_linear_parts(F, B, Hq * D, H, 1, o, w->w_o, 0, x, nullptr, x, cnt, part, s))) return r;
+  if ((r = run_linear_parts(F, B, Hq * D, H, 0, ob, w->w_o, 1, 0, x, nullptr, x, part, s))) return r;
   // MLP block
   if ((r = hip_status(launch_rmsnorm(rows, H, x, w->mlp_norm_gain, w->rms_eps, h, s), "rmsnorm launch"))) return r;
-  if ((r = run_linear_parts(F, B, H, 2 * I, 0, h, w->w_gate_up, 0, gu, nullptr, nullptr, cnt, part, s))) return r;
+  if ((r = run_linear_parts(F, B, H, 2 * I, 0, h, w->w_gate_up, 1, 0, gu, nullptr, nullptr, part, s))) return r;
   if ((r = hip_status(launch_swiglu(F, B, I, gu, F == 2 ? w->couple_b : nullptr, h, s), "swiglu launch"))) return r;
-  return run_linear_parts(F, B, I, H, 0, h, w->w_down, 0, x, F == 2 ? w->couple_c : nullptr, x, cnt, part, s);
+  return run_linear_parts(F, B, I, H, 0, h, w->w_down, 1, 0, x, F == 2 ? w->couple_c : nullptr, x, part, s);
   DFX_END
 }
 

@@ -29,20 +29,6 @@
 
 namespace dfx {
 
-__device__ __forceinline__ int64_t kv_row(const AttnArgs &p, int b, int g, int pos) {
-  int64_t blk;
-  int slot;
-  if (p.block_shift >= 0) {
-    const uint32_t e = (uint32_t)p.table[(int64_t)b * p.max_blocks + (pos >> p.block_shift)];
-    blk = (uint64_t)e < (uint64_t)p.num_blocks ? (int64_t)e : p.num_blocks - 1;
-    slot = pos & (p.block_size - 1);
-  } else {
-    blk = b;
-    slot = pos;
-  }
-  return ((blk * p.num_kv_heads + g) * (int64_t)p.block_size + slot) * p.head_dim;
-}
-
 template <bool BF16>
 __device__ __forceinline__ void load8(const void *base, int64_t off, float *out) {
   if constexpr (BF16) {
@@ -74,7 +60,9 @@ __device__ __forceinline__ void store_result(const AttnArgs &p, int split, int b
   const float lse2 = L > 0.f ? M + __log2f(L) : -INFINITY;
   if (p.num_splits == 1) {
     float *out = f == 0 ? p.o1 : p.o2;
-    out[((int64_t)b * Hq + h) * D + d] = o;
+    const int64_t oi = ((int64_t)b * Hq + h) * D + d;
+    if (p.o_bf16) ((uint16_t *)out)[oi] = (uint16_t)f32_to_bf16_rne(o);
+    else out[oi] = o;
     if (d == 0 && p.lse) p.lse[((int64_t)f * p.batch + b) * Hq + h] = lse2 * kLn2;
   } else {
     const int64_t row = (((int64_t)split * p.n_flows + f) * p.batch + b) * Hq + h;
@@ -83,12 +71,146 @@ __device__ __forceinline__ void store_result(const AttnArgs &p, int split, int b
   }
 }
 
-template <int D, bool QBF16>
+constexpr int kMaxChunkBlocks = 1024;  // block ids of one split held in LDS
+
+template <int D>
+struct TileRegs {
+  u32x4 kf[2][D / 32];            // K rows of two 16-token blocks (A operand)
+  uint32_t vr[8][D / 32];         // V: D/16 elements of the 8 token rows tau(j, v)
+};
+
+// Element offsets of the first row of each 16-token half of the tile at t0 and the
+// largest in-half index that is still inside [t0, end). A half lies in one block (paged
+// blocks hold >= 16 tokens and halves start 16-aligned); a half entirely past `end`
+// reuses the first half, and rows past `end` are clamped to the last valid one (their
+// scores are masked), so every address stays inside this split's staged blocks.
+template <bool PAGED>
+__device__ __forceinline__ void half_bases(const AttnArgs &p, const int32_t *tbl, int first_blk,
+                                           int b, int g, int t0, int end, int64_t *hb, int *lastx) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int hs = t0 + 16 * h < end ? t0 + 16 * h : t0;
+    int64_t blk;
+    int slot;
+    if constexpr (PAGED) {
+      blk = tbl[(hs >> p.block_shift) - first_blk];
+      slot = hs & (p.block_size - 1);
+    } else {
+      blk = b;
+      slot = hs;
+    }
+    hb[h] = ((blk * p.num_kv_heads + g) * (int64_t)p.block_size + slot) * p.head_dim;
+    lastx[h] = end - 1 - hs;
+  }
+}
+
+// Issue the K (resp. V) loads of the tile described by (hb, lastx).
+template <int D>
+__device__ __forceinline__ void load_k(const uint16_t *kp, const int64_t *hb, const int *lastx,
+                                       int n, int j, TileRegs<D> &r) {
+  constexpr int KS = D / 32;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const uint16_t *row = kp + hb[mb] + (int64_t)min(n, lastx[mb]) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) r.kf[mb][s] = *(const u32x4 *)(row + 8 * (4 * s + j));
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(const uint16_t *vp, const int64_t *hb, const int *lastx,
+                                       int n, int j, TileRegs<D> &r) {
+  constexpr int VEC = D / 16;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int h = v >> 2, x = 4 * j + (v & 3);  // token tau(j, v) = t0 + 16 h + x
+    const uint16_t *src = vp + hb[h] + (int64_t)min(x, lastx[h]) * D + VEC * n;
+    if constexpr (VEC == 8) {
+      const u32x4 y = *(const u32x4 *)src;
+      r.vr[v][0] = y[0]; r.vr[v][1] = y[1]; r.vr[v][2] = y[2]; r.vr[v][3] = y[3];
+    } else {
+      const u32x2 y = *(const u32x2 *)src;
+      r.vr[v][0] = y[0]; r.vr[v][1] = y[1];
+    }
+  }
+}
+
+// Scores of one loaded tile (S^T blocks for its two 16-token halves).
+template <int D>
+__device__ __forceinline__ void tile_scores(const TileRegs<D> &r, const u32x4 *qh, const u32x4 *ql,
+                                            f32x4 *sacc) {
+  constexpr int KS = D / 32;
+  sacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      sacc[mb] = mfma16x16x32(as_bf16x8(r.kf[mb][s]), as_bf16x8(qh[s]), sacc[mb]);
+      sacc[mb] = mfma16x16x32(as_bf16x8(r.kf[mb][s]), as_bf16x8(ql[s]), sacc[mb]);
+    }
+}
+
+// Online-softmax update for query row n (the lane holds 8 of the tile's 32 tokens) and
+// P.V accumulation into O^T.
+template <int D>
+__device__ __forceinline__ void tile_softmax_pv(const AttnArgs &p, const TileRegs<D> &r,
+                                                const f32x4 *sacc, int t0, int end, int j,
+                                                float &m_run, float &l_run, f32x4 *oacc) {
+  constexpr int VEC = D / 16;
+  float sv[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = t0 + 16 * mb + 4 * j + i;
+      const float x = tok < end ? sacc[mb][i] * p.scale_log2 : -INFINITY;
+      sv[4 * mb + i] = x;
+      mx = fmaxf(mx, x);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  const float alpha = exp2f(m_run - m_new);
+  float psum = 0.f;
+  uint32_t phi[8], plo[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const float pv = exp2f(sv[v] - m_new);
+    psum += pv;
+    split_bf16(pv, phi[v], plo[v]);
+  }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  u32x4 pH, pL;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    pH[w] = phi[2 * w] | (phi[2 * w + 1] << 16);
+    pL[w] = plo[2 * w] | (plo[2 * w + 1] << 16);
+  }
+#pragma unroll
+  for (int mb = 0; mb < VEC; ++mb) {
+    oacc[mb] *= alpha;
+    // V^T rows d = VEC*n + mb over tokens tau(j, 0..7): element mb of each loaded row
+    u32x4 af;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x0 = r.vr[2 * w][mb >> 1], x1 = r.vr[2 * w + 1][mb >> 1];
+      af[w] = (mb & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+    }
+    oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pH), oacc[mb]);
+    oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pL), oacc[mb]);
+  }
+}
+
+template <int D, bool QBF16, bool PAGED>
 __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs p) {
   constexpr int KS = D / 32;  // k-steps of the score contraction
   constexpr int VEC = D / 16; // head-dim elements one lane loads per V row; also O^T blocks
   __shared__ float s_o[4][16][D];
   __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ int32_t s_tbl[kMaxChunkBlocks];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -141,84 +263,39 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs p) {
   for (int mb = 0; mb < VEC; ++mb) oacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int t0 = start + 32 * wave; t0 < end; t0 += 128) {
-    // K rows of the two 16-token blocks (A operand rows = tokens t0 + 16 mb + n)
-    u32x4 kf[2][KS];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int64_t base = kv_row(p, b, g, min(t0 + 16 * mb + n, ctx - 1));
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kf[mb][s] = *(const u32x4 *)(kp + base + 8 * (4 * s + j));
+  // Block ids of this chunk go to LDS once, so no K/V load waits on a table load.
+  const int first_blk = PAGED ? (start >> p.block_shift) : 0;
+  if constexpr (PAGED) {
+    const int nblk = end > start ? ((end - 1) >> p.block_shift) - first_blk + 1 : 0;
+    for (int i = threadIdx.x; i < nblk; i += 256) {
+      const uint32_t e = (uint32_t)p.table[(int64_t)b * p.max_blocks + first_blk + i];
+      s_tbl[i] = (uint64_t)e < (uint64_t)p.num_blocks ? (int32_t)e : (int32_t)(p.num_blocks - 1);
     }
-    // V: VEC elements (head-dim VEC*n ..) of the 8 token rows tau(j, v)
-    uint32_t vr[8][VEC / 2];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int tok = min(t0 + (v < 4 ? 4 * j + v : 12 + 4 * j + v), ctx - 1);
-      const uint16_t *src = vp + kv_row(p, b, g, tok) + VEC * n;
-      if constexpr (VEC == 8) {
-        const u32x4 x = *(const u32x4 *)src;
-        vr[v][0] = x[0]; vr[v][1] = x[1]; vr[v][2] = x[2]; vr[v][3] = x[3];
-      } else {
-        const u32x2 x = *(const u32x2 *)src;
-        vr[v][0] = x[0]; vr[v][1] = x[1];
-      }
-    }
+  }
+  __syncthreads();
 
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        sacc[mb] = mfma16x16x32(as_bf16x8(kf[mb][s]), as_bf16x8(qh[s]), sacc[mb]);
-        sacc[mb] = mfma16x16x32(as_bf16x8(kf[mb][s]), as_bf16x8(ql[s]), sacc[mb]);
-      }
-
-    // online softmax over this tile for query row n (lane holds 8 of its 32 tokens)
-    float sv[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 16 * mb + 4 * j + i;
-        const float x = tok < end ? sacc[mb][i] * p.scale_log2 : -INFINITY;
-        sv[4 * mb + i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    float psum = 0.f;
-    uint32_t phi[8], plo[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const float pv = exp2f(sv[v] - m_new);
-      psum += pv;
-      split_bf16(pv, phi[v], plo[v]);
+  // Tiles of a wave are 128 tokens apart (the four waves interleave). The next tile's K
+  // loads are issued as soon as this tile's scores have consumed the K registers, and
+  // its V loads as soon as P.V has consumed the V registers. The steady-state loop has
+  // no conditional loads, so the compiler can wait for exactly the loads it needs.
+  TileRegs<D> tr;
+  int t0 = start + 32 * wave;
+  if (t0 < end) {
+    int64_t hb[2];
+    int lx[2];
+    half_bases<PAGED>(p, s_tbl, first_blk, b, g, t0, end, hb, lx);
+    load_k<D>(kp, hb, lx, n, j, tr);
+    load_v<D>(vp, hb, lx, n, j, tr);
+    f32x4 sacc[2];
+    for (; t0 + 128 < end; t0 += 128) {
+      half_bases<PAGED>(p, s_tbl, first_blk, b, g, t0 + 128, end, hb, lx);
+      tile_scores<D>(tr, qh, ql, sacc);
+      load_k<D>(kp, hb, lx, n, j, tr);
+      tile_softmax_pv<D>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
+      load_v<D>(vp, hb, lx, n, j, tr);
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    u32x4 pH, pL;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      pH[w] = phi[2 * w] | (phi[2 * w + 1] << 16);
-      pL[w] = plo[2 * w] | (plo[2 * w + 1] << 16);
-    }
-#pragma unroll
-    for (int mb = 0; mb < VEC; ++mb) {
-      oacc[mb] *= alpha;
-      // V^T rows d = VEC*n + mb over tokens tau(j, 0..7): element mb of each loaded row
-      u32x4 af;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = vr[2 * w][mb >> 1], x1 = vr[2 * w + 1][mb >> 1];
-        af[w] = (mb & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-      }
-      oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pH), oacc[mb]);
-      oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pL), oacc[mb]);
-    }
+    tile_scores<D>(tr, qh, ql, sacc);
+    tile_softmax_pv<D>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
   }
 
   // ---- combine the four waves (fixed order), then store output or split partial
@@ -251,13 +328,16 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs p) {
 
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s) {
   const dim3 grid(a.num_splits, a.num_kv_heads, a.batch), block(256);
+  const bool paged = a.block_shift >= 0;
+#define DFX_ATTN_LAUNCH(D, QB, PG) attn_mfma_kernel<D, QB, PG><<<grid, block, 0, s>>>(a)
   if (a.head_dim == 128) {
-    if (a.q_bf16) attn_mfma_kernel<128, true><<<grid, block, 0, s>>>(a);
-    else attn_mfma_kernel<128, false><<<grid, block, 0, s>>>(a);
+    if (a.q_bf16) { if (paged) DFX_ATTN_LAUNCH(128, true, true); else DFX_ATTN_LAUNCH(128, true, false); }
+    else { if (paged) DFX_ATTN_LAUNCH(128, false, true); else DFX_ATTN_LAUNCH(128, false, false); }
   } else {
-    if (a.q_bf16) attn_mfma_kernel<64, true><<<grid, block, 0, s>>>(a);
-    else attn_mfma_kernel<64, false><<<grid, block, 0, s>>>(a);
+    if (a.q_bf16) { if (paged) DFX_ATTN_LAUNCH(64, true, true); else DFX_ATTN_LAUNCH(64, true, false); }
+    else { if (paged) DFX_ATTN_LAUNCH(64, false, true); else DFX_ATTN_LAUNCH(64, false, false); }
   }
+#undef DFX_ATTN_LAUNCH
   return hipGetLastError();
 }
 
@@ -285,9 +365,14 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs p) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) O[k] += c * po[lane + 64 * k];
   }
-  float *out = (f == 0 ? p.o1 : p.o2) + ((int64_t)b * Hq + h) * D;
+  float *out = f == 0 ? p.o1 : p.o2;
+  const int64_t ob = ((int64_t)b * Hq + h) * D;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) out[lane + 64 * k] = nvalid ? O[k] / L : 0.f;
+  for (int k = 0; k < PER; ++k) {
+    const float o = nvalid ? O[k] / L : 0.f;
+    if (p.o_bf16) ((uint16_t *)out)[ob + lane + 64 * k] = (uint16_t)f32_to_bf16_rne(o);
+    else out[ob + lane + 64 * k] = o;
+  }
   if (lane == 0 && p.lse)
     p.lse[((int64_t)f * p.batch + b) * Hq + h] = nvalid ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }

@@ -127,7 +127,9 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs p) {
       const float lse2 = L > 0.f ? M + __log2f(L) : -INFINITY;
       if (p.num_splits == 1) {
         float *out = f == 0 ? p.o1 : p.o2;
-        out[((int64_t)b * p.num_q_heads + h) * D + d] = o;
+        const int64_t oi = ((int64_t)b * p.num_q_heads + h) * D + d;
+        if (p.o_bf16) ((uint16_t *)out)[oi] = (uint16_t)f32_to_bf16_rne(o);
+        else out[oi] = o;
         if (d == 0 && p.lse) p.lse[((int64_t)f * p.batch + b) * p.num_q_heads + h] = lse2 * kLn2;
       } else {
         const int64_t row = (((int64_t)split * p.n_flows + f) * p.batch + b) * p.num_q_heads + h;

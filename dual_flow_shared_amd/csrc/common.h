@@ -64,6 +64,7 @@ struct AttnArgs {
   int32_t a_hstride;
   float scale_log2;  // softmax scale * log2(e)
   float *o1, *o2, *lse;
+  int32_t o_bf16;  // o1/o2 hold bf16 (uint16) rows instead of fp32
   float *part_o, *part_lse;  // [S][F][B][Hq][D], [S][F][B][Hq] (log2 domain)
   int32_t num_splits, chunk;
 };
@@ -73,12 +74,12 @@ struct GemmArgs {
   int32_t x_f32;
   const void *x;
   const uint16_t *w;
+  int32_t w_packed;  // DFX_W_PACKED fragment order instead of row-major
   int32_t y_bf16;
   void *y;
   const float *couple, *residual;
-  int32_t ksplit;      // work-groups along K per feature tile
-  float *partial;      // [ksplit][groups][tiles][64][NT] when ksplit > 1
-  uint32_t *counters;  // [groups][tiles] arrival counters (zero between calls)
+  int32_t ksplit;      // work-groups along K per 64-feature tile
+  float *partial;      // [ksplit][groups][64 rows][N] fp32 when ksplit > 1
 };
 
 // Kernel launchers (defined next to their kernels). They assume validated arguments.
@@ -88,7 +89,9 @@ hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t s);
 hipError_t launch_kv_append(const dfx_kv_cache &kv, int32_t batch, const int32_t *positions,
                             int32_t pos_minus_one, int32_t src_f32, const void *k_new,
                             const void *v_new, int64_t src_stride, hipStream_t s);
-hipError_t launch_grouped_linear(const GemmArgs &g, int nt, hipStream_t s);
+hipError_t launch_grouped_linear(const GemmArgs &g, hipStream_t s);
+hipError_t launch_pack_weight(int32_t N, int32_t K, const uint16_t *w, uint16_t *packed,
+                              hipStream_t s);
 hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
                           uint16_t *y, hipStream_t s);
 hipError_t launch_swiglu(int32_t n_flows, int32_t rows, int32_t dim, const float *gu,

@@ -51,6 +51,14 @@ typedef enum {
 
 typedef enum { DFX_F32 = 0, DFX_BF16 = 1 } dfx_dtype;
 
+/* Layout of a bf16 weight matrix W with N output and K input features.
+ *  DFX_W_ROW_MAJOR: W[n][k] at n*K + k.
+ *  DFX_W_PACKED:    matrix-core fragment order (see dfx_pack_weight): each 16-row x
+ *                   32-column block is 1 KiB contiguous and a 16-row slab is one
+ *                   contiguous stream, so the grouped linear reads weights at full
+ *                   HBM burst length. */
+typedef enum { DFX_W_ROW_MAJOR = 0, DFX_W_PACKED = 1 } dfx_weight_layout;
+
 /*
  * The single persistent K/V cache of the primary flow (same page, section
  * "Architettura Core": only the primary writes it, the auxiliary flow reads it).
@@ -116,8 +124,10 @@ dfx_status dfx_decode_attn_plan(const dfx_kv_cache *kv, int32_t batch, int32_t n
  *  lse          device fp32 [n_flows][batch][num_q_heads] (natural log) or NULL.
  *  max_context  host upper bound of context_lens (used for split planning and
  *               clamping; <= the cache capacity).
- *  num_splits   0 = automatic; otherwise the number of context splits, each
- *               merged in a fixed order by a log-sum-exp combine (deterministic).
+ *  num_splits   0 = automatic; otherwise the requested number of context splits,
+ *               merged in a fixed order by a log-sum-exp combine (deterministic). With
+ *               a paged cache one split spans at most 1023 blocks, so the plan may use
+ *               more splits than requested; dfx_decode_attn_plan reports the count.
  *  workspace    device scratch of >= the dfx_decode_attn_plan size (may be NULL
  *               when that size is 0); owned by the caller, not kept after the call.
  * The pool is only read. Results for one (b, h, f) do not depend on the other
@@ -161,7 +171,8 @@ dfx_status dfx_kv_append_primary(const dfx_kv_cache *kv, int32_t batch, const in
  *
  *  x        device [n_flows][rows][in_features], x_dtype (fp32 rows are rounded
  *           to bf16 on load), 16-byte aligned, in_features a multiple of 32.
- *  w        device bf16 [out_features][in_features], out_features a multiple of 16.
+ *  w        device bf16 weights of out_features x in_features (out_features a multiple
+ *           of 16) in w_layout (DFX_W_PACKED streams at full bandwidth).
  *  y        device [n_flows][rows][out_features] of y_dtype; may alias residual
  *           (in-place residual update), must not overlap x or w.
  *  couple   device fp32 [out_features] or NULL; residual device fp32 or NULL.
@@ -178,9 +189,18 @@ dfx_status dfx_grouped_linear_workspace_size(int32_t n_flows, int32_t rows, int3
 
 dfx_status dfx_grouped_linear(int32_t n_flows, int32_t rows, int32_t in_features,
                               int32_t out_features, int32_t x_dtype, const void *x,
-                              const uint16_t *w, int32_t y_dtype, void *y, const float *couple,
-                              const float *residual, void *workspace, size_t workspace_bytes,
-                              void *stream);
+                              const uint16_t *w, int32_t w_layout, int32_t y_dtype, void *y,
+                              const float *couple, const float *residual, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
+ * Reorder a row-major bf16 weight matrix into DFX_W_PACKED (a pure permutation, done once
+ * per static weight): packed[((t * K/32 + s) * 64 + l) * 8 + v] = w[16 t + l % 16][32 s +
+ * 8 (l / 16) + v] for t < N/16, s < K/32, l < 64, v < 8. N must be a multiple of 16 and K
+ * of 32; w and packed are device buffers of N*K elements that must not overlap.
+ */
+dfx_status dfx_pack_weight(int32_t out_features, int32_t in_features, const uint16_t *w,
+                           uint16_t *packed, void *stream);
 
 /*
  * RMSNorm with one gain vector shared by all rows (the flows add no
@@ -212,7 +232,8 @@ dfx_status dfx_swiglu_couple(int32_t n_flows, int32_t rows, int32_t dim, const f
  * MLP-output levels (same page, sections "Architettura Core" and "Meccanismi
  * Chiave"). NULL coupling vectors give the minimal two-flow form (separate
  * rows, shared cache, no coupling; section "Risultati" reports this variant).
- * All pointers are device pointers; matrices are bf16 row-major [out][in].
+ * All pointers are device pointers; the four matrices are bf16 [out][in] in
+ * DFX_W_PACKED layout (dfx_pack_weight).
  */
 typedef struct dfx_layer_weights {
   int32_t hidden;             /* model width; a multiple of 32, at most 16384 */
@@ -222,11 +243,11 @@ typedef struct dfx_layer_weights {
   int32_t intermediate;       /* MLP width; a multiple of 32 */
   float rms_eps;
   const float *attn_norm_gain;     /* [hidden] */
-  const uint16_t *w_qkv;           /* [(num_q_heads + 2*num_kv_heads)*head_dim][hidden]: Q, K, V rows */
-  const uint16_t *w_o;             /* [hidden][num_q_heads*head_dim] */
+  const uint16_t *w_qkv;           /* packed [(num_q_heads + 2*num_kv_heads)*head_dim][hidden]: Q, K, V rows */
+  const uint16_t *w_o;             /* packed [hidden][num_q_heads*head_dim] */
   const float *mlp_norm_gain;      /* [hidden] */
-  const uint16_t *w_gate_up;       /* [2*intermediate][hidden]: gate rows, then up rows */
-  const uint16_t *w_down;          /* [hidden][intermediate] */
+  const uint16_t *w_gate_up;       /* packed [2*intermediate][hidden]: gate rows, then up rows */
+  const uint16_t *w_down;          /* packed [hidden][intermediate] */
   const float *couple_a;           /* [head_dim] (one vector for all heads) or NULL */
   const float *couple_b;           /* [intermediate] or NULL */
   const float *couple_c;           /* [hidden] or NULL */

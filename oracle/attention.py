@@ -27,14 +27,14 @@ import numpy as np
 from .numerics import widen
 
 
-def _queries(q1, q2_raw, a, a_head_stride):
-    Q1 = widen(q1)
+def _queries(q1, q2_raw, a, a_head_stride, dtype=np.float64):
+    Q1 = widen(q1).astype(dtype)
     B, Hq, D = Q1.shape
     flows = [Q1]
     if q2_raw is not None:
-        Q2 = widen(q2_raw)
+        Q2 = widen(q2_raw).astype(dtype)
         if a is not None:
-            A = widen(a)
+            A = widen(a).astype(dtype)
             A = A.reshape(1, 1, D) if a_head_stride == 0 else A.reshape(1, Hq, D)
             Q2 = Q2 + A * Q1
         flows.append(Q2)
@@ -52,15 +52,16 @@ def gather_kv(pool, block_table, b, n):
 
 
 def decode_attention(q1, q2_raw, a, a_head_stride, k_pool, v_pool, block_table, context_lens,
-                     softmax_scale=None, batches=None, return_weights=False):
+                     softmax_scale=None, batches=None, return_weights=False, dtype=np.float64):
     """Dual-flow decode attention in fp64.
 
     q1, q2_raw: [B][Hq][D] (uint16 bf16 bits, float32 or float64); q2_raw may be
     None (primary only). a: [D] or [Hq][D] or None. Pools: [blocks][Hkv][bs][D].
     Returns (o1, o2 or None, lse) with o_f [B][Hq][D] and lse [F][B][Hq] (natural log).
-    ``batches`` restricts the work to some sequences (other rows stay NaN).
+    ``batches`` restricts the work to some sequences (other rows stay NaN). ``dtype`` is
+    the working precision (float64; float32 evaluates the same definition in single).
     """
-    flows = _queries(q1, q2_raw, a, a_head_stride)
+    flows = _queries(q1, q2_raw, a, a_head_stride, dtype)
     F = len(flows)
     B, Hq, D = flows[0].shape
     Hkv = k_pool.shape[1]
@@ -79,12 +80,12 @@ def decode_attention(q1, q2_raw, a, a_head_stride, k_pool, v_pool, block_table, 
                 out[f][b] = 0.0
             lse[:, b] = -np.inf
             continue
-        K = widen(gather_kv(k_pool, block_table, b, n))
-        V = widen(gather_kv(v_pool, block_table, b, n))
+        K = widen(gather_kv(k_pool, block_table, b, n)).astype(dtype)
+        V = widen(gather_kv(v_pool, block_table, b, n)).astype(dtype)
         for g in range(Hkv):
             heads = slice(g * G, (g + 1) * G)
             Q = np.concatenate([fl[b, heads] for fl in flows], axis=0)      # [F*G][D]
-            S = scale * (Q @ K[g].T)                                        # [F*G][n]
+            S = dtype(scale) * (Q @ K[g].T)                                 # [F*G][n]
             m = S.max(axis=1, keepdims=True)
             E = np.exp(S - m)
             l = E.sum(axis=1, keepdims=True)

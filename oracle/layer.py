@@ -25,20 +25,23 @@ from .numerics import bf16_bits
 
 def dual_flow_layer(x, g_attn, g_mlp, w_qkv, w_o, w_gate_up, w_down, a, b, c, eps,
                     k_pool, v_pool, block_table, context_lens_before, num_q_heads,
-                    num_kv_heads, head_dim, batches=None):
+                    num_kv_heads, head_dim, batches=None, dtype=np.float64):
     """x: float [F][B][hidden] (F = 1 primary only, F = 2 both flows).
 
     context_lens_before[b] tokens are in the cache before the step; the
     primary row is appended at that position and both flows attend to
     context_lens_before[b] + 1 positions. Returns (x_out [F][B][hidden] fp64,
     k_pool', v_pool', dict of intermediates). ``batches`` limits attention to
-    some sequences (their rows only are meaningful in x_out).
+    some sequences (their rows only are meaningful in x_out). ``dtype`` is the working
+    precision: float64, or float32 for the same definition in single precision (whose
+    distance from the float64 result measures how much the five bf16 rounding points
+    amplify single-precision arithmetic).
     """
     x = np.asarray(x, dtype=np.float64)
     F, B, H = x.shape
     Hq, Hkv, D = num_q_heads, num_kv_heads, head_dim
-    h1 = rmsnorm(x, g_attn, eps)                                   # R1
-    qkv = grouped_linear(h1, w_qkv)                                # fp64
+    h1 = rmsnorm(x, g_attn, eps, dtype)                            # R1
+    qkv = grouped_linear(h1, w_qkv, dtype=dtype)
     q = qkv[..., : Hq * D]
     k_new = qkv[0, :, Hq * D: (Hq + Hkv) * D]
     v_new = qkv[0, :, (Hq + Hkv) * D:]
@@ -46,11 +49,12 @@ def dual_flow_layer(x, g_attn, g_mlp, w_qkv, w_o, w_gate_up, w_down, a, b, c, ep
     kp, vp = kv_append(k_pool, v_pool, block_table, pos, bf16_bits(k_new), bf16_bits(v_new))  # R2
     ctx = pos + 1
     o1, o2, _ = decode_attention(q[0].reshape(B, Hq, D), q[1].reshape(B, Hq, D) if F == 2 else None,
-                                 a if F == 2 else None, 0, kp, vp, block_table, ctx, batches=batches)
+                                 a if F == 2 else None, 0, kp, vp, block_table, ctx, batches=batches,
+                                 dtype=dtype)
     o = np.stack([o1] + ([o2] if F == 2 else [])).reshape(F, B, Hq * D)
-    x1 = grouped_linear(o, w_o, residual=x)                        # R3 inside (fp64 -> bf16)
-    h2 = rmsnorm(x1, g_mlp, eps)                                   # R4
-    gu = grouped_linear(h2, w_gate_up)
-    inter = swiglu_couple(gu, b if F == 2 else None)               # R5
-    x2 = grouped_linear(inter, w_down, couple=c if F == 2 else None, residual=x1)
+    x1 = grouped_linear(o, w_o, residual=x, dtype=dtype)           # R3 inside (-> bf16)
+    h2 = rmsnorm(x1, g_mlp, eps, dtype)                            # R4
+    gu = grouped_linear(h2, w_gate_up, dtype=dtype)
+    inter = swiglu_couple(gu, b if F == 2 else None, dtype)        # R5
+    x2 = grouped_linear(inter, w_down, couple=c if F == 2 else None, residual=x1, dtype=dtype)
     return x2, kp, vp, dict(h1=h1, qkv=qkv, o=o, x1=x1, h2=h2, gu=gu, inter=inter)

@@ -14,39 +14,40 @@ import numpy as np
 from .numerics import bf16_bits, round_bf16, widen
 
 
-def grouped_linear(x, w, couple=None, residual=None, y_bf16=False):
+def grouped_linear(x, w, couple=None, residual=None, y_bf16=False, dtype=np.float64):
     """Y[f] = bf16(X[f]) @ W^T for every flow f, then the optional coupling
     Y[1] += couple * Y[0], then the optional residual add.
 
     x: [F][rows][K] (uint16 bf16 bits, or float32/float64 which are rounded to
     bf16 first); w: [N][K] uint16 bf16 bits. Returns float64 [F][rows][N], or
-    bf16 bits when y_bf16.
+    bf16 bits when y_bf16. ``dtype`` is the working precision of the arithmetic (float64;
+    float32 gives the same definition evaluated in single precision).
     """
     x = np.asarray(x)
-    X = widen(x) if x.dtype == np.uint16 else round_bf16(widen(x))
-    W = widen(w)
+    X = (widen(x) if x.dtype == np.uint16 else round_bf16(widen(x))).astype(dtype)
+    W = widen(w).astype(dtype)
     Y = X @ W.T
     if couple is not None and Y.shape[0] == 2:
-        Y[1] = Y[1] + widen(couple) * Y[0]
+        Y[1] = Y[1] + widen(couple).astype(dtype) * Y[0]
     if residual is not None:
-        Y = widen(residual) + Y
+        Y = widen(residual).astype(dtype) + Y
     return bf16_bits(Y) if y_bf16 else Y
 
 
-def rmsnorm(x, gain, eps):
+def rmsnorm(x, gain, eps, dtype=np.float64):
     """y = x / sqrt(mean(x^2) + eps) * gain over the last axis, rounded to bf16 (fp64 values)."""
-    X = widen(x)
-    r = 1.0 / np.sqrt(np.mean(X * X, axis=-1, keepdims=True) + eps)
-    return round_bf16(X * r * widen(gain))
+    X = widen(x).astype(dtype)
+    r = dtype(1.0) / np.sqrt(np.mean(X * X, axis=-1, keepdims=True) + dtype(eps))
+    return round_bf16(X * r * widen(gain).astype(dtype))
 
 
-def swiglu_couple(gate_up, b=None):
+def swiglu_couple(gate_up, b=None, dtype=np.float64):
     """inter = silu(gate) * up with gate_up = [gate | up] on the last axis; for
     two flows inter[1] += b * inter[0]; rounded to bf16 (fp64 values)."""
-    GU = widen(gate_up)
+    GU = widen(gate_up).astype(dtype)
     I = GU.shape[-1] // 2
     gate, up = GU[..., :I], GU[..., I:]
-    inter = gate / (1.0 + np.exp(-gate)) * up
+    inter = gate / (dtype(1.0) + np.exp(-gate)) * up
     if b is not None and inter.shape[0] == 2:
-        inter[1] = inter[1] + widen(b) * inter[0]
+        inter[1] = inter[1] + widen(b).astype(dtype) * inter[0]
     return round_bf16(inter)

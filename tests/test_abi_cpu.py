@@ -21,7 +21,7 @@ def declared():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = _abi.lib()
     names = declared()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, n
@@ -78,10 +78,17 @@ def test_plan_is_host_arithmetic():
     k = kv(mb=8192, nb=65536)
     assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 0, ctypes.byref(s), ctypes.byref(n)) == 0
     assert s.value > 1 and n.value >= s.value * 2 * 8 * 64 * 129 * 4
+    # a paged split holds at most 1023 blocks (its block ids sit in LDS): one requested
+    # split over 131072 tokens of 16-token blocks becomes ceil(131072 / 16256) = 9
     assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 1, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value == 9 and n.value > 0
+    kc = kv(table=None, bs=131072, nb=8)
+    assert lib.dfx_decode_attn_plan(ctypes.byref(kc), 8, 64, 2, 131072, 1, ctypes.byref(s), ctypes.byref(n)) == 0
     assert s.value == 1 and n.value == 0
     assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 7, ctypes.byref(s), ctypes.byref(n)) == 0
-    assert s.value == 7
+    assert s.value == 9          # raised to respect the 1023-block split limit
+    assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 20, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value == 20
     # the plan does not depend on the number of flows (primary results stay bit-identical)
     s1 = ctypes.c_int32()
     lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 1, 131072, 0, ctypes.byref(s1), ctypes.byref(n))
@@ -96,10 +103,13 @@ def test_linear_and_glue_reject():
     assert lib.dfx_grouped_linear_workspace_size(2, 4, 48, 64, ctypes.byref(n)) == 2
     assert lib.dfx_grouped_linear_workspace_size(2, 4, 64, 24, ctypes.byref(n)) == 2
     assert lib.dfx_grouped_linear_workspace_size(2, 32, 4096, 4096, ctypes.byref(n)) == 0 and n.value > 0
-    st = lib.dfx_grouped_linear(2, 32, 4096, 4096, 1, FAKE, FAKE, 0, FAKE, None, None, None, 0, None)
+    st = lib.dfx_grouped_linear(2, 32, 4096, 4096, 1, FAKE, FAKE, 1, 0, FAKE, None, None, None, 0, None)
     assert st == 3 and "workspace" in lib.dfx_last_error().decode()
-    assert lib.dfx_grouped_linear(2, 4, 64, 64, 9, FAKE, FAKE, 0, FAKE, None, None, None, 0, None) == 1
-    assert lib.dfx_grouped_linear(2, 4, 64, 64, 1, FAKE + 8, FAKE, 0, FAKE, None, None, None, 0, None) == 1
+    assert lib.dfx_grouped_linear(2, 4, 64, 64, 9, FAKE, FAKE, 0, 0, FAKE, None, None, None, 0, None) == 1
+    assert lib.dfx_grouped_linear(2, 4, 64, 64, 1, FAKE + 8, FAKE, 0, 0, FAKE, None, None, None, 0, None) == 1
+    assert lib.dfx_grouped_linear(2, 4, 64, 64, 1, FAKE, FAKE, 2, 0, FAKE, None, None, None, 0, None) == 1
+    assert lib.dfx_pack_weight(24, 64, FAKE, FAKE + 4096, None) == 1
+    assert lib.dfx_pack_weight(32, 64, FAKE, FAKE + 1024, None) == 1      # overlapping buffers
     assert lib.dfx_rmsnorm(4, 30, FAKE, FAKE, 1e-5, FAKE, None) == 1
     assert lib.dfx_rmsnorm(4, 64, None, FAKE, 1e-5, FAKE, None) == 1
     assert lib.dfx_swiglu_couple(3, 4, 64, FAKE, None, FAKE, None) == 1
