@@ -226,7 +226,9 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic_from_profiles("attn_mfma.hip", args.workload),
-                "kernel": "dfx_decode_attn (attn_mfma_kernel + attn_merge_kernel)",
+                "kernel": ("attn_mfma_kernel" if splits == 1 else
+                           f"attn_mfma_kernel + attn_merge_kernel ({splits} splits)")
+                if shape["kv_el"] == 2 else "attn_valu_kernel",
                 "bytes_per_launch": int(abytes)}
 
     # ---- CPU oracle on the host cores (reported baseline only)

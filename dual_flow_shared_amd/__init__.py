@@ -17,7 +17,7 @@ from ._abi import (DFX_BF16, DFX_F32, DFX_W_PACKED, DFX_W_ROW_MAJOR, DfxError, K
 
 __all__ = ["DfxError", "KVCache", "LayerWeights", "decode_attn", "decode_attn_plan",
            "kv_append_primary", "grouped_linear", "pack_weight", "rmsnorm", "swiglu_couple",
-           "dual_flow_decode_layer", "layer_workspace_size", "copy_bytes", "fill_bytes",
+           "dual_flow_decode_layer", "layer_workspace_size", "copy_bytes", "read_bytes", "fill_bytes",
            "Workspace", "version"]
 
 
@@ -299,6 +299,15 @@ def dual_flow_decode_layer(x: torch.Tensor, weights: LayerWeights, cache: KVCach
 def copy_bytes(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
     n = min(dst.numel() * dst.element_size(), src.numel() * src.element_size())
     check(lib().dfx_copy_bytes(_ptr(dst), _ptr(src), n - n % 16, _stream(stream)))
+
+
+def read_bytes(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Read every byte of src once on the GPU (achievable read bandwidth)."""
+    if sink is None:
+        sink = torch.empty(4096 * 256, dtype=torch.int32, device=src.device)
+    n = src.numel() * src.element_size()
+    check(lib().dfx_read_bytes(_ptr(src), n - n % 16, _ptr(sink), _stream(stream)))
+    return sink
 
 
 def fill_bytes(dst: torch.Tensor, pattern: int = 0, stream=None) -> None:

@@ -32,13 +32,14 @@ bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kChunkQuantum = 128;  // tokens: 4 waves x 32-token tiles
-constexpr int kMinChunk = 1024;
+constexpr int kMinChunk = 1024;   // tokens: shorter splits cost more in merge than they gain
+constexpr int kMaxChunk = 8192;   // tokens: longer splits leave CUs idle when lengths differ
 // Launch-shape defaults (compile-time so that alternatives can be measured).
 #ifndef DFX_ATTN_TARGET
-#define DFX_ATTN_TARGET 1024
+#define DFX_ATTN_TARGET 256
 #endif
 #ifndef DFX_GEMM_TARGET
-#define DFX_GEMM_TARGET 512
+#define DFX_GEMM_TARGET 256
 #endif
 constexpr int kTargetAttnGroups = DFX_ATTN_TARGET;
 constexpr int kTargetGemmGroups = DFX_GEMM_TARGET;
@@ -81,8 +82,11 @@ void attn_plan(int batch, int hkv, int max_ctx, int requested, int block_size, i
   if (requested > 0) {
     s = requested < max_s ? requested : max_s;
   } else {
+    // enough work-groups to fill the CUs, and no split longer than kMaxChunk
     const int pairs = batch * hkv > 0 ? batch * hkv : 1;
     s = (kTargetAttnGroups + pairs - 1) / pairs;
+    const int by_max = (max_ctx + kMaxChunk - 1) / kMaxChunk;
+    if (s < by_max) s = by_max;
     const int by_min = max_ctx > kMinChunk ? (max_ctx + kMinChunk - 1) / kMinChunk : 1;
     if (s > by_min) s = by_min;
     if (s > max_s) s = max_s;
@@ -145,14 +149,15 @@ dfx_status check_linear(int32_t n_flows, int32_t rows, int32_t K, int32_t N) {
 dfx_status run_linear_parts(int32_t n_flows, int32_t rows, int32_t K, int32_t N, int x_f32,
                             const void *x, const uint16_t *w, int w_packed, int y_bf16, void *y,
                             const float *couple, const float *residual, float *partial,
-                            hipStream_t s) {
+                            hipStream_t s, int tiles_only = 0) {
   if (rows == 0) return DFX_OK;
   const GemmPlan g = gemm_plan(n_flows, rows, K, N);
   GemmArgs a{};
   a.n_flows = n_flows; a.rows = rows; a.K = K; a.N = N;
   a.x_f32 = x_f32; a.x = x; a.w = w; a.w_packed = w_packed; a.y_bf16 = y_bf16; a.y = y;
   a.couple = couple; a.residual = residual; a.ksplit = g.ksplit;
-  a.partial = g.ksplit > 1 ? partial : nullptr;
+  a.partial = g.ksplit > 1 || tiles_only ? partial : nullptr;
+  a.tiles_only = tiles_only;
   return hip_status(launch_grouped_linear(a, s), "grouped_linear launch");
 }
 
@@ -385,7 +390,7 @@ dfx_status dfx_swiglu_couple(int32_t n_flows, int32_t rows, int32_t dim, const f
 namespace {
 
 struct LayerPlan {
-  size_t h, qkv, o, gu, attn_ws, partials, total;
+  size_t h, qkv, o, attn_ws, tiles, total;
   int splits;
 };
 
@@ -409,22 +414,22 @@ dfx_status layer_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_
   const int Nqkv = (Hq + 2 * w->num_kv_heads) * D, I = w->intermediate;
   LayerPlan p{};
   auto a256 = [](size_t x) { return round_up(x, 256); };
-  p.h = a256((size_t)F * B * (H > I ? H : I) * 2);
-  p.qkv = a256((size_t)F * B * Nqkv * 4);
-  p.o = a256((size_t)F * B * Hq * D * 4);
-  p.gu = a256((size_t)F * B * 2 * I * 4);
-  // (the bf16 MLP intermediate reuses the h buffer)
+  p.h = a256((size_t)F * B * (H > I ? H : I) * 2);  // normed rows, then the MLP intermediate
+  p.qkv = a256((size_t)F * B * Nqkv * 4);           // Q columns (row stride Nqkv)
+  p.o = a256((size_t)F * B * Hq * D * 2);           // attention rows (bf16)
   int chunk;
   attn_plan(B, kv->num_kv_heads, max_context, 0, paged_bs(kv), &p.splits, &chunk);
   p.attn_ws = a256(attn_ws_bytes(p.splits, F, B, Hq, D));
-  // one split-K partial region shared by the four projections (they run in stream order)
+  // every projection writes its fp32 tiles [ksplit][groups][64][N]; they run in stream
+  // order, so one region serves all four
   const int shapes[4][2] = {{H, Nqkv}, {Hq * D, H}, {H, 2 * I}, {I, H}};
   for (auto &sh : shapes) {
     const GemmPlan g = gemm_plan(F, B, sh[0], sh[1]);
-    p.partials = g.partial_bytes > p.partials ? g.partial_bytes : p.partials;
+    const size_t t = (size_t)g.ksplit * g.groups * 64 * sh[1] * sizeof(float);
+    p.tiles = t > p.tiles ? t : p.tiles;
   }
-  p.partials = a256(p.partials);
-  p.total = p.partials + p.h + p.qkv + p.o + p.gu + p.attn_ws;
+  p.tiles = a256(p.tiles);
+  p.total = p.tiles + p.h + p.qkv + p.o + p.attn_ws;
   *pl = p;
   return DFX_OK;
 }
@@ -462,31 +467,39 @@ dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_c
   const int F = n_flows, B = batch, H = w->hidden, D = w->head_dim, Hq = w->num_q_heads;
   const int Hkv = w->num_kv_heads, Nqkv = (Hq + 2 * Hkv) * D, I = w->intermediate;
   char *base = (char *)workspace;
-  float *part = (float *)base;
-  uint16_t *h = (uint16_t *)(base + p.partials);
+  float *tiles = (float *)base;
+  uint16_t *h = (uint16_t *)(base + p.tiles);
   float *qkv = (float *)((char *)h + p.h);
-  float *o = (float *)((char *)qkv + p.qkv);
-  float *gu = (float *)((char *)o + p.o);
-  void *aws = (char *)gu + p.gu;
+  uint16_t *ob = (uint16_t *)((char *)qkv + p.qkv);
+  void *aws = (char *)ob + p.o;
   const int rows = F * B;
   dfx_status r;
-  // attention block
+  LayerGlueArgs g{};
+  g.n_flows = F; g.batch = B; g.tiles = tiles; g.x = x; g.h = h; g.eps = w->rms_eps;
+  g.kv = *kv; g.ctx = context_lens; g.num_q_heads = Hq; g.head_dim = D;
+  auto ksplit = [&](int K, int N) { return gemm_plan(F, B, K, N).ksplit; };
+  // attention block: norm, shared Q/K/V projection, primary-only append, dual attention
   if ((r = hip_status(launch_rmsnorm(rows, H, x, w->attn_norm_gain, w->rms_eps, h, s), "rmsnorm launch"))) return r;
-  if ((r = run_linear_parts(F, B, H, Nqkv, 0, h, w->w_qkv, 1, 0, qkv, nullptr, nullptr, part, s))) return r;
-  if ((r = hip_status(launch_kv_append(*kv, B, context_lens, 1, 1, qkv + Hq * D, qkv + (Hq + Hkv) * D,
-                                       Nqkv, s), "kv_append launch"))) return r;
+  if ((r = run_linear_parts(F, B, H, Nqkv, 0, h, w->w_qkv, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  g.N = Nqkv; g.ksplit = ksplit(H, Nqkv); g.out = qkv;
+  if ((r = hip_status(launch_layer_glue(kGlueQkv, g, s), "qkv finish launch"))) return r;
   // attention writes its rows already rounded to bf16 (the rows entering W_o)
-  uint16_t *ob = (uint16_t *)o;
   AttnCall c{kv, context_lens, B, max_context, Hq, DFX_F32, qkv, F == 2 ? qkv + (size_t)B * Nqkv : nullptr,
              Nqkv, F == 2 ? w->couple_a : nullptr, 0, 0.f, (float *)ob,
              F == 2 ? (float *)(ob + (size_t)B * Hq * D) : nullptr, nullptr, 0, aws, p.attn_ws, 1};
   if ((r = run_attn(c, s))) return r;
-  if ((r = run_linear_parts(F, B, Hq * D, H, 0, ob, w->w_o, 1, 0, x, nullptr, x, part, s))) return r;
-  // MLP block
-  if ((r = hip_status(launch_rmsnorm(rows, H, x, w->mlp_norm_gain, w->rms_eps, h, s), "rmsnorm launch"))) return r;
-  if ((r = run_linear_parts(F, B, H, 2 * I, 0, h, w->w_gate_up, 1, 0, gu, nullptr, nullptr, part, s))) return r;
-  if ((r = hip_status(launch_swiglu(F, B, I, gu, F == 2 ? w->couple_b : nullptr, h, s), "swiglu launch"))) return r;
-  return run_linear_parts(F, B, I, H, 0, h, w->w_down, 1, 0, x, F == 2 ? w->couple_c : nullptr, x, part, s);
+  // output projection + residual, then the MLP norm
+  if ((r = run_linear_parts(F, B, Hq * D, H, 0, ob, w->w_o, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  g.N = H; g.ksplit = ksplit(Hq * D, H); g.gain = w->mlp_norm_gain;
+  if ((r = hip_status(launch_layer_glue(kGlueONorm, g, s), "o finish launch"))) return r;
+  // MLP: shared gate/up projection, SwiGLU with b coupling, shared down projection with
+  // c coupling and the residual
+  if ((r = run_linear_parts(F, B, H, 2 * I, 0, h, w->w_gate_up, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  g.N = 2 * I; g.ksplit = ksplit(H, 2 * I); g.couple = F == 2 ? w->couple_b : nullptr;
+  if ((r = hip_status(launch_layer_glue(kGlueSwiglu, g, s), "swiglu finish launch"))) return r;
+  if ((r = run_linear_parts(F, B, I, H, 0, h, w->w_down, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  g.N = H; g.ksplit = ksplit(I, H); g.couple = F == 2 ? w->couple_c : nullptr;
+  return hip_status(launch_layer_glue(kGlueDown, g, s), "down finish launch");
   DFX_END
 }
 
@@ -495,6 +508,14 @@ dfx_status dfx_copy_bytes(void *dst, const void *src, size_t bytes, void *stream
   if (bytes % 16 || !aligned16(dst) || !aligned16(src) || (bytes && (!dst || !src)))
     return fail(DFX_EINVAL, "copy needs 16-byte aligned pointers and a multiple of 16 bytes");
   return hip_status(launch_copy(dst, src, bytes, (hipStream_t)stream), "copy launch");
+  DFX_END
+}
+
+dfx_status dfx_read_bytes(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+  DFX_BEGIN
+  if (bytes % 16 || !aligned16(src) || (bytes && (!src || !sink)))
+    return fail(DFX_EINVAL, "read needs a 16-byte aligned source, a multiple of 16 bytes and a sink");
+  return hip_status(launch_read(src, bytes, sink, (hipStream_t)stream), "read launch");
   DFX_END
 }
 

@@ -79,7 +79,24 @@ struct GemmArgs {
   void *y;
   const float *couple, *residual;
   int32_t ksplit;      // work-groups along K per 64-feature tile
-  float *partial;      // [ksplit][groups][64 rows][N] fp32 when ksplit > 1
+  float *partial;      // [ksplit][groups][64 rows][N] fp32 when ksplit > 1 or tiles_only
+  int32_t tiles_only;  // write the fp32 tiles even for one split (a finish kernel follows)
+};
+
+// Arguments of the kernels that finish a projection of the decode layer.
+enum { kGlueQkv = 0, kGlueONorm = 1, kGlueSwiglu = 2, kGlueDown = 3 };
+struct LayerGlueArgs {
+  int32_t n_flows, batch, N, ksplit;
+  const float *tiles;  // [ksplit][groups][64][N]
+  float *out;          // qkv: Q columns [F][B][N] fp32
+  float *x;            // residual rows [F][B][N] fp32 (in place)
+  uint16_t *h;         // bf16 rows for the next projection
+  const float *gain;   // RMSNorm gain
+  float eps;
+  const float *couple; // b (SwiGLU) or c (down) coupling vector, or NULL
+  dfx_kv_cache kv;     // cache written by the Q/K/V finish (primary rows only)
+  const int32_t *ctx;  // context lengths after the step (append position = ctx - 1)
+  int32_t num_q_heads, head_dim;
 };
 
 // Kernel launchers (defined next to their kernels). They assume validated arguments.
@@ -92,11 +109,14 @@ hipError_t launch_kv_append(const dfx_kv_cache &kv, int32_t batch, const int32_t
 hipError_t launch_grouped_linear(const GemmArgs &g, hipStream_t s);
 hipError_t launch_pack_weight(int32_t N, int32_t K, const uint16_t *w, uint16_t *packed,
                               hipStream_t s);
+hipError_t launch_layer_glue(int which, const LayerGlueArgs &a, hipStream_t s);
 hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
                           uint16_t *y, hipStream_t s);
 hipError_t launch_swiglu(int32_t n_flows, int32_t rows, int32_t dim, const float *gu,
                          const float *b, uint16_t *out, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+constexpr int kReadBlocks = 4096;  // work-groups of the read-bandwidth helper
+hipError_t launch_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t launch_fill(void *dst, size_t bytes, uint32_t pattern, hipStream_t s);
 
 }  // namespace dfx

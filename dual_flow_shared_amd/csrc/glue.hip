@@ -82,6 +82,24 @@ __global__ void __launch_bounds__(256) fill_kernel(u32x4 *dst, int64_t n, uint32
     dst[i] = u32x4{v, v, v, v};
 }
 
+// Reads every 16-byte word once (a measurement of achievable read bandwidth); the XOR of
+// what each thread read goes to sink[thread] so the loads cannot be dropped.
+__global__ void __launch_bounds__(256) read_kernel(const u32x4 *src, int64_t n, uint32_t *sink) {
+  uint32_t acc = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const u32x4 v = src[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+hipError_t launch_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 16);
+  if (n == 0) return hipSuccess;
+  read_kernel<<<kReadBlocks, 256, 0, s>>>((const u32x4 *)src, n, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s) {
   const int64_t n = (int64_t)(bytes / 16);
   if (n == 0) return hipSuccess;

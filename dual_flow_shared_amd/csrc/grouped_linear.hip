@@ -163,7 +163,7 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
 
     // C layout: lane holds row q = 16 nb + n and features col0 + 4 j + i
     const int col = col0 + 4 * j;
-    if (p.ksplit > 1) {
+    if (p.ksplit > 1 || p.tiles_only) {
       // partial tile [ks][grp][64 rows][N]
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
@@ -317,7 +317,7 @@ __global__ void __launch_bounds__(256) grouped_linear_chunked_kernel(GemmArgs p)
 
     const int col = col0 + 4 * j;
     if (!wave_live) continue;
-    if (p.ksplit > 1) {
+    if (p.ksplit > 1 || p.tiles_only) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         float *dst = p.partial + (((int64_t)ks * groups + grp) * 64 + 16 * nb + n) * N + col;
@@ -384,7 +384,7 @@ hipError_t launch_grouped_linear(const GemmArgs &g, hipStream_t s) {
     else grouped_linear_kernel<false, false><<<grid, block, 0, s>>>(g);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || g.ksplit == 1) return e;
+  if (e != hipSuccess || g.ksplit == 1 || g.tiles_only) return e;
   const int rpg = 64 / g.n_flows;
   const int groups = (g.rows + rpg - 1) / rpg;
   const int64_t threads = (int64_t)groups * rpg * (g.N / 4);

@@ -1,0 +1,162 @@
+// Layer-internal kernels that finish each grouped projection of the decode layer: they
+// sum the K-split fp32 tiles of the projection in split order and apply the glue that
+// follows it, so no separate reduction pass, norm or activation pass touches HBM.
+//
+// Tiles are [ksplit][groups][64 rows][N]; row q of a group is flow q / (64 / F), batch
+// row grp * (64 / F) + q % (64 / F) (the layout the grouped linear writes).
+#include "common.h"
+
+namespace dfx {
+
+__device__ __forceinline__ f32x4 sum_tiles(const float *tiles, int ksplit, int groups, int N,
+                                           int f, int rr, int rpg, int col) {
+  const int grp = rr / rpg, q = f * rpg + rr % rpg;
+  f32x4 s{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < ksplit; ++k)
+    s += *(const f32x4 *)(tiles + (((int64_t)k * groups + grp) * 64 + q) * N + col);
+  return s;
+}
+
+// Q columns of both flows -> qkv rows (fp32); K and V columns of flow 0 -> the cache at
+// position context_lens[b] - 1 as bf16 (the auxiliary flow's K/V columns are dropped: only
+// the primary flow writes the cache). One thread per 4 columns of one (flow, row).
+__global__ void __launch_bounds__(256) qkv_finish_kernel(LayerGlueArgs a) {
+  const int F = a.n_flows, B = a.batch, N = a.N;
+  const int rpg = 64 / F, groups = (B + rpg - 1) / rpg;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int n4 = N / 4;
+  if (idx >= (int64_t)F * B * n4) return;
+  const int col = (int)(idx % n4) * 4;
+  const int row = (int)(idx / n4);
+  const int f = row / B, b = row % B;
+  const int qcols = a.num_q_heads * a.head_dim;
+  if (col >= qcols && f != 0) return;
+  const f32x4 v = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, col);
+  if (col < qcols) {
+    *(f32x4 *)(a.out + ((int64_t)f * B + b) * N + col) = v;
+    return;
+  }
+  const dfx_kv_cache &kv = a.kv;
+  const int kvcols = kv.num_kv_heads * kv.head_dim;
+  const int c = col - qcols;
+  const bool is_v = c >= kvcols;
+  const int cc = is_v ? c - kvcols : c;
+  const int g = cc / kv.head_dim, d = cc % kv.head_dim;
+  const bool paged = kv.block_table != nullptr;
+  const int64_t cap = paged ? (int64_t)kv.max_blocks_per_seq * kv.block_size : kv.block_size;
+  int64_t pos = (int64_t)a.ctx[b] - 1;
+  pos = pos < 0 ? 0 : (pos >= cap ? cap - 1 : pos);
+  int64_t blk, slot;
+  if (paged) {
+    const uint32_t e = (uint32_t)kv.block_table[(int64_t)b * kv.max_blocks_per_seq + pos / kv.block_size];
+    blk = (uint64_t)e < (uint64_t)kv.num_blocks ? (int64_t)e : kv.num_blocks - 1;
+    slot = pos % kv.block_size;
+  } else {
+    blk = b;
+    slot = pos;
+  }
+  uint16_t *pool = (uint16_t *)(is_v ? kv.v : kv.k);
+  const int64_t dst = ((blk * kv.num_kv_heads + g) * kv.block_size + slot) * kv.head_dim + d;
+  *(u32x2 *)(pool + dst) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+// x += sum of the W_o tiles (in place), then h = bf16(rmsnorm(x) * gain). One work-group
+// per (flow, row); each thread owns N / 256 columns as float4.
+__global__ void __launch_bounds__(256) o_finish_norm_kernel(LayerGlueArgs a) {
+  __shared__ float red[4];
+  const int F = a.n_flows, B = a.batch, N = a.N;
+  const int rpg = 64 / F, groups = (B + rpg - 1) / rpg;
+  const int row = blockIdx.x, f = row / B, b = row % B;
+  float *xr = a.x + (int64_t)row * N;
+  float ss = 0.f;
+  for (int col = 4 * threadIdx.x; col < N; col += 1024) {
+    f32x4 v = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, col) + *(const f32x4 *)(xr + col);
+    *(f32x4 *)(xr + col) = v;
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)N + a.eps);
+  uint16_t *hr = a.h + (int64_t)row * N;
+  for (int col = 4 * threadIdx.x; col < N; col += 1024) {
+    const f32x4 v = *(const f32x4 *)(xr + col), g = *(const f32x4 *)(a.gain + col);
+    *(u32x2 *)(hr + col) = u32x2{pack_bf16x2(v[0] * r * g[0], v[1] * r * g[1]),
+                                 pack_bf16x2(v[2] * r * g[2], v[3] * r * g[3])};
+  }
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+// inter = silu(gate) * up from the summed gate/up tiles; flow 1 += b * flow 0; bf16 out.
+// One thread per 4 intermediate columns of one row index (both flows).
+__global__ void __launch_bounds__(256) gu_finish_swiglu_kernel(LayerGlueArgs a) {
+  const int F = a.n_flows, B = a.batch, N = a.N, I = N / 2;
+  const int rpg = 64 / F, groups = (B + rpg - 1) / rpg;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int i4 = I / 4;
+  if (idx >= (int64_t)B * i4) return;
+  const int col = (int)(idx % i4) * 4, b = (int)(idx / i4);
+  f32x4 prim;
+  for (int f = 0; f < F; ++f) {
+    const f32x4 g = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, col);
+    const f32x4 u = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, I + col);
+    f32x4 v{silu_f(g[0]) * u[0], silu_f(g[1]) * u[1], silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]};
+    if (f == 0) prim = v;
+    else if (a.couple) {
+      const f32x4 c = *(const f32x4 *)(a.couple + col);
+      v = f32x4{fmaf(c[0], prim[0], v[0]), fmaf(c[1], prim[1], v[1]), fmaf(c[2], prim[2], v[2]),
+                fmaf(c[3], prim[3], v[3])};
+    }
+    *(u32x2 *)(a.h + ((int64_t)f * B + b) * I + col) =
+        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+}
+
+// m = summed W_down tiles; flow 1 += c * flow 0; x += m (in place). One thread per 4
+// columns of one row index (both flows).
+__global__ void __launch_bounds__(256) down_finish_kernel(LayerGlueArgs a) {
+  const int F = a.n_flows, B = a.batch, N = a.N;
+  const int rpg = 64 / F, groups = (B + rpg - 1) / rpg;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int n4 = N / 4;
+  if (idx >= (int64_t)B * n4) return;
+  const int col = (int)(idx % n4) * 4, b = (int)(idx / n4);
+  f32x4 prim;
+  for (int f = 0; f < F; ++f) {
+    f32x4 m = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, col);
+    if (f == 0) prim = m;
+    else if (a.couple) {
+      const f32x4 c = *(const f32x4 *)(a.couple + col);
+      m = f32x4{fmaf(c[0], prim[0], m[0]), fmaf(c[1], prim[1], m[1]), fmaf(c[2], prim[2], m[2]),
+                fmaf(c[3], prim[3], m[3])};
+    }
+    float *xr = a.x + ((int64_t)f * B + b) * N + col;
+    *(f32x4 *)xr = *(const f32x4 *)xr + m;
+  }
+}
+
+hipError_t launch_layer_glue(int which, const LayerGlueArgs &a, hipStream_t s) {
+  const int F = a.n_flows, B = a.batch;
+  int64_t threads = 0;
+  switch (which) {
+    case kGlueQkv:
+      threads = (int64_t)F * B * (a.N / 4);
+      qkv_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a);
+      break;
+    case kGlueONorm:
+      o_finish_norm_kernel<<<F * B, 256, 0, s>>>(a);
+      break;
+    case kGlueSwiglu:
+      threads = (int64_t)B * (a.N / 8);
+      gu_finish_swiglu_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a);
+      break;
+    default:
+      threads = (int64_t)B * (a.N / 4);
+      down_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dfx

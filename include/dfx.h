@@ -283,10 +283,12 @@ dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_c
 /*
  * Measurement helpers (not part of the method): a plain device copy of
  * `bytes` (multiple of 16, both pointers 16-byte aligned) used to calibrate
- * hardware traffic counters, and a write of `bytes` used to evict caches
- * between timed iterations.
+ * hardware traffic counters, a read of `bytes` (achievable read bandwidth;
+ * sink: device uint32 [4096 * 256] receiving per-thread XORs of the data),
+ * and a write of `bytes` used to evict caches between timed iterations.
  */
 dfx_status dfx_copy_bytes(void *dst, const void *src, size_t bytes, void *stream);
+dfx_status dfx_read_bytes(const void *src, size_t bytes, uint32_t *sink, void *stream);
 dfx_status dfx_fill_bytes(void *dst, size_t bytes, uint32_t pattern, void *stream);
 
 #ifdef __cplusplus

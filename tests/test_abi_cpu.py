@@ -21,7 +21,7 @@ def declared():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = _abi.lib()
     names = declared()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, n
@@ -115,6 +115,7 @@ def test_linear_and_glue_reject():
     assert lib.dfx_swiglu_couple(3, 4, 64, FAKE, None, FAKE, None) == 1
     assert lib.dfx_copy_bytes(FAKE, FAKE, 17, None) == 1
     assert lib.dfx_fill_bytes(FAKE + 4, 32, 0, None) == 1
+    assert lib.dfx_read_bytes(FAKE, 32, None, None) == 1
     k = kv()
     assert lib.dfx_kv_append_primary(ctypes.byref(k), 2, FAKE, 0, FAKE, FAKE, 12, None) == 1
     assert lib.dfx_kv_append_primary(ctypes.byref(k), 2, FAKE, 3, FAKE, FAKE, 0, None) == 1
