@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--splits", type=int, default=0, help="attention context splits (0 = plan)")
     p.add_argument("--kernel-reps", type=int, default=20)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run the plain copy kernel on BYTES (5 launches): the reference "
+                        "for scaling hardware traffic counters")
     return p.parse_args()
 
 
@@ -124,6 +127,15 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     extra = {}
+    if args.copy_calibration:
+        n = args.copy_calibration - args.copy_calibration % 16
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dfx.copy_bytes(dst, src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
 
     if args.workload == "layer":
         c = gen.config_layer()
