@@ -41,8 +41,12 @@ constexpr int kMaxChunk = 8192;   // tokens: longer splits leave CUs idle when l
 #ifndef DFX_GEMM_TARGET
 #define DFX_GEMM_TARGET 256
 #endif
+#ifndef DFX_GEMM_MIN_STEPS
+#define DFX_GEMM_MIN_STEPS 8
+#endif
 constexpr int kTargetAttnGroups = DFX_ATTN_TARGET;
 constexpr int kTargetGemmGroups = DFX_GEMM_TARGET;
+constexpr int kMinGemmSteps = DFX_GEMM_MIN_STEPS;  // k-steps of 32 per split, at least
 
 dfx_status check_kv(const dfx_kv_cache *kv, int32_t batch) {
   if (!kv) return fail(DFX_EINVAL, "kv is NULL");
@@ -107,33 +111,34 @@ size_t attn_ws_bytes(int splits, int n_flows, int batch, int hq, int d) {
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
 }
 
-// The linear kernel tiles 64 output features per work-group (16 per wave) and may split K
-// over ksplit work-groups, whose fp32 tiles a second kernel sums in split order.
+// The linear kernel tiles 128 output features per work-group (32 per wave) and may split K
+// over ksplit work-groups of kper k-steps each, whose fp32 tiles a second kernel (or the
+// layer's finish kernel) sums in split order. Splits are whole multiples of the kernel's
+// 4-step unroll where K allows, so no split streams padding steps.
 struct GemmPlan {
-  int ksplit, tiles, groups;
+  int ksplit, kper, tiles, groups;
   size_t partial_bytes;
   size_t total() const { return partial_bytes; }
 };
 
 GemmPlan gemm_plan(int n_flows, int rows, int K, int N) {
   GemmPlan g{};
-  g.tiles = (N + 63) / 64;
+  g.tiles = (N + 127) / 128;
   const int nks = K / 32;
-  int ks = (kTargetGemmGroups + g.tiles - 1) / g.tiles;
-  const int max_ks = nks / 16 > 1 ? nks / 16 : 1;  // keep >= 16 k-steps per work-group
+  // about kTargetGemmGroups work-groups (one per CU): more would add split-K partial
+  // traffic faster than they add bandwidth
+  int ks = kTargetGemmGroups / g.tiles;
+  const int max_ks = nks / kMinGemmSteps > 1 ? nks / kMinGemmSteps : 1;
   if (ks > max_ks) ks = max_ks;
   if (ks > 16) ks = 16;
   if (ks < 1) ks = 1;
-  if (K % 256 == 0) {
-    // the chunked kernel splits K into whole 256-column chunks: `per` chunks per split
-    const int nch = K / 256;
-    const int per = (nch + ks - 1) / ks;
-    ks = (nch + per - 1) / per;
-  }
-  g.ksplit = ks;
+  int per = (nks + ks - 1) / ks;
+  if (ks > 1) per = (per + 3) / 4 * 4;
+  g.kper = per;
+  g.ksplit = (nks + per - 1) / per;
   const int rpg = 64 / n_flows;
   g.groups = rows > 0 ? (rows + rpg - 1) / rpg : 0;
-  if (ks > 1) g.partial_bytes = round_up((size_t)ks * g.groups * 64 * N * sizeof(float), 256);
+  if (g.ksplit > 1) g.partial_bytes = round_up((size_t)g.ksplit * g.groups * 64 * N * sizeof(float), 256);
   return g;
 }
 
@@ -146,6 +151,7 @@ dfx_status check_linear(int32_t n_flows, int32_t rows, int32_t K, int32_t N) {
 }
 
 // partial: >= plan.partial_bytes of scratch (unused when the plan has one K split).
+// x_f32: 0 bf16 row-major, 1 fp32 row-major, 2 bf16 in the fragment order of xpack_offset.
 dfx_status run_linear_parts(int32_t n_flows, int32_t rows, int32_t K, int32_t N, int x_f32,
                             const void *x, const uint16_t *w, int w_packed, int y_bf16, void *y,
                             const float *couple, const float *residual, float *partial,
@@ -154,8 +160,9 @@ dfx_status run_linear_parts(int32_t n_flows, int32_t rows, int32_t K, int32_t N,
   const GemmPlan g = gemm_plan(n_flows, rows, K, N);
   GemmArgs a{};
   a.n_flows = n_flows; a.rows = rows; a.K = K; a.N = N;
-  a.x_f32 = x_f32; a.x = x; a.w = w; a.w_packed = w_packed; a.y_bf16 = y_bf16; a.y = y;
-  a.couple = couple; a.residual = residual; a.ksplit = g.ksplit;
+  a.x_f32 = x_f32 == 1; a.x_packed = x_f32 == 2;
+  a.x = x; a.w = w; a.w_packed = w_packed; a.y_bf16 = y_bf16; a.y = y;
+  a.couple = couple; a.residual = residual; a.ksplit = g.ksplit; a.kper = g.kper;
   a.partial = g.ksplit > 1 || tiles_only ? partial : nullptr;
   a.tiles_only = tiles_only;
   return hip_status(launch_grouped_linear(a, s), "grouped_linear launch");
@@ -185,7 +192,8 @@ struct AttnCall {
   int32_t splits;
   void *ws;
   size_t ws_bytes;
-  int32_t o_bf16;  // layer-internal: outputs rounded to bf16 (the rows entering W_o)
+  int32_t o_bf16;  // layer-internal: 1 = outputs rounded to bf16 (the rows entering W_o),
+                   // 2 = bf16 in the grouped linear's fragment order, both flows from o1
 };
 
 dfx_status validate_attn(const AttnCall &c) {
@@ -240,7 +248,7 @@ dfx_status run_attn(const AttnCall &c, hipStream_t s) {
   a.a = c.a; a.a_hstride = c.a_stride;
   const float scale = c.scale > 0.f ? c.scale : 1.0f / sqrtf((float)kv->head_dim);
   a.scale_log2 = scale * kLog2e;
-  a.o1 = c.o1; a.o2 = c.o2; a.lse = c.lse; a.o_bf16 = c.o_bf16;
+  a.o1 = c.o1; a.o2 = c.o2; a.lse = c.lse; a.o_bf16 = c.o_bf16 != 0; a.o_packed = c.o_bf16 == 2;
   a.num_splits = splits; a.chunk = chunk;
   if (splits > 1) {
     const size_t rows = (size_t)splits * F * c.batch * c.hq;
@@ -414,9 +422,11 @@ dfx_status layer_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_
   const int Nqkv = (Hq + 2 * w->num_kv_heads) * D, I = w->intermediate;
   LayerPlan p{};
   auto a256 = [](size_t x) { return round_up(x, 256); };
-  p.h = a256((size_t)F * B * (H > I ? H : I) * 2);  // normed rows, then the MLP intermediate
-  p.qkv = a256((size_t)F * B * Nqkv * 4);           // Q columns (row stride Nqkv)
-  p.o = a256((size_t)F * B * Hq * D * 2);           // attention rows (bf16)
+  // bf16 rows entering a projection are stored in its fragment order: 64 rows per group
+  const size_t prow = (size_t)(B + 64 / F - 1) / (64 / F) * 64;
+  p.h = a256(prow * (H > I ? H : I) * 2);  // normed rows, then the MLP intermediate
+  p.qkv = a256((size_t)F * B * Nqkv * 4);  // Q columns (row stride Nqkv)
+  p.o = a256(prow * Hq * D * 2);           // attention rows (bf16)
   int chunk;
   attn_plan(B, kv->num_kv_heads, max_context, 0, paged_bs(kv), &p.splits, &chunk);
   p.attn_ws = a256(attn_ws_bytes(p.splits, F, B, Hq, D));
@@ -479,25 +489,25 @@ dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_c
   g.kv = *kv; g.ctx = context_lens; g.num_q_heads = Hq; g.head_dim = D;
   auto ksplit = [&](int K, int N) { return gemm_plan(F, B, K, N).ksplit; };
   // attention block: norm, shared Q/K/V projection, primary-only append, dual attention
-  if ((r = hip_status(launch_rmsnorm(rows, H, x, w->attn_norm_gain, w->rms_eps, h, s), "rmsnorm launch"))) return r;
-  if ((r = run_linear_parts(F, B, H, Nqkv, 0, h, w->w_qkv, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  if ((r = hip_status(launch_rmsnorm(rows, H, x, w->attn_norm_gain, w->rms_eps, h, s, F), "rmsnorm launch"))) return r;
+  if ((r = run_linear_parts(F, B, H, Nqkv, 2, h, w->w_qkv, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
   g.N = Nqkv; g.ksplit = ksplit(H, Nqkv); g.out = qkv;
   if ((r = hip_status(launch_layer_glue(kGlueQkv, g, s), "qkv finish launch"))) return r;
-  // attention writes its rows already rounded to bf16 (the rows entering W_o)
+  // attention writes its rows already rounded to bf16, in W_o's fragment order
   AttnCall c{kv, context_lens, B, max_context, Hq, DFX_F32, qkv, F == 2 ? qkv + (size_t)B * Nqkv : nullptr,
              Nqkv, F == 2 ? w->couple_a : nullptr, 0, 0.f, (float *)ob,
-             F == 2 ? (float *)(ob + (size_t)B * Hq * D) : nullptr, nullptr, 0, aws, p.attn_ws, 1};
+             F == 2 ? (float *)ob : nullptr, nullptr, 0, aws, p.attn_ws, 2};
   if ((r = run_attn(c, s))) return r;
   // output projection + residual, then the MLP norm
-  if ((r = run_linear_parts(F, B, Hq * D, H, 0, ob, w->w_o, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  if ((r = run_linear_parts(F, B, Hq * D, H, 2, ob, w->w_o, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
   g.N = H; g.ksplit = ksplit(Hq * D, H); g.gain = w->mlp_norm_gain;
   if ((r = hip_status(launch_layer_glue(kGlueONorm, g, s), "o finish launch"))) return r;
   // MLP: shared gate/up projection, SwiGLU with b coupling, shared down projection with
   // c coupling and the residual
-  if ((r = run_linear_parts(F, B, H, 2 * I, 0, h, w->w_gate_up, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  if ((r = run_linear_parts(F, B, H, 2 * I, 2, h, w->w_gate_up, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
   g.N = 2 * I; g.ksplit = ksplit(H, 2 * I); g.couple = F == 2 ? w->couple_b : nullptr;
   if ((r = hip_status(launch_layer_glue(kGlueSwiglu, g, s), "swiglu finish launch"))) return r;
-  if ((r = run_linear_parts(F, B, I, H, 0, h, w->w_down, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  if ((r = run_linear_parts(F, B, I, H, 2, h, w->w_down, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
   g.N = H; g.ksplit = ksplit(I, H); g.couple = F == 2 ? w->couple_c : nullptr;
   return hip_status(launch_layer_glue(kGlueDown, g, s), "down finish launch");
   DFX_END

@@ -59,8 +59,8 @@ __device__ __forceinline__ void store_result(const AttnArgs &p, int split, int b
   const float o = L > 0.f ? O / L : 0.f;
   const float lse2 = L > 0.f ? M + __log2f(L) : -INFINITY;
   if (p.num_splits == 1) {
-    float *out = f == 0 ? p.o1 : p.o2;
-    const int64_t oi = ((int64_t)b * Hq + h) * D + d;
+    int64_t oi;
+    float *out = attn_out(p, f, b, h * D + d, &oi);
     if (p.o_bf16) ((uint16_t *)out)[oi] = (uint16_t)f32_to_bf16_rne(o);
     else out[oi] = o;
     if (d == 0 && p.lse) p.lse[((int64_t)f * p.batch + b) * Hq + h] = lse2 * kLn2;
@@ -365,13 +365,13 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs p) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) O[k] += c * po[lane + 64 * k];
   }
-  float *out = f == 0 ? p.o1 : p.o2;
-  const int64_t ob = ((int64_t)b * Hq + h) * D;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const float o = nvalid ? O[k] / L : 0.f;
-    if (p.o_bf16) ((uint16_t *)out)[ob + lane + 64 * k] = (uint16_t)f32_to_bf16_rne(o);
-    else out[ob + lane + 64 * k] = o;
+    int64_t oi;
+    float *out = attn_out(p, f, b, h * D + lane + 64 * k, &oi);
+    if (p.o_bf16) ((uint16_t *)out)[oi] = (uint16_t)f32_to_bf16_rne(o);
+    else out[oi] = o;
   }
   if (lane == 0 && p.lse)
     p.lse[((int64_t)f * p.batch + b) * Hq + h] = nvalid ? (M + __log2f(L)) * kLn2 : -INFINITY;

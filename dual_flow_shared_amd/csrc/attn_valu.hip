@@ -126,8 +126,8 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs p) {
       const float o = L > 0.f ? acc[i] / L : 0.f;
       const float lse2 = L > 0.f ? M + __log2f(L) : -INFINITY;
       if (p.num_splits == 1) {
-        float *out = f == 0 ? p.o1 : p.o2;
-        const int64_t oi = ((int64_t)b * p.num_q_heads + h) * D + d;
+        int64_t oi;
+        float *out = attn_out(p, f, b, h * D + d, &oi);
         if (p.o_bf16) ((uint16_t *)out)[oi] = (uint16_t)f32_to_bf16_rne(o);
         else out[oi] = o;
         if (d == 0 && p.lse) p.lse[((int64_t)f * p.batch + b) * p.num_q_heads + h] = lse2 * kLn2;

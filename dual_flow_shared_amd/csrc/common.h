@@ -47,6 +47,17 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Element offset of row r of flow f, column k, in the fragment-ordered activations that the
+// grouped linear reads directly: [groups][K/32][4 blocks][64 lanes][8]. Row group r / (64/F)
+// holds row q = f (64/F) + r % (64/F); lane (q % 16) + 16 ((k % 32) / 8) of block q / 16
+// holds columns 8 ((k % 32) / 8) .. +7 of k-step k / 32, i.e. exactly one B operand of the
+// 16x16x32 MFMA. A buffer of F rows of B sequences holds ceil(B / (64/F)) * 64 * K elements.
+__device__ __forceinline__ int64_t xpack_offset(int F, int f, int r, int k, int K) {
+  const int rpg = 64 / F, grp = r / rpg, q = f * rpg + r % rpg;
+  return ((((int64_t)grp * (K >> 5) + (k >> 5)) * 4 + (q >> 4)) * 64 + (q & 15) + 16 * ((k & 31) >> 3)) * 8 +
+         (k & 7);
+}
+
 // ---- launch-time parameter blocks --------------------------------------------------
 
 struct AttnArgs {
@@ -65,6 +76,7 @@ struct AttnArgs {
   float scale_log2;  // softmax scale * log2(e)
   float *o1, *o2, *lse;
   int32_t o_bf16;  // o1/o2 hold bf16 (uint16) rows instead of fp32
+  int32_t o_packed;  // bf16 rows in the grouped linear's fragment order, both flows in o1
   float *part_o, *part_lse;  // [S][F][B][Hq][D], [S][F][B][Hq] (log2 domain)
   int32_t num_splits, chunk;
 };
@@ -72,16 +84,31 @@ struct AttnArgs {
 struct GemmArgs {
   int32_t n_flows, rows, K, N;
   int32_t x_f32;
+  int32_t x_packed;  // bf16 rows in the fragment order of xpack_offset instead of row-major
   const void *x;
   const uint16_t *w;
   int32_t w_packed;  // DFX_W_PACKED fragment order instead of row-major
   int32_t y_bf16;
   void *y;
   const float *couple, *residual;
-  int32_t ksplit;      // work-groups along K per 64-feature tile
+  int32_t ksplit;      // work-groups along K per feature tile
+  int32_t kper;        // k-steps of 32 per split (the last split may have fewer)
   float *partial;      // [ksplit][groups][64 rows][N] fp32 when ksplit > 1 or tiles_only
   int32_t tiles_only;  // write the fp32 tiles even for one split (a finish kernel follows)
 };
+
+// Destination of attention output (flow f, sequence b, column c = head * D + d): rows
+// [B][Hq * D] of o1 / o2, or, with o_packed, both flows in o1 in the fragment order of
+// xpack_offset (K = Hq * D). Returns the row base pointer; *off receives the element offset.
+__device__ __forceinline__ float *attn_out(const AttnArgs &p, int f, int b, int c, int64_t *off) {
+  const int K = p.num_q_heads * p.head_dim;
+  if (p.o_packed) {
+    *off = xpack_offset(p.n_flows, f, b, c, K);
+    return p.o1;
+  }
+  *off = (int64_t)b * K + c;
+  return f == 0 ? p.o1 : p.o2;
+}
 
 // Arguments of the kernels that finish a projection of the decode layer.
 enum { kGlueQkv = 0, kGlueONorm = 1, kGlueSwiglu = 2, kGlueDown = 3 };
@@ -90,7 +117,7 @@ struct LayerGlueArgs {
   const float *tiles;  // [ksplit][groups][64][N]
   float *out;          // qkv: Q columns [F][B][N] fp32
   float *x;            // residual rows [F][B][N] fp32 (in place)
-  uint16_t *h;         // bf16 rows for the next projection
+  uint16_t *h;         // bf16 rows for the next projection (fragment order, xpack_offset)
   const float *gain;   // RMSNorm gain
   float eps;
   const float *couple; // b (SwiGLU) or c (down) coupling vector, or NULL
@@ -110,8 +137,10 @@ hipError_t launch_grouped_linear(const GemmArgs &g, hipStream_t s);
 hipError_t launch_pack_weight(int32_t N, int32_t K, const uint16_t *w, uint16_t *packed,
                               hipStream_t s);
 hipError_t launch_layer_glue(int which, const LayerGlueArgs &a, hipStream_t s);
+// packed_flows > 0: y in the fragment order of xpack_offset for that many flows (rows =
+// flows x batch); 0: row-major.
 hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
-                          uint16_t *y, hipStream_t s);
+                          uint16_t *y, hipStream_t s, int packed_flows = 0);
 hipError_t launch_swiglu(int32_t n_flows, int32_t rows, int32_t dim, const float *gu,
                          const float *b, uint16_t *out, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);

@@ -4,36 +4,41 @@
 
 namespace dfx {
 
-// One work-group per row; each thread owns dim/256 elements read as float4.
-__global__ void __launch_bounds__(256) rmsnorm_kernel(int32_t dim, const float *x,
-                                                      const float *gain, float eps, uint16_t *y) {
-  __shared__ float red[4];
+// One work-group of 1024 threads per row; each thread owns float4 slices of the row.
+// packed_flows > 0: row r = f * batch + b is written in the fragment order of xpack_offset.
+__global__ void __launch_bounds__(1024) rmsnorm_kernel(int32_t dim, const float *x,
+                                                       const float *gain, float eps, uint16_t *y,
+                                                       int packed_flows, int batch) {
+  __shared__ float red[16];
   const int64_t row = blockIdx.x;
   const f32x4 *xr = (const f32x4 *)(x + row * dim);
   const int n4 = dim / 4;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n4; i += 256) {
+  for (int i = threadIdx.x; i < n4; i += 1024) {
     const f32x4 v = xr[i];
     ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  float tot = 0.f;
+  for (int w = 0; w < 16; ++w) tot += red[w];
   const float r = 1.0f / sqrtf(tot / (float)dim + eps);
   const f32x4 *g4 = (const f32x4 *)gain;
-  u32x2 *yr = (u32x2 *)(y + row * dim);
-  for (int i = threadIdx.x; i < n4; i += 256) {
+  const int f = packed_flows ? (int)(row / batch) : 0, b = packed_flows ? (int)(row % batch) : 0;
+  for (int i = threadIdx.x; i < n4; i += 1024) {
     const f32x4 v = xr[i], gg = g4[i];
-    yr[i] = u32x2{pack_bf16x2(v[0] * r * gg[0], v[1] * r * gg[1]),
-                  pack_bf16x2(v[2] * r * gg[2], v[3] * r * gg[3])};
+    const u32x2 o{pack_bf16x2(v[0] * r * gg[0], v[1] * r * gg[1]), pack_bf16x2(v[2] * r * gg[2], v[3] * r * gg[3])};
+    const int64_t at = packed_flows ? xpack_offset(packed_flows, f, b, 4 * i, dim) : row * dim + 4 * i;
+    *(u32x2 *)(y + at) = o;
   }
 }
 
 hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
-                          uint16_t *y, hipStream_t s) {
+                          uint16_t *y, hipStream_t s, int packed_flows) {
   if (rows == 0) return hipSuccess;
-  rmsnorm_kernel<<<rows, 256, 0, s>>>(dim, x, gain, eps, y);
+  rmsnorm_kernel<<<rows, 1024, 0, s>>>(dim, x, gain, eps, y, packed_flows,
+                                       packed_flows ? rows / packed_flows : rows);
   return hipGetLastError();
 }
 

@@ -60,16 +60,17 @@ __global__ void __launch_bounds__(256) qkv_finish_kernel(LayerGlueArgs a) {
   *(u32x2 *)(pool + dst) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
-// x += sum of the W_o tiles (in place), then h = bf16(rmsnorm(x) * gain). One work-group
-// per (flow, row); each thread owns N / 256 columns as float4.
-__global__ void __launch_bounds__(256) o_finish_norm_kernel(LayerGlueArgs a) {
-  __shared__ float red[4];
+// x += sum of the W_o tiles (in place), then h = bf16(rmsnorm(x) * gain) in the fragment
+// order of the next projection (xpack_offset). One work-group of 1024 threads per
+// (flow, row); each thread owns 4-column slices as float4.
+__global__ void __launch_bounds__(1024) o_finish_norm_kernel(LayerGlueArgs a) {
+  __shared__ float red[16];
   const int F = a.n_flows, B = a.batch, N = a.N;
   const int rpg = 64 / F, groups = (B + rpg - 1) / rpg;
   const int row = blockIdx.x, f = row / B, b = row % B;
   float *xr = a.x + (int64_t)row * N;
   float ss = 0.f;
-  for (int col = 4 * threadIdx.x; col < N; col += 1024) {
+  for (int col = 4 * threadIdx.x; col < N; col += 4096) {
     f32x4 v = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, col) + *(const f32x4 *)(xr + col);
     *(f32x4 *)(xr + col) = v;
     ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
@@ -77,19 +78,21 @@ __global__ void __launch_bounds__(256) o_finish_norm_kernel(LayerGlueArgs a) {
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float r = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)N + a.eps);
-  uint16_t *hr = a.h + (int64_t)row * N;
-  for (int col = 4 * threadIdx.x; col < N; col += 1024) {
+  float tot = 0.f;
+  for (int w = 0; w < 16; ++w) tot += red[w];
+  const float r = 1.0f / sqrtf(tot / (float)N + a.eps);
+  for (int col = 4 * threadIdx.x; col < N; col += 4096) {
     const f32x4 v = *(const f32x4 *)(xr + col), g = *(const f32x4 *)(a.gain + col);
-    *(u32x2 *)(hr + col) = u32x2{pack_bf16x2(v[0] * r * g[0], v[1] * r * g[1]),
-                                 pack_bf16x2(v[2] * r * g[2], v[3] * r * g[3])};
+    *(u32x2 *)(a.h + xpack_offset(F, f, b, col, N)) =
+        u32x2{pack_bf16x2(v[0] * r * g[0], v[1] * r * g[1]), pack_bf16x2(v[2] * r * g[2], v[3] * r * g[3])};
   }
 }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// inter = silu(gate) * up from the summed gate/up tiles; flow 1 += b * flow 0; bf16 out.
-// One thread per 4 intermediate columns of one row index (both flows).
+// inter = silu(gate) * up from the summed gate/up tiles; flow 1 += b * flow 0; bf16 out in
+// the fragment order of the down projection (xpack_offset). One thread per 4 intermediate
+// columns of one row index (both flows).
 __global__ void __launch_bounds__(256) gu_finish_swiglu_kernel(LayerGlueArgs a) {
   const int F = a.n_flows, B = a.batch, N = a.N, I = N / 2;
   const int rpg = 64 / F, groups = (B + rpg - 1) / rpg;
@@ -108,8 +111,7 @@ __global__ void __launch_bounds__(256) gu_finish_swiglu_kernel(LayerGlueArgs a) 
       v = f32x4{fmaf(c[0], prim[0], v[0]), fmaf(c[1], prim[1], v[1]), fmaf(c[2], prim[2], v[2]),
                 fmaf(c[3], prim[3], v[3])};
     }
-    *(u32x2 *)(a.h + ((int64_t)f * B + b) * I + col) =
-        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *(u32x2 *)(a.h + xpack_offset(F, f, b, col, I)) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   }
 }
 
@@ -145,7 +147,7 @@ hipError_t launch_layer_glue(int which, const LayerGlueArgs &a, hipStream_t s) {
       qkv_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a);
       break;
     case kGlueONorm:
-      o_finish_norm_kernel<<<F * B, 256, 0, s>>>(a);
+      o_finish_norm_kernel<<<F * B, 1024, 0, s>>>(a);
       break;
     case kGlueSwiglu:
       threads = (int64_t)B * (a.N / 8);

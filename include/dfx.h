@@ -54,9 +54,9 @@ typedef enum { DFX_F32 = 0, DFX_BF16 = 1 } dfx_dtype;
 /* Layout of a bf16 weight matrix W with N output and K input features.
  *  DFX_W_ROW_MAJOR: W[n][k] at n*K + k.
  *  DFX_W_PACKED:    matrix-core fragment order (see dfx_pack_weight): each 16-row x
- *                   32-column block is 1 KiB contiguous and a 16-row slab is one
- *                   contiguous stream, so the grouped linear reads weights at full
- *                   HBM burst length. */
+ *                   32-column block is 1 KiB contiguous and the blocks of one
+ *                   32-column slice of all rows are adjacent, so the grouped linear's
+ *                   work-groups read neighbouring KiB runs at full HBM burst length. */
 typedef enum { DFX_W_ROW_MAJOR = 0, DFX_W_PACKED = 1 } dfx_weight_layout;
 
 /*
@@ -177,9 +177,9 @@ dfx_status dfx_kv_append_primary(const dfx_kv_cache *kv, int32_t batch, const in
  *           (in-place residual update), must not overlap x or w.
  *  couple   device fp32 [out_features] or NULL; residual device fp32 or NULL.
  *  workspace  device scratch of >= dfx_grouped_linear_workspace_size bytes (may be
- *           NULL when that is 0). It must be zero-filled before its first use; every
- *           completed call leaves it ready for the next one (its arrival counters
- *           back at zero). Calls sharing one workspace must not overlap in time.
+ *           NULL when that is 0): the fp32 partial tiles of the K splits, fully
+ *           written by each call before they are read (no initial contents needed).
+ *           Calls sharing one workspace must not overlap in time.
  * The K-reduction order of every output element is fixed by (in_features,
  * out_features) alone: flow-0 outputs are bit-identical for n_flows 1 and 2
  * and for any row count.
@@ -195,7 +195,7 @@ dfx_status dfx_grouped_linear(int32_t n_flows, int32_t rows, int32_t in_features
 
 /*
  * Reorder a row-major bf16 weight matrix into DFX_W_PACKED (a pure permutation, done once
- * per static weight): packed[((t * K/32 + s) * 64 + l) * 8 + v] = w[16 t + l % 16][32 s +
+ * per static weight): packed[((s * N/16 + t) * 64 + l) * 8 + v] = w[16 t + l % 16][32 s +
  * 8 (l / 16) + v] for t < N/16, s < K/32, l < 64, v < 8. N must be a multiple of 16 and K
  * of 32; w and packed are device buffers of N*K elements that must not overlap.
  */

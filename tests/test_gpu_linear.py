@@ -21,6 +21,7 @@ LIN = [
     (1, 1, 32, 16),
     (2, 40, 256, 128),      # rows of one flow span two row groups
     (1, 100, 512, 64),
+    (2, 17, 4128, 272),     # ragged K splits (129 k-steps) and an odd number of 16-column groups
 ]
 
 
@@ -47,8 +48,8 @@ def test_pack_weight_is_the_fragment_permutation():
     N, K = 48, 96
     w = rng.integers(0, 65535, size=(N, K), dtype=np.uint16)
     got = host_bits(dfx.pack_weight(dev(w)))
-    # packed[t][s][lane = n + 16 j][v] = w[16 t + n][32 s + 8 j + v]
-    want = w.reshape(N // 16, 16, K // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(N, K)
+    # packed[s][t][lane = n + 16 j][v] = w[16 t + n][32 s + 8 j + v]
+    want = w.reshape(N // 16, 16, K // 32, 4, 8).transpose(2, 0, 3, 1, 4).reshape(N, K)
     assert np.array_equal(got, want)
 
 
