@@ -13,12 +13,12 @@ from typing import Optional
 import torch
 
 from ._abi import (DFX_BF16, DFX_F32, DFX_W_PACKED, DFX_W_ROW_MAJOR, DfxError, KVCacheStruct,
-                   LayerWeightsStruct, check, lib)
+                   LayerTapsStruct, LayerWeightsStruct, check, lib)
 
 __all__ = ["DfxError", "KVCache", "LayerWeights", "decode_attn", "decode_attn_plan",
            "kv_append_primary", "grouped_linear", "pack_weight", "rmsnorm", "swiglu_couple",
            "dual_flow_decode_layer", "layer_workspace_size", "copy_bytes", "read_bytes", "fill_bytes",
-           "Workspace", "version"]
+           "layer_taps", "Workspace", "version"]
 
 
 def version() -> int:
@@ -53,8 +53,8 @@ def _contig(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 class Workspace:
-    """A zero-filled device byte buffer grown on demand (the library's split-K counters
-    need zero on first use and leave it zero after each call)."""
+    """A device byte buffer grown on demand (scratch for the library's split partials and
+    the layer's intermediates)."""
 
     def __init__(self, device=None):
         self.device = torch.device("cuda") if device is None else torch.device(device)
@@ -70,8 +70,8 @@ _default_ws = {}
 
 
 def _workspace(ws: Optional[Workspace], device, purpose: str) -> Workspace:
-    """Default workspaces are kept per device and per purpose: split-K counters of the
-    linear and layer calls must not share memory with attention partials."""
+    """Default workspaces are kept per device and per purpose, so that the intermediates a
+    layer call leaves in its workspace survive later calls of other entry points."""
     if ws is not None:
         return ws
     d = torch.device(device)
@@ -294,6 +294,17 @@ def dual_flow_decode_layer(x: torch.Tensor, weights: LayerWeights, cache: KVCach
     check(lib().dfx_dual_flow_decode_layer(ctypes.byref(w), ctypes.byref(c), _ptr(context_lens), B,
                                            max_context, F, _ptr(x), _ptr(ws), need, _stream(stream)))
     return x
+
+
+def layer_taps(weights: LayerWeights, cache: KVCache, batch: int, n_flows: int,
+               max_context: int) -> dict:
+    """Byte offsets of a layer call's intermediates in its workspace: h1, q, o, h2, inter
+    (layouts in include/dfx.h, dfx_dual_flow_decode_layer_taps)."""
+    t = LayerTapsStruct()
+    w, c = weights.struct(), cache.struct()
+    check(lib().dfx_dual_flow_decode_layer_taps(ctypes.byref(w), ctypes.byref(c), batch, n_flows,
+                                                max_context, ctypes.byref(t)))
+    return {name: getattr(t, name) for name, _ in t._fields_}
 
 
 def copy_bytes(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

@@ -35,6 +35,11 @@ class LayerWeightsStruct(ctypes.Structure):
                 ("couple_a", P), ("couple_b", P), ("couple_c", P)]
 
 
+class LayerTapsStruct(ctypes.Structure):
+    _fields_ = [("h1", ctypes.c_size_t), ("q", ctypes.c_size_t), ("o", ctypes.c_size_t),
+                ("h2", ctypes.c_size_t), ("inter", ctypes.c_size_t)]
+
+
 KVP = ctypes.POINTER(KVCacheStruct)
 LWP = ctypes.POINTER(LayerWeightsStruct)
 PSZ = ctypes.POINTER(ctypes.c_size_t)
@@ -53,6 +58,7 @@ SIGNATURES = {
     "dfx_swiglu_couple": (I32, [I32, I32, I32, P, P, P, P]),
     "dfx_dual_flow_decode_layer_workspace_size": (I32, [LWP, KVP, I32, I32, I32, PSZ]),
     "dfx_dual_flow_decode_layer": (I32, [LWP, KVP, P, I32, I32, I32, P, P, SZ, P]),
+    "dfx_dual_flow_decode_layer_taps": (I32, [LWP, KVP, I32, I32, I32, ctypes.POINTER(LayerTapsStruct)]),
     "dfx_copy_bytes": (I32, [P, P, SZ, P]),
     "dfx_read_bytes": (I32, [P, SZ, P, P]),
     "dfx_fill_bytes": (I32, [P, SZ, U32, P]),

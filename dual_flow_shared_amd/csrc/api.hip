@@ -397,8 +397,12 @@ dfx_status dfx_swiglu_couple(int32_t n_flows, int32_t rows, int32_t dim, const f
 
 namespace {
 
+// Workspace regions of one layer call, in this order: the projections' split-K tiles, then
+// every intermediate the step rounds to bf16 or hands on, each in a region of its own so
+// that it can be inspected after the call (dfx_dual_flow_decode_layer_taps), then the
+// attention's split partials.
 struct LayerPlan {
-  size_t h, qkv, o, attn_ws, tiles, total;
+  size_t tiles, h1, qkv, o, h2, inter, attn_ws, total;
   int splits;
 };
 
@@ -424,9 +428,11 @@ dfx_status layer_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_
   auto a256 = [](size_t x) { return round_up(x, 256); };
   // bf16 rows entering a projection are stored in its fragment order: 64 rows per group
   const size_t prow = (size_t)(B + 64 / F - 1) / (64 / F) * 64;
-  p.h = a256(prow * (H > I ? H : I) * 2);  // normed rows, then the MLP intermediate
+  p.h1 = a256(prow * H * 2);               // normed rows entering W_qkv
   p.qkv = a256((size_t)F * B * Nqkv * 4);  // Q columns (row stride Nqkv)
-  p.o = a256(prow * Hq * D * 2);           // attention rows (bf16)
+  p.o = a256(prow * Hq * D * 2);           // attention rows entering W_o
+  p.h2 = a256(prow * H * 2);               // normed rows entering W_gate_up
+  p.inter = a256(prow * I * 2);            // SwiGLU rows entering W_down
   int chunk;
   attn_plan(B, kv->num_kv_heads, max_context, 0, paged_bs(kv), &p.splits, &chunk);
   p.attn_ws = a256(attn_ws_bytes(p.splits, F, B, Hq, D));
@@ -439,7 +445,7 @@ dfx_status layer_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_
     p.tiles = t > p.tiles ? t : p.tiles;
   }
   p.tiles = a256(p.tiles);
-  p.total = p.tiles + p.h + p.qkv + p.o + p.attn_ws;
+  p.total = p.tiles + p.h1 + p.qkv + p.o + p.h2 + p.inter + p.attn_ws;
   *pl = p;
   return DFX_OK;
 }
@@ -478,19 +484,21 @@ dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_c
   const int Hkv = w->num_kv_heads, Nqkv = (Hq + 2 * Hkv) * D, I = w->intermediate;
   char *base = (char *)workspace;
   float *tiles = (float *)base;
-  uint16_t *h = (uint16_t *)(base + p.tiles);
-  float *qkv = (float *)((char *)h + p.h);
+  uint16_t *h1 = (uint16_t *)(base + p.tiles);
+  float *qkv = (float *)((char *)h1 + p.h1);
   uint16_t *ob = (uint16_t *)((char *)qkv + p.qkv);
-  void *aws = (char *)ob + p.o;
+  uint16_t *h2 = (uint16_t *)((char *)ob + p.o);
+  uint16_t *inter = (uint16_t *)((char *)h2 + p.h2);
+  void *aws = (char *)inter + p.inter;
   const int rows = F * B;
   dfx_status r;
   LayerGlueArgs g{};
-  g.n_flows = F; g.batch = B; g.tiles = tiles; g.x = x; g.h = h; g.eps = w->rms_eps;
+  g.n_flows = F; g.batch = B; g.tiles = tiles; g.x = x; g.eps = w->rms_eps;
   g.kv = *kv; g.ctx = context_lens; g.num_q_heads = Hq; g.head_dim = D;
   auto ksplit = [&](int K, int N) { return gemm_plan(F, B, K, N).ksplit; };
   // attention block: norm, shared Q/K/V projection, primary-only append, dual attention
-  if ((r = hip_status(launch_rmsnorm(rows, H, x, w->attn_norm_gain, w->rms_eps, h, s, F), "rmsnorm launch"))) return r;
-  if ((r = run_linear_parts(F, B, H, Nqkv, 2, h, w->w_qkv, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  if ((r = hip_status(launch_rmsnorm(rows, H, x, w->attn_norm_gain, w->rms_eps, h1, s, F), "rmsnorm launch"))) return r;
+  if ((r = run_linear_parts(F, B, H, Nqkv, 2, h1, w->w_qkv, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
   g.N = Nqkv; g.ksplit = ksplit(H, Nqkv); g.out = qkv;
   if ((r = hip_status(launch_layer_glue(kGlueQkv, g, s), "qkv finish launch"))) return r;
   // attention writes its rows already rounded to bf16, in W_o's fragment order
@@ -500,16 +508,33 @@ dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_c
   if ((r = run_attn(c, s))) return r;
   // output projection + residual, then the MLP norm
   if ((r = run_linear_parts(F, B, Hq * D, H, 2, ob, w->w_o, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
-  g.N = H; g.ksplit = ksplit(Hq * D, H); g.gain = w->mlp_norm_gain;
+  g.N = H; g.ksplit = ksplit(Hq * D, H); g.gain = w->mlp_norm_gain; g.h = h2;
   if ((r = hip_status(launch_layer_glue(kGlueONorm, g, s), "o finish launch"))) return r;
   // MLP: shared gate/up projection, SwiGLU with b coupling, shared down projection with
   // c coupling and the residual
-  if ((r = run_linear_parts(F, B, H, 2 * I, 2, h, w->w_gate_up, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
-  g.N = 2 * I; g.ksplit = ksplit(H, 2 * I); g.couple = F == 2 ? w->couple_b : nullptr;
+  if ((r = run_linear_parts(F, B, H, 2 * I, 2, h2, w->w_gate_up, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  g.N = 2 * I; g.ksplit = ksplit(H, 2 * I); g.couple = F == 2 ? w->couple_b : nullptr; g.h = inter;
   if ((r = hip_status(launch_layer_glue(kGlueSwiglu, g, s), "swiglu finish launch"))) return r;
-  if ((r = run_linear_parts(F, B, I, H, 2, h, w->w_down, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  if ((r = run_linear_parts(F, B, I, H, 2, inter, w->w_down, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
   g.N = H; g.ksplit = ksplit(I, H); g.couple = F == 2 ? w->couple_c : nullptr;
   return hip_status(launch_layer_glue(kGlueDown, g, s), "down finish launch");
+  DFX_END
+}
+
+dfx_status dfx_dual_flow_decode_layer_taps(const dfx_layer_weights *w, const dfx_kv_cache *kv,
+                                           int32_t batch, int32_t n_flows, int32_t max_context,
+                                           dfx_layer_taps *taps) {
+  DFX_BEGIN
+  LayerPlan p;
+  dfx_status st = layer_plan(w, kv, batch, n_flows, max_context, &p);
+  if (st) return st;
+  if (!taps) return fail(DFX_EINVAL, "taps is NULL");
+  taps->h1 = p.tiles;
+  taps->q = taps->h1 + p.h1;
+  taps->o = taps->q + p.qkv;
+  taps->h2 = taps->o + p.o;
+  taps->inter = taps->h2 + p.h2;
+  return DFX_OK;
   DFX_END
 }
 

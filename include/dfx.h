@@ -253,6 +253,11 @@ typedef struct dfx_layer_weights {
   const float *couple_c;           /* [hidden] or NULL */
 } dfx_layer_weights;
 
+/* Byte offsets of a layer call's intermediates in its workspace (see below). */
+typedef struct dfx_layer_taps {
+  size_t h1, q, o, h2, inter;
+} dfx_layer_taps;
+
 /* Workspace bytes dfx_dual_flow_decode_layer needs for these sizes. */
 dfx_status dfx_dual_flow_decode_layer_workspace_size(const dfx_layer_weights *w,
                                                      const dfx_kv_cache *kv, int32_t batch,
@@ -262,23 +267,43 @@ dfx_status dfx_dual_flow_decode_layer_workspace_size(const dfx_layer_weights *w,
 /*
  * One decode step of one layer for both flows (n_flows = 2) or the primary
  * alone (n_flows = 1), in place on the fp32 residual rows x [n_flows][batch][hidden]:
- *   h  = rmsnorm(x, attn_norm_gain)                               (bf16)
- *   qkv = h W_qkv^T                                               (one weight pass, both flows)
- *   append K, V columns of the flow-0 rows at position context_lens[b] - 1
- *   o  = dfx_decode_attn(Q1 = flow-0 Q columns, q2_raw = flow-1 Q columns, a)
- *   x += o W_o^T                                                  (o rounded to bf16 on load)
- *   h  = rmsnorm(x, mlp_norm_gain)
- *   inter = swiglu_couple(h W_gate_up^T, b)
+ *   h1 = rmsnorm(x, attn_norm_gain)                               (bf16)
+ *   qkv = h1 W_qkv^T                                              (one weight pass, both flows)
+ *   append K, V columns of the flow-0 rows at position context_lens[b] - 1   (bf16)
+ *   o  = dfx_decode_attn(Q1 = flow-0 Q columns, q2_raw = flow-1 Q columns, a)   (bf16)
+ *   x += o W_o^T
+ *   h2 = rmsnorm(x, mlp_norm_gain)                                (bf16)
+ *   inter = swiglu_couple(h2 W_gate_up^T, b)                      (bf16)
  *   m  = inter W_down^T;  m[1] += c * m[0];  x += m
  * context_lens (device int32 [batch]) counts the positions attended in this
  * step, the new one included (>= 1). The flow-1 K, V columns are computed by
- * the shared projection and discarded. workspace: >= the size above, zero-filled
- * before its first use (as for dfx_grouped_linear; calls leave it reusable).
+ * the shared projection and discarded. workspace: >= the size above, no initial
+ * contents needed; after the call it holds the step's intermediates
+ * (dfx_dual_flow_decode_layer_taps). Calls sharing a workspace must not overlap.
  */
 dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv,
                                       const int32_t *context_lens, int32_t batch,
                                       int32_t max_context, int32_t n_flows, float *x,
                                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Where a completed dfx_dual_flow_decode_layer call with the same sizes leaves its
+ * intermediates in the workspace: byte offsets of
+ *   h1     bf16 normed rows entering W_qkv            [hidden columns]
+ *   q      fp32 rows [n_flows][batch][(Hq + 2 Hkv) * D]; columns < Hq * D hold the
+ *          flows' queries (q2_raw for flow 1), the rest is unspecified
+ *   o      bf16 attention rows entering W_o             [Hq * D columns]
+ *   h2     bf16 normed rows entering W_gate_up          [hidden columns]
+ *   inter  bf16 SwiGLU rows entering W_down            [intermediate columns]
+ * The bf16 regions use the activation fragment order of the grouped linear: element
+ * (flow f, sequence b, column k) of a K-column region sits at
+ *   ((((g * K/32 + k/32) * 4 + q/16) * 64 + q%16 + 16 ((k%32)/8)) * 8 + k%8)
+ * with R = 64 / n_flows, g = b / R, q = f R + b % R (64-row groups; rows past the batch
+ * are unspecified). The appended K/V rows are in the cache. Host-only: no GPU work.
+ */
+dfx_status dfx_dual_flow_decode_layer_taps(const dfx_layer_weights *w, const dfx_kv_cache *kv,
+                                           int32_t batch, int32_t n_flows, int32_t max_context,
+                                           struct dfx_layer_taps *taps);
 
 /*
  * Measurement helpers (not part of the method): a plain device copy of

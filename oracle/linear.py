@@ -34,20 +34,23 @@ def grouped_linear(x, w, couple=None, residual=None, y_bf16=False, dtype=np.floa
     return bf16_bits(Y) if y_bf16 else Y
 
 
-def rmsnorm(x, gain, eps, dtype=np.float64):
-    """y = x / sqrt(mean(x^2) + eps) * gain over the last axis, rounded to bf16 (fp64 values)."""
+def rmsnorm(x, gain, eps, dtype=np.float64, rounded=True):
+    """y = x / sqrt(mean(x^2) + eps) * gain over the last axis, rounded to bf16 (fp64 values);
+    rounded=False returns the value before that rounding."""
     X = widen(x).astype(dtype)
     r = dtype(1.0) / np.sqrt(np.mean(X * X, axis=-1, keepdims=True) + dtype(eps))
-    return round_bf16(X * r * widen(gain).astype(dtype))
+    y = X * r * widen(gain).astype(dtype)
+    return round_bf16(y) if rounded else y
 
 
-def swiglu_couple(gate_up, b=None, dtype=np.float64):
+def swiglu_couple(gate_up, b=None, dtype=np.float64, rounded=True):
     """inter = silu(gate) * up with gate_up = [gate | up] on the last axis; for
-    two flows inter[1] += b * inter[0]; rounded to bf16 (fp64 values)."""
+    two flows inter[1] += b * inter[0]; rounded to bf16 (fp64 values); rounded=False
+    returns the value before that rounding."""
     GU = widen(gate_up).astype(dtype)
     I = GU.shape[-1] // 2
     gate, up = GU[..., :I], GU[..., I:]
     inter = gate / (dtype(1.0) + np.exp(-gate)) * up
     if b is not None and inter.shape[0] == 2:
         inter[1] = inter[1] + widen(b).astype(dtype) * inter[0]
-    return round_bf16(inter)
+    return round_bf16(inter) if rounded else inter

@@ -74,3 +74,15 @@ def bf16_decisions_agree(gpu_bits, oracle_fp64, rel=2e-6, scale=None):
         ok = np.abs(g - x) <= rel * sc + half_ulp
         assert ok.all(), f"{(~ok).sum()} bf16 outputs farther from the exact value than rounding allows"
     return float(same.mean())
+
+
+def unpack_rows(region, n_flows, batch, K):
+    """[F][B][K] bf16 bits out of a region in the activation fragment order of the grouped
+    linear (include/dfx.h, dfx_dual_flow_decode_layer_taps): pure index arithmetic."""
+    R = 64 // n_flows
+    f = np.arange(n_flows)[:, None, None]
+    b = np.arange(batch)[None, :, None]
+    k = np.arange(K)[None, None, :]
+    g, q = b // R, f * R + b % R
+    idx = ((((g * (K // 32) + k // 32) * 4 + q // 16) * 64 + q % 16 + 16 * ((k % 32) // 8)) * 8 + k % 8)
+    return np.asarray(region)[idx]

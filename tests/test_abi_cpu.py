@@ -21,7 +21,7 @@ def declared():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = _abi.lib()
     names = declared()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, n
@@ -137,3 +137,26 @@ def test_layer_rejects():
     w.head_dim = 128
     k32 = kv(dtype=0, mb=512, nb=16384)
     assert lib.dfx_dual_flow_decode_layer_workspace_size(ctypes.byref(w), ctypes.byref(k32), 32, 2, 8192, ctypes.byref(n)) == 2
+
+
+def test_layer_taps_are_disjoint_regions_of_the_workspace():
+    lib = _abi.lib()
+    w = _abi.LayerWeightsStruct()
+    H, Hq, Hkv, D, I = 4096, 32, 8, 128, 14336
+    w.hidden, w.num_q_heads, w.num_kv_heads, w.head_dim, w.intermediate, w.rms_eps = H, Hq, Hkv, D, I, 1e-5
+    for f in ("attn_norm_gain", "w_qkv", "w_o", "mlp_norm_gain", "w_gate_up", "w_down"):
+        setattr(w, f, FAKE)
+    k = kv(mb=512, nb=16384)
+    for F, B in ((2, 32), (1, 32), (2, 40), (1, 1)):
+        n, t = ctypes.c_size_t(), _abi.LayerTapsStruct()
+        assert lib.dfx_dual_flow_decode_layer_workspace_size(ctypes.byref(w), ctypes.byref(k), B, F, 8192, ctypes.byref(n)) == 0
+        assert lib.dfx_dual_flow_decode_layer_taps(ctypes.byref(w), ctypes.byref(k), B, F, 8192, ctypes.byref(t)) == 0
+        rows = -(-B // (64 // F)) * 64                     # fragment order pads to 64-row groups
+        need = [("h1", rows * H * 2), ("q", F * B * (Hq + 2 * Hkv) * D * 4), ("o", rows * Hq * D * 2),
+                ("h2", rows * H * 2), ("inter", rows * I * 2)]
+        offs = [getattr(t, name) for name, _ in need]
+        assert all(o % 256 == 0 for o in offs)
+        for (name, size), start, nxt in zip(need, offs, offs[1:] + [n.value]):
+            assert start + size <= nxt, (F, B, name)
+    assert lib.dfx_dual_flow_decode_layer_taps(ctypes.byref(w), ctypes.byref(k), 32, 3, 8192, ctypes.byref(t)) == 1
+    assert lib.dfx_dual_flow_decode_layer_taps(ctypes.byref(w), ctypes.byref(k), 32, 2, 8192, None) == 1

@@ -5,8 +5,10 @@ import torch
 
 import dfx_inputs as gen
 import dual_flow_shared_amd as dfx
-from gpu_util import cache_of, dev, host_bits, max_err
+from gpu_util import bf16_decisions_agree, cache_of, dev, host_bits, unpack_rows
+from oracle.attention import decode_attention, gather_kv
 from oracle.layer import dual_flow_layer
+from oracle.linear import grouped_linear, rmsnorm, swiglu_couple
 from oracle.numerics import widen
 
 pytestmark = pytest.mark.gpu
@@ -38,23 +40,134 @@ def run_oracle(c, flows=2, x=None, couple=True, batches=None, dtype=np.float64):
                            dtype=dtype)
 
 
-def layer_close(y, want, twin):
-    """The layer rounds to bf16 at five points. Where a single-precision value and the
-    fp64 value straddle a bf16 midpoint they round to neighbours, and with fp32
-    accumulation over 4096-14336 terms about one element in a thousand does so; each
-    flip moves downstream outputs by ulp * |w|. The yardstick is the oracle's own
-    definition evaluated in float32 (`twin`): the kernel's distance from the fp64 oracle
-    must be of the same size -- max within 3x and mean within 4x the twin's (matrix-core
-    accumulation adds 32-term dot products sequentially, a little less accurately than a
-    blocked BLAS sum, so slightly more values flip) -- and the median within 2e-3."""
-    y, want, twin = (np.asarray(a, np.float64) for a in (y, want, twin))
-    err, ref = np.abs(y - want), np.abs(twin - want)
-    stats = dict(max=float(err.max()), mean=float(err.mean()), p50=float(np.median(err)),
-                 twin_max=float(ref.max()), twin_mean=float(ref.mean()))
-    print("layer error vs fp64 oracle:", stats)
-    assert stats["max"] <= 3 * stats["twin_max"] + 1e-3, stats
-    assert stats["mean"] <= 4 * stats["twin_mean"] + 1e-4, stats
-    assert stats["p50"] < 2e-3, stats
+def layer_close(y, want):
+    """End-to-end sanity against the fp64 oracle. The five bf16 rounding points make this
+    comparison discontinuous (an intermediate next to a rounding midpoint may land on either
+    neighbour, moving its row's downstream outputs by ulp * |w|), so it only bounds gross
+    deviations; the per-stage chain check below carries the precise claim."""
+    err = np.abs(np.asarray(y, np.float64) - np.asarray(want, np.float64))
+    print("layer error vs fp64 oracle: max %.3g mean %.3g p50 %.3g" % (err.max(), err.mean(), np.median(err)))
+    assert np.median(err) < 2e-3 and err.max() < 5e-2
+
+
+U = 2.0 ** -24                 # fp32 unit roundoff
+SPLIT = 2.0 ** -16             # relative error of a value split into two bf16 terms
+
+
+def gamma(k):
+    """Accumulation bound of a k-term fp32 dot product on the matrix cores: 32-term MFMA
+    blocks added in sequence over k / 32 steps, plus the split-K partial sums and the
+    residual add (a few more roundings)."""
+    return (k / 32 + 64) * U
+
+
+def check_layer_chain(c, flows=2, couple=True, rows=None):
+    """Runs the layer and checks every stage against the oracle applied to the GPU's own
+    previous stage (read from the workspace through dfx_dual_flow_decode_layer_taps): each
+    fp32 value within its accumulation bound, and every bf16 rounding decision (R1 normed
+    rows, R2 appended K/V, R3 attention rows, R4 normed rows, R5 SwiGLU rows) the rounding of
+    a value within that bound of the oracle's exact one. Returns (x_out, k pool, v pool)."""
+    F, B = flows, c.batch
+    H, Hq, Hkv, D = c.g_attn.shape[0], c.num_q_heads, c.num_kv_heads, c.head_dim
+    I = c.w_down.shape[1]
+    HqD, Nqkv = Hq * D, (Hq + 2 * Hkv) * D
+    rows = np.arange(B) if rows is None else np.asarray(rows)
+    cache = cache_of(c.cache)
+    ctx_after = c.cache.context_lens + 1
+    maxc = int(ctx_after.max())
+    xt = dev(c.x[:F].copy())
+    w = weights_of(c, couple)
+    ws = dfx.Workspace()
+    dfx.dual_flow_decode_layer(xt, w, cache, dev(ctx_after), maxc, workspace=ws)
+    torch.cuda.synchronize()
+    taps = dfx.layer_taps(w, cache, B, F, maxc)
+    buf = ws.buf.cpu().numpy()
+    padded = -(-B // (64 // F)) * 64
+
+    def bf16_region(name, K):
+        r = buf[taps[name]: taps[name] + padded * K * 2].view(np.uint16)
+        return unpack_rows(r, F, B, K)[:, rows]
+
+    h1, o, h2, inter = bf16_region("h1", H), bf16_region("o", HqD), bf16_region("h2", H), bf16_region("inter", I)
+    q = buf[taps["q"]: taps["q"] + F * B * Nqkv * 4].view(np.float32).reshape(F, B, Nqkv)[:, rows, :HqD]
+    x_out = xt.cpu().numpy().astype(np.float64)
+    kp, vp = host_bits(cache.k), host_bits(cache.v)
+    x0 = widen(c.x[:F][:, rows])
+    a_vec, b_vec, c_vec = (c.a, c.b, c.c) if (couple and F == 2) else (None, None, None)
+    absw = lambda m: np.abs(widen(m))
+
+    def norm_scale(xin, err_in, gain, y):
+        # y = x r g: error from the input's error (through x and through r) and from the
+        # fp32 norm (sum of squares over H terms, reciprocal square root, two products)
+        r = 1.0 / np.sqrt(np.mean(xin * xin, axis=-1, keepdims=True) + c.eps)
+        rel_r = np.linalg.norm(err_in, axis=-1, keepdims=True) / np.linalg.norm(xin, axis=-1, keepdims=True)
+        return np.abs(widen(gain)) * r * (err_in + np.abs(xin) * (rel_r + (H / 2 + 8) * U)) + 4 * U * np.abs(y)
+
+    # R1: normed rows from the exact input
+    h1_exact = rmsnorm(x0, c.g_attn, c.eps, rounded=False)
+    same = {"h1": bf16_decisions_agree(h1, h1_exact, rel=1.0, scale=norm_scale(x0, 0 * x0, c.g_attn, h1_exact))}
+    # Q columns (fp32) and the appended K/V rows (R2) from the GPU's normed rows
+    qkv_ref = grouped_linear(h1, c.w_qkv)
+    qkv_abs = absw(h1) @ absw(c.w_qkv).T
+    assert np.all(np.abs(q - qkv_ref[..., :HqD]) <= gamma(H) * qkv_abs[..., :HqD] + 1e-30)
+    kv = c.cache
+    pos = kv.context_lens[rows]
+    blk = kv.block_table[rows, pos // kv.k_pool.shape[2]]
+    slot = pos % kv.k_pool.shape[2]
+    for pool, lo in ((kp, HqD), (vp, HqD + Hkv * D)):
+        got = pool[blk, :, slot, :].reshape(len(rows), Hkv * D)
+        same["kv%d" % lo] = bf16_decisions_agree(got, qkv_ref[0, :, lo: lo + Hkv * D], rel=gamma(H),
+                                                 scale=qkv_abs[0, :, lo: lo + Hkv * D])
+    # R3: attention rows from the GPU's queries and the GPU's cache
+    q1 = q[0].reshape(len(rows), Hq, D)
+    q2 = q[1].reshape(len(rows), Hq, D) if F == 2 else None
+    sub = lambda t: t[rows]
+    o1, o2, _, wts = decode_attention(q1, q2, a_vec, 0, kp, vp, sub(kv.block_table), sub(ctx_after), return_weights=True)
+    o_exact = np.stack([o1] + ([o2] if F == 2 else [])).reshape(F, len(rows), HqD)
+    o_scale = np.zeros_like(o_exact)
+    G = Hq // Hkv
+    Qs = [q1] + ([q2 + widen(a_vec) * q1 if a_vec is not None else q2] if F == 2 else [])
+    for i, b in enumerate(rows):
+        n = int(ctx_after[b])
+        K = widen(gather_kv(kp, kv.block_table[rows], i, n))
+        V = widen(gather_kv(vp, kv.block_table[rows], i, n))
+        for g in range(Hkv):
+            Wt = wts[(i, g)]                                                  # [F*G][n]
+            for f in range(F):
+                for hh in range(G):
+                    h = g * G + hh
+                    sabs = np.abs(Qs[f][i, h]) @ np.abs(K[g]).T / np.sqrt(D)  # [n]
+                    ds = sabs.max() * (SPLIT + (D / 32 + 64) * U)
+                    rel = 2 * ds + 2 * SPLIT + (n / 32 + 64) * U
+                    o_scale[f, i, h * D:(h + 1) * D] = rel * (Wt[f * G + hh] @ np.abs(V[g]))
+    same["o"] = bf16_decisions_agree(o, o_exact, rel=1.0, scale=o_scale)
+    # x1 (not kept by the layer) from the GPU's attention rows, R4 from it
+    wo_abs = absw(o) @ absw(c.w_o).T
+    x1 = grouped_linear(o, c.w_o, residual=x0)
+    e1 = gamma(HqD) * wo_abs + U * np.abs(x1)
+    h2_exact = rmsnorm(x1, c.g_mlp, c.eps, rounded=False)
+    same["h2"] = bf16_decisions_agree(h2, h2_exact, rel=1.0, scale=norm_scale(x1, e1, c.g_mlp, h2_exact))
+    # R5 from the GPU's normed rows
+    gu = grouped_linear(h2, c.w_gate_up)
+    gu_err = gamma(H) * (absw(h2) @ absw(c.w_gate_up).T)
+    gate, up = gu[..., :I], gu[..., I:]
+    sig = 1.0 / (1.0 + np.exp(-gate))
+    e_int = 1.1 * gu_err[..., :I] * np.abs(up) + np.abs(gate * sig) * gu_err[..., I:] + 6 * U * np.abs(gate * sig * up)
+    if b_vec is not None:
+        e_int[1] = e_int[1] + np.abs(widen(b_vec)) * e_int[0]
+    inter_exact = swiglu_couple(gu, b_vec, rounded=False)
+    same["inter"] = bf16_decisions_agree(inter, inter_exact, rel=1.0, scale=e_int + U * np.abs(inter_exact))
+    # output rows from the GPU's SwiGLU rows
+    m_abs = absw(inter) @ absw(c.w_down).T
+    if c_vec is not None:
+        m_abs[1] = m_abs[1] + np.abs(widen(c_vec)) * m_abs[0]
+    x2 = grouped_linear(inter, c.w_down, couple=c_vec, residual=x1)
+    bound = e1 + gamma(I) * m_abs + U * np.abs(x2)
+    err = np.abs(x_out[:, rows] - x2)
+    print("chain: bf16 decisions equal to the oracle's:", {k: round(v, 5) for k, v in same.items()},
+          "| output error / bound: max %.3g" % float((err / bound).max()))
+    assert np.all(err <= bound), float((err / bound).max())
+    return x_out, kp, vp
 
 
 SMALL = dict(batch=4, context=300, hidden=512, num_q_heads=8, num_kv_heads=2, head_dim=128,
@@ -63,18 +176,31 @@ SMALL = dict(batch=4, context=300, hidden=512, num_q_heads=8, num_kv_heads=2, he
 
 def test_small_layer_parity_and_cache_diff():
     c = gen.layer_case(801, **SMALL)
-    y, kp, vp = run_layer(c)
+    y, kp, vp = check_layer_chain(c)
     want, wk, wv, mid = run_oracle(c)
-    layer_close(y, want, run_oracle(c, dtype=np.float32)[0])
+    layer_close(y, want)
     # the pool changed exactly at the primary's new slots
     changed = np.argwhere(np.any(kp != c.cache.k_pool, axis=-1))
     assert len(changed) == c.batch * c.num_kv_heads
     assert np.array_equal(np.argwhere(np.any(wk != c.cache.k_pool, axis=-1)), changed)
-    # appended rows are bf16 roundings of fp32 (GPU) and fp64 (oracle) projections: the same
-    # bits except next to a rounding midpoint, where they are one bf16 step apart
-    diff = kp != wk
-    assert diff.mean() < 1e-4
-    assert np.all(np.abs(widen(kp[diff]) - widen(wk[diff])) <= np.abs(widen(wk[diff])) * 2.0 ** -7)
+
+
+@pytest.mark.parametrize("seed", [804, 805])
+def test_layer_two_row_groups(seed):
+    # 40 sequences of two flows fill two 64-row groups of the projections (the second one
+    # partly), with head_dim 64
+    c = gen.layer_case(seed, batch=40, context=200, hidden=256, num_q_heads=4, num_kv_heads=2,
+                       head_dim=64, intermediate=512, w_std=0.05)
+    y, _, _ = check_layer_chain(c)
+    layer_close(y, run_oracle(c)[0])
+    y1, _, _ = check_layer_chain(c, flows=1)
+    assert np.array_equal(y1[0], y[0])
+
+
+def test_layer_primary_only_chain():
+    c = gen.layer_case(806, **SMALL)
+    check_layer_chain(c, flows=1)
+    check_layer_chain(c, flows=2, couple=False)
 
 
 def test_aux_never_changes_primary_or_cache():
@@ -97,11 +223,10 @@ def test_aux_equals_primary_without_coupling():
 
 def test_full_size_layer_sampled():
     c = gen.config_layer()
-    y, kp, _ = run_layer(c)
     rows = [0, 31]
-    want, wk, _, _ = run_oracle(c, batches=rows)
-    twin = run_oracle(c, batches=rows, dtype=np.float32)[0]
-    layer_close(y[:, rows], want[:, rows], twin[:, rows])
+    y, kp, _ = check_layer_chain(c, rows=rows)
+    want = run_oracle(c, batches=rows)[0]
+    layer_close(y[:, rows], want[:, rows])
     assert np.all(np.isfinite(y))
     changed = np.argwhere(np.any(kp != c.cache.k_pool, axis=-1))
     assert len(changed) == c.batch * c.num_kv_heads
