@@ -34,6 +34,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 constexpr int kChunkQuantum = 128;  // tokens: 4 waves x 32-token tiles
 constexpr int kMinChunk = 1024;   // tokens: shorter splits cost more in merge than they gain
 constexpr int kMaxChunk = 8192;   // tokens: longer splits leave CUs idle when lengths differ
+                                  // (doubled for small batches, see attn_plan)
 // Launch-shape defaults (compile-time so that alternatives can be measured).
 #ifndef DFX_ATTN_TARGET
 #define DFX_ATTN_TARGET 256
@@ -79,17 +80,23 @@ constexpr int kMaxChunkBlocks = 1024;
 void attn_plan(int batch, int hkv, int max_ctx, int requested, int block_size, int *splits,
                int *chunk) {
   const int max_s = max_ctx > 0 ? (max_ctx + kChunkQuantum - 1) / kChunkQuantum : 1;
-  const int64_t cap = block_size > 0
-      ? ((int64_t)(kMaxChunkBlocks - 1) * block_size) / kChunkQuantum * kChunkQuantum
-      : (int64_t)1 << 30;
+  // Splits start at multiples of kChunkQuantum, so with blocks of at most that many tokens
+  // a split covers whole blocks and may span all kMaxChunkBlocks of them.
+  const int64_t cap = block_size <= 0 ? (int64_t)1 << 30
+      : block_size <= kChunkQuantum ? (int64_t)kMaxChunkBlocks * block_size
+      : ((int64_t)(kMaxChunkBlocks - 1) * block_size) / kChunkQuantum * kChunkQuantum;
   int s;
   if (requested > 0) {
     s = requested < max_s ? requested : max_s;
   } else {
-    // enough work-groups to fill the CUs, and no split longer than kMaxChunk
+    // Enough work-groups to fill the CUs, and no split longer than kMaxChunk when the
+    // batch alone fills them (large batches are where context lengths differ, and shorter
+    // splits balance the load); small batches with long contexts take twice that, since
+    // there every split is full and fewer, longer ones stream better.
     const int pairs = batch * hkv > 0 ? batch * hkv : 1;
     s = (kTargetAttnGroups + pairs - 1) / pairs;
-    const int by_max = (max_ctx + kMaxChunk - 1) / kMaxChunk;
+    const int max_chunk = pairs >= kTargetAttnGroups ? kMaxChunk : 2 * kMaxChunk;
+    const int by_max = (max_ctx + max_chunk - 1) / max_chunk;
     if (s < by_max) s = by_max;
     const int by_min = max_ctx > kMinChunk ? (max_ctx + kMinChunk - 1) / kMinChunk : 1;
     if (s > by_min) s = by_min;

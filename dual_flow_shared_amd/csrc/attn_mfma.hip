@@ -104,6 +104,17 @@ __device__ __forceinline__ void half_bases(const AttnArgs &p, const int32_t *tbl
   }
 }
 
+#ifndef DFX_ATTN_NT
+#define DFX_ATTN_NT 1
+#endif
+// K/V loads: non-temporal by default (each line is read once per call, and the hint keeps
+// the stream from displacing the rest of L2); 0 gives plain loads for comparison.
+template <typename T>
+__device__ __forceinline__ T kv_load(const uint16_t *p) {
+  if constexpr (DFX_ATTN_NT) return __builtin_nontemporal_load((const T *)p);
+  else return *(const T *)p;
+}
+
 // Issue the K (resp. V) loads of the tile described by (hb, lastx).
 template <int D>
 __device__ __forceinline__ void load_k(const uint16_t *kp, const int64_t *hb, const int *lastx,
@@ -113,7 +124,7 @@ __device__ __forceinline__ void load_k(const uint16_t *kp, const int64_t *hb, co
   for (int mb = 0; mb < 2; ++mb) {
     const uint16_t *row = kp + hb[mb] + (int64_t)min(n, lastx[mb]) * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) r.kf[mb][s] = *(const u32x4 *)(row + 8 * (4 * s + j));
+    for (int s = 0; s < KS; ++s) r.kf[mb][s] = kv_load<u32x4>(row + 8 * (4 * s + j));
   }
 }
 
@@ -126,10 +137,10 @@ __device__ __forceinline__ void load_v(const uint16_t *vp, const int64_t *hb, co
     const int h = v >> 2, x = 4 * j + (v & 3);  // token tau(j, v) = t0 + 16 h + x
     const uint16_t *src = vp + hb[h] + (int64_t)min(x, lastx[h]) * D + VEC * n;
     if constexpr (VEC == 8) {
-      const u32x4 y = *(const u32x4 *)src;
+      const u32x4 y = kv_load<u32x4>(src);
       r.vr[v][0] = y[0]; r.vr[v][1] = y[1]; r.vr[v][2] = y[2]; r.vr[v][3] = y[3];
     } else {
-      const u32x2 y = *(const u32x2 *)src;
+      const u32x2 y = kv_load<u32x2>(src);
       r.vr[v][0] = y[0]; r.vr[v][1] = y[1];
     }
   }
@@ -212,7 +223,7 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs p) {
   __shared__ float s_m[4][16], s_l[4][16];
   __shared__ int32_t s_tbl[kMaxChunkBlocks];
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
   const int ctx = min(max(p.ctx[b], 0), p.max_context);
@@ -327,7 +338,10 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs p) {
 }
 
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s) {
-  const dim3 grid(a.num_splits, a.num_kv_heads, a.batch), block(256);
+  // The hardware hands work-group i to XCD i % 8. With the KV head fastest, XCD k serves
+  // head k of every sequence (an equal share whatever the context lengths), and each XCD
+  // dispatches all first splits (the longest pieces of ragged batches) before the later ones.
+  const dim3 grid(a.num_kv_heads, a.batch, a.num_splits), block(256);
   const bool paged = a.block_shift >= 0;
 #define DFX_ATTN_LAUNCH(D, QB, PG) attn_mfma_kernel<D, QB, PG><<<grid, block, 0, s>>>(a)
   if (a.head_dim == 128) {

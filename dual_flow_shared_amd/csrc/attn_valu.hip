@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs p) {
   __shared__ float p_s[kMaxR][kT];
   __shared__ float m_s[kMaxR], l_s[kMaxR], a_s[kMaxR];
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ctx = min(max(p.ctx[b], 0), p.max_context);
   const int start = split * p.chunk;
@@ -142,7 +142,10 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs p) {
 
 hipError_t launch_attn_valu(const AttnArgs &a, hipStream_t s) {
   if (a.head_dim > kMaxD || a.n_flows * a.group > kMaxR) return hipErrorInvalidValue;
-  const dim3 grid(a.num_splits, a.num_kv_heads, a.batch), block(256);
+  // The hardware hands work-group i to XCD i % 8. With the KV head fastest, XCD k serves
+  // head k of every sequence (an equal share whatever the context lengths), and each XCD
+  // dispatches all first splits (the longest pieces of ragged batches) before the later ones.
+  const dim3 grid(a.num_kv_heads, a.batch, a.num_splits), block(256);
   if (a.kv_bf16) {
     if (a.q_bf16) attn_valu_kernel<true, true><<<grid, block, 0, s>>>(a);
     else attn_valu_kernel<true, false><<<grid, block, 0, s>>>(a);

@@ -78,15 +78,26 @@ def test_plan_is_host_arithmetic():
     k = kv(mb=8192, nb=65536)
     assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 0, ctypes.byref(s), ctypes.byref(n)) == 0
     assert s.value > 1 and n.value >= s.value * 2 * 8 * 64 * 129 * 4
-    # a paged split holds at most 1023 blocks (its block ids sit in LDS): one requested
-    # split over 131072 tokens of 16-token blocks becomes ceil(131072 / 16256) = 9
+    # a paged split holds at most 1024 blocks (its block ids sit in LDS): one requested
+    # split over 131072 tokens of 16-token blocks becomes 131072 / 16384 = 8
     assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 1, ctypes.byref(s), ctypes.byref(n)) == 0
-    assert s.value == 9 and n.value > 0
+    assert s.value == 8 and n.value > 0
+    # the default for this small batch: 64 (sequence, KV head) pairs, splits of 16384 tokens
+    assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 0, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value == 8
+    # a large batch (512 pairs) keeps splits of at most 8192 tokens
+    assert lib.dfx_decode_attn_plan(ctypes.byref(k), 64, 32, 2, 16384, 0, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value == 2
+    # blocks longer than the 128-token split quantum: a split may start inside a block, so
+    # it spans at most 1023 whole blocks plus the partial first one
+    kb = kv(bs=256, mb=1024, nb=4096)
+    assert lib.dfx_decode_attn_plan(ctypes.byref(kb), 1, 8, 1, 262144, 1, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value == -(-262144 // (1023 * 256 // 128 * 128))
     kc = kv(table=None, bs=131072, nb=8)
     assert lib.dfx_decode_attn_plan(ctypes.byref(kc), 8, 64, 2, 131072, 1, ctypes.byref(s), ctypes.byref(n)) == 0
     assert s.value == 1 and n.value == 0
     assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 7, ctypes.byref(s), ctypes.byref(n)) == 0
-    assert s.value == 9          # raised to respect the 1023-block split limit
+    assert s.value == 8          # raised to respect the 1024-block split limit
     assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 20, ctypes.byref(s), ctypes.byref(n)) == 0
     assert s.value == 20
     # the plan does not depend on the number of flows (primary results stay bit-identical)
