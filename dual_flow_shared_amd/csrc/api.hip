@@ -175,6 +175,18 @@ dfx_status run_linear_parts(int32_t n_flows, int32_t rows, int32_t K, int32_t N,
   return hip_status(launch_grouped_linear(a, s), "grouped_linear launch");
 }
 
+// Gate/up projection fused with SwiGLU and the b coupling (one split, no tiles): bf16 rows of
+// the intermediate, in the down projection's fragment order, straight from the accumulators.
+dfx_status run_gate_up_swiglu(int32_t n_flows, int32_t rows, int32_t H, int32_t I, const void *x_packed,
+                              const uint16_t *w_packed, const float *b, uint16_t *inter, hipStream_t s) {
+  if (rows == 0) return DFX_OK;
+  GemmArgs a{};
+  a.n_flows = n_flows; a.rows = rows; a.K = H; a.N = 2 * I;
+  a.x_packed = 1; a.x = x_packed; a.w = w_packed; a.w_packed = 1; a.y = inter;
+  a.couple = n_flows == 2 ? b : nullptr; a.ksplit = 1; a.kper = H / 32; a.swiglu = 1;
+  return hip_status(launch_grouped_linear(a, s), "gate/up launch");
+}
+
 dfx_status run_linear(int32_t n_flows, int32_t rows, int32_t K, int32_t N, int x_f32, const void *x,
                       const uint16_t *w, int w_packed, int y_bf16, void *y, const float *couple,
                       const float *residual, void *ws, size_t ws_bytes, hipStream_t s) {
@@ -443,9 +455,9 @@ dfx_status layer_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_
   int chunk;
   attn_plan(B, kv->num_kv_heads, max_context, 0, paged_bs(kv), &p.splits, &chunk);
   p.attn_ws = a256(attn_ws_bytes(p.splits, F, B, Hq, D));
-  // every projection writes its fp32 tiles [ksplit][groups][64][N]; they run in stream
-  // order, so one region serves all four
-  const int shapes[4][2] = {{H, Nqkv}, {Hq * D, H}, {H, 2 * I}, {I, H}};
+  // the projections followed by a finish kernel write their fp32 tiles
+  // [ksplit][groups][64][N]; they run in stream order, so one region serves them all
+  const int shapes[3][2] = {{H, Nqkv}, {Hq * D, H}, {I, H}};  // the gate/up pass writes no tiles
   for (auto &sh : shapes) {
     const GemmPlan g = gemm_plan(F, B, sh[0], sh[1]);
     const size_t t = (size_t)g.ksplit * g.groups * 64 * sh[1] * sizeof(float);
@@ -519,9 +531,7 @@ dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_c
   if ((r = hip_status(launch_layer_glue(kGlueONorm, g, s), "o finish launch"))) return r;
   // MLP: shared gate/up projection, SwiGLU with b coupling, shared down projection with
   // c coupling and the residual
-  if ((r = run_linear_parts(F, B, H, 2 * I, 2, h2, w->w_gate_up, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
-  g.N = 2 * I; g.ksplit = ksplit(H, 2 * I); g.couple = F == 2 ? w->couple_b : nullptr; g.h = inter;
-  if ((r = hip_status(launch_layer_glue(kGlueSwiglu, g, s), "swiglu finish launch"))) return r;
+  if ((r = run_gate_up_swiglu(F, B, H, I, h2, w->w_gate_up, w->couple_b, inter, s))) return r;
   if ((r = run_linear_parts(F, B, I, H, 2, inter, w->w_down, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
   g.N = H; g.ksplit = ksplit(I, H); g.couple = F == 2 ? w->couple_c : nullptr;
   return hip_status(launch_layer_glue(kGlueDown, g, s), "down finish launch");

@@ -47,6 +47,9 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// silu(g) = g * sigmoid(g), the gate of SwiGLU
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
 // Element offset of row r of flow f, column k, in the fragment-ordered activations that the
 // grouped linear reads directly: [groups][K/32][4 blocks][64 lanes][8]. Row group r / (64/F)
 // holds row q = f (64/F) + r % (64/F); lane (q % 16) + 16 ((k % 32) / 8) of block q / 16
@@ -95,6 +98,10 @@ struct GemmArgs {
   int32_t kper;        // k-steps of 32 per split (the last split may have fewer)
   float *partial;      // [ksplit][groups][64 rows][N] fp32 when ksplit > 1 or tiles_only
   int32_t tiles_only;  // write the fp32 tiles even for one split (a finish kernel follows)
+  // gate/up mode (one split): N = 2 I with the gate rows of W first; a wave pairs gate
+  // features c.. c+15 with up features I + c..; y receives bf16 silu(gate) * up, flow 1
+  // plus couple * flow 0, in the fragment order of xpack_offset with K = I
+  int32_t swiglu;
 };
 
 // Destination of attention output (flow f, sequence b, column c = head * D + d): rows
@@ -111,7 +118,7 @@ __device__ __forceinline__ float *attn_out(const AttnArgs &p, int f, int b, int 
 }
 
 // Arguments of the kernels that finish a projection of the decode layer.
-enum { kGlueQkv = 0, kGlueONorm = 1, kGlueSwiglu = 2, kGlueDown = 3 };
+enum { kGlueQkv = 0, kGlueONorm = 1, kGlueDown = 3 };
 struct LayerGlueArgs {
   int32_t n_flows, batch, N, ksplit;
   const float *tiles;  // [ksplit][groups][64][N]
@@ -120,7 +127,7 @@ struct LayerGlueArgs {
   uint16_t *h;         // bf16 rows for the next projection (fragment order, xpack_offset)
   const float *gain;   // RMSNorm gain
   float eps;
-  const float *couple; // b (SwiGLU) or c (down) coupling vector, or NULL
+  const float *couple; // c coupling vector of the down projection, or NULL
   dfx_kv_cache kv;     // cache written by the Q/K/V finish (primary rows only)
   const int32_t *ctx;  // context lengths after the step (append position = ctx - 1)
   int32_t num_q_heads, head_dim;

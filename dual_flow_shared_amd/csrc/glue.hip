@@ -42,8 +42,6 @@ hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float
   return hipGetLastError();
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
-
 // One thread per 4 intermediate elements of one row index, covering both flows.
 __global__ void __launch_bounds__(256) swiglu_kernel(int32_t n_flows, int32_t rows, int32_t dim,
                                                      const float *gu, const float *bvec,

@@ -98,8 +98,12 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
   const int nks = K / 32, ng = N / 16;
   const int kbeg = ks * p.kper;
   const int nk = min(p.kper, nks - kbeg);  // >= 1: the plan leaves no split empty
-  const int cg = 2 * (tile * 4 + wave);    // this wave's column groups cg, cg + 1 (16 each)
-  const int cga = min(cg, ng - 1), cgb = min(cg + 1, ng - 1);  // a dead group streams a live one
+  // this wave's two 16-feature groups: cg and cg + 1, or in gate/up mode gate group cg and
+  // the matching up group cg + ngh (a dead group streams a live one and stores nothing)
+  const int ngh = ng / 2;
+  const int cg = p.swiglu ? tile * 4 + wave : 2 * (tile * 4 + wave);
+  const int cga = p.swiglu ? min(cg, ngh - 1) : min(cg, ng - 1);
+  const int cgb = p.swiglu ? cga + ngh : min(cg + 1, ng - 1);
   // weight fragments of k-step kk of this split: wa + kk * wstep and wb + kk * wstep
   const uint16_t *wa, *wb;
   int64_t wstep;
@@ -179,7 +183,32 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
     }
     __syncthreads();  // the staging slots are reused by the next row group
 
-    // C layout: lane holds row q = 16 nb + n and features 16 (cg + h) + 4 j + i
+    // C layout: lane holds row q = 16 nb + n and features 16 (cg + h) + 4 j + i (gate/up
+    // mode: gate feature 16 cg + 4 j + i in acc[0], its up feature in acc[1])
+    if (p.swiglu) {
+      if (cg >= ngh) continue;
+      const int I = N / 2, col = 16 * cg + 4 * j;
+      f32x4 inter[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) inter[nb][i] = silu(acc[0][nb][i]) * acc[1][nb][i];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int q = 16 * nb + n, f = q / rpg, rr = grp * rpg + q % rpg;
+        if (f >= F || rr >= rows) continue;
+        f32x4 v = inter[nb];
+        if (f == 1 && p.couple) {
+          // the flow-0 partner row q - 32 is block nb - 2 in this same lane
+          const f32x4 c = *(const f32x4 *)(p.couple + col), pr = inter[nb >= 2 ? nb - 2 : 0];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = fmaf(c[i], pr[i], v[i]);
+        }
+        *(u32x2 *)((uint16_t *)p.y + xpack_offset(F, f, rr, col, I)) =
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+      continue;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (cg + h >= ng) continue;
@@ -240,7 +269,7 @@ __global__ void __launch_bounds__(256) grouped_linear_reduce_kernel(GemmArgs p) 
 }
 
 hipError_t launch_grouped_linear(const GemmArgs &g, hipStream_t s) {
-  const dim3 grid((g.N + 127) / 128, g.ksplit), block(256);
+  const dim3 grid(g.swiglu ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128, g.ksplit), block(256);
 #define DFX_GL(XF, XP, WP) grouped_linear_kernel<XF, XP, WP><<<grid, block, 0, s>>>(g)
   if (g.x_packed) {
     if (g.w_packed) DFX_GL(false, true, true); else DFX_GL(false, true, false);
@@ -251,7 +280,7 @@ hipError_t launch_grouped_linear(const GemmArgs &g, hipStream_t s) {
   }
 #undef DFX_GL
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || g.ksplit == 1 || g.tiles_only) return e;
+  if (e != hipSuccess || g.ksplit == 1 || g.tiles_only || g.swiglu) return e;
   const int rpg = 64 / g.n_flows;
   const int groups = (g.rows + rpg - 1) / rpg;
   const int64_t threads = (int64_t)groups * rpg * (g.N / 4);

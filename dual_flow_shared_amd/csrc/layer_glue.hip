@@ -1,4 +1,5 @@
-// Layer-internal kernels that finish each grouped projection of the decode layer: they
+// Layer-internal kernels that finish the K-split projections of the decode layer (Q/K/V,
+// output, down; the gate/up projection finishes in its own epilogue): they
 // sum the K-split fp32 tiles of the projection in split order and apply the glue that
 // follows it, so no separate reduction pass, norm or activation pass touches HBM.
 //
@@ -88,33 +89,6 @@ __global__ void __launch_bounds__(1024) o_finish_norm_kernel(LayerGlueArgs a) {
   }
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
-
-// inter = silu(gate) * up from the summed gate/up tiles; flow 1 += b * flow 0; bf16 out in
-// the fragment order of the down projection (xpack_offset). One thread per 4 intermediate
-// columns of one row index (both flows).
-__global__ void __launch_bounds__(256) gu_finish_swiglu_kernel(LayerGlueArgs a) {
-  const int F = a.n_flows, B = a.batch, N = a.N, I = N / 2;
-  const int rpg = 64 / F, groups = (B + rpg - 1) / rpg;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int i4 = I / 4;
-  if (idx >= (int64_t)B * i4) return;
-  const int col = (int)(idx % i4) * 4, b = (int)(idx / i4);
-  f32x4 prim;
-  for (int f = 0; f < F; ++f) {
-    const f32x4 g = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, col);
-    const f32x4 u = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, I + col);
-    f32x4 v{silu_f(g[0]) * u[0], silu_f(g[1]) * u[1], silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]};
-    if (f == 0) prim = v;
-    else if (a.couple) {
-      const f32x4 c = *(const f32x4 *)(a.couple + col);
-      v = f32x4{fmaf(c[0], prim[0], v[0]), fmaf(c[1], prim[1], v[1]), fmaf(c[2], prim[2], v[2]),
-                fmaf(c[3], prim[3], v[3])};
-    }
-    *(u32x2 *)(a.h + xpack_offset(F, f, b, col, I)) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-  }
-}
-
 // m = summed W_down tiles; flow 1 += c * flow 0; x += m (in place). One thread per 4
 // columns of one row index (both flows).
 __global__ void __launch_bounds__(256) down_finish_kernel(LayerGlueArgs a) {
@@ -148,10 +122,6 @@ hipError_t launch_layer_glue(int which, const LayerGlueArgs &a, hipStream_t s) {
       break;
     case kGlueONorm:
       o_finish_norm_kernel<<<F * B, 1024, 0, s>>>(a);
-      break;
-    case kGlueSwiglu:
-      threads = (int64_t)B * (a.N / 8);
-      gu_finish_swiglu_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a);
       break;
     default:
       threads = (int64_t)B * (a.N / 4);
