@@ -76,6 +76,27 @@ def test_split_counts(splits):
     check(case, run_attn(case, num_splits=splits), oracle(case))
 
 
+def test_shared_workspace_across_shapes_and_splits():
+    """One workspace serves calls of changing shape and split count: each result equals a
+    fresh workspace's bit for bit (split partials are fully written before they are read)."""
+    import dual_flow_shared_amd as dfx
+    ws = dfx.Workspace()
+    cases = [(gen.attention_case(611, 3, 32, 8, 128, [4096, 1500, 3001], dtype="bf16", paged=True), 7),
+             (gen.attention_case(612, 9, 16, 8, 64, [700] * 9, dtype="bf16", paged=True), 2),
+             (gen.attention_case(613, 2, 32, 4, 128, [2500, 600], dtype="bf16"), 5),
+             (gen.attention_case(611, 3, 32, 8, 128, [4096, 1500, 3001], dtype="bf16", paged=True), 3)]
+    for _ in range(2):
+        for case, splits in cases:
+            cache, ctx = cache_of(case), dev(case.context_lens)
+            args = (dev(case.q1), dev(case.q2), dev(case.a))
+            kw = dict(cache=cache, context_lens=ctx, max_context=int(case.context_lens.max()), num_splits=splits)
+            got = dfx.decode_attn(*args, workspace=ws, **kw)
+            fresh = dfx.decode_attn(*args, workspace=dfx.Workspace(), **kw)
+            torch.cuda.synchronize()
+            for g, f in zip(got, fresh):
+                assert torch.equal(g, f)
+
+
 def test_contiguous_batch16_context4096():
     case = gen.config_attention(2)
     check(case, run_attn(case), oracle(case))
