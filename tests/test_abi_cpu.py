@@ -85,9 +85,12 @@ def test_plan_is_host_arithmetic():
     # the default for this small batch: 64 (sequence, KV head) pairs, splits of 16384 tokens
     assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 0, ctypes.byref(s), ctypes.byref(n)) == 0
     assert s.value == 8
-    # a large batch (512 pairs) keeps splits of at most 8192 tokens
-    assert lib.dfx_decode_attn_plan(ctypes.byref(k), 64, 32, 2, 16384, 0, ctypes.byref(s), ctypes.byref(n)) == 0
+    # one (sequence, KV head) pair per CU (256 pairs): splits of at most 8192 tokens
+    assert lib.dfx_decode_attn_plan(ctypes.byref(k), 32, 32, 2, 16384, 0, ctypes.byref(s), ctypes.byref(n)) == 0
     assert s.value == 2
+    # two or more pairs per CU (512): splits of at most 3072 tokens, 16384 / 2816 -> 6
+    assert lib.dfx_decode_attn_plan(ctypes.byref(k), 64, 32, 2, 16384, 0, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value == 6
     # blocks longer than the 128-token split quantum: a split may start inside a block, so
     # it spans at most 1023 whole blocks plus the partial first one
     kb = kv(bs=256, mb=1024, nb=4096)
