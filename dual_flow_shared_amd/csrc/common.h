@@ -61,6 +61,28 @@ __device__ __forceinline__ int64_t xpack_offset(int F, int f, int r, int k, int 
          (k & 7);
 }
 
+// Sum of the K-split fp32 tiles [ksplit][groups][64 rows][N] at one (group, row q, col),
+// added in split order. The loads of each group of 8 splits are all issued before the first
+// add (indices past the last split re-read it and are not added), so the sum costs one
+// memory round trip per 8 splits instead of one per split.
+__device__ __forceinline__ f32x4 sum_split_tiles(const float *tiles, int ksplit, int groups, int N,
+                                                 int grp, int q, int col) {
+  constexpr int U = 8;
+  f32x4 s{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < ksplit; k0 += U) {
+    f32x4 t[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = min(k0 + u, ksplit - 1);
+      t[u] = *(const f32x4 *)(tiles + (((int64_t)k * groups + grp) * 64 + q) * N + col);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (k0 + u < ksplit) s += t[u];
+  }
+  return s;
+}
+
 // ---- launch-time parameter blocks --------------------------------------------------
 
 struct AttnArgs {

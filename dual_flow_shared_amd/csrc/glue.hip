@@ -4,31 +4,42 @@
 
 namespace dfx {
 
-// One work-group of 1024 threads per row; each thread owns float4 slices of the row.
+// One work-group of 1024 threads per row; thread t owns float4 slices t, t + 1024, ... of the
+// row (at most 4: dim <= 16384), held in registers, and its gain slices are loaded up front,
+// so the kernel makes one round trip to memory before the reduction.
 // packed_flows > 0: row r = f * batch + b is written in the fragment order of xpack_offset.
 __global__ void __launch_bounds__(1024) rmsnorm_kernel(int32_t dim, const float *x,
                                                        const float *gain, float eps, uint16_t *y,
                                                        int packed_flows, int batch) {
+  constexpr int PT = 4;
   __shared__ float red[16];
   const int64_t row = blockIdx.x;
   const f32x4 *xr = (const f32x4 *)(x + row * dim);
+  const f32x4 *g4 = (const f32x4 *)gain;
   const int n4 = dim / 4;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < n4; i += 1024) {
-    const f32x4 v = xr[i];
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  f32x4 v[PT], gg[PT];
+#pragma unroll
+  for (int t = 0; t < PT; ++t) {
+    const int i = threadIdx.x + 1024 * t;
+    v[t] = i < n4 ? xr[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    gg[t] = i < n4 ? g4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  float ss = 0.f;
+#pragma unroll
+  for (int t = 0; t < PT; ++t) ss += v[t][0] * v[t][0] + v[t][1] * v[t][1] + v[t][2] * v[t][2] + v[t][3] * v[t][3];
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   float tot = 0.f;
   for (int w = 0; w < 16; ++w) tot += red[w];
   const float r = 1.0f / sqrtf(tot / (float)dim + eps);
-  const f32x4 *g4 = (const f32x4 *)gain;
   const int f = packed_flows ? (int)(row / batch) : 0, b = packed_flows ? (int)(row % batch) : 0;
-  for (int i = threadIdx.x; i < n4; i += 1024) {
-    const f32x4 v = xr[i], gg = g4[i];
-    const u32x2 o{pack_bf16x2(v[0] * r * gg[0], v[1] * r * gg[1]), pack_bf16x2(v[2] * r * gg[2], v[3] * r * gg[3])};
+#pragma unroll
+  for (int t = 0; t < PT; ++t) {
+    const int i = threadIdx.x + 1024 * t;
+    if (i >= n4) continue;
+    const u32x2 o{pack_bf16x2(v[t][0] * r * gg[t][0], v[t][1] * r * gg[t][1]),
+                  pack_bf16x2(v[t][2] * r * gg[t][2], v[t][3] * r * gg[t][3])};
     const int64_t at = packed_flows ? xpack_offset(packed_flows, f, b, 4 * i, dim) : row * dim + 4 * i;
     *(u32x2 *)(y + at) = o;
   }

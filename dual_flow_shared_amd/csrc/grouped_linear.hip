@@ -256,10 +256,7 @@ __global__ void __launch_bounds__(256) grouped_linear_reduce_kernel(GemmArgs p) 
   // rows q = qr (flow 0) and q = qr + 32 (flow 1) of this group, summed in split order
   float v[2][4];
   for (int f = 0; f < F; ++f) {
-    const int q = f * rpg + qr;
-    f32x4 s{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < p.ksplit; ++k)
-      s += *(const f32x4 *)(p.partial + (((int64_t)k * groups + grp) * 64 + q) * N + col);
+    const f32x4 s = sum_split_tiles(p.partial, p.ksplit, groups, N, grp, f * rpg + qr, col);
     v[f][0] = s[0]; v[f][1] = s[1]; v[f][2] = s[2]; v[f][3] = s[3];
   }
   for (int f = 0; f < F; ++f) {

@@ -11,11 +11,7 @@ namespace dfx {
 
 __device__ __forceinline__ f32x4 sum_tiles(const float *tiles, int ksplit, int groups, int N,
                                            int f, int rr, int rpg, int col) {
-  const int grp = rr / rpg, q = f * rpg + rr % rpg;
-  f32x4 s{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < ksplit; ++k)
-    s += *(const f32x4 *)(tiles + (((int64_t)k * groups + grp) * 64 + q) * N + col);
-  return s;
+  return sum_split_tiles(tiles, ksplit, groups, N, rr / rpg, f * rpg + rr % rpg, col);
 }
 
 // Q columns of both flows -> qkv rows (fp32); K and V columns of flow 0 -> the cache at
@@ -63,18 +59,32 @@ __global__ void __launch_bounds__(256) qkv_finish_kernel(LayerGlueArgs a) {
 
 // x += sum of the W_o tiles (in place), then h = bf16(rmsnorm(x) * gain) in the fragment
 // order of the next projection (xpack_offset). One work-group of 1024 threads per
-// (flow, row); each thread owns 4-column slices as float4.
+// (flow, row); thread t owns float4 slices t, t + 1024, ... (at most 4: N <= 16384), held in
+// registers, and every load (tiles, residual, gain) is issued before the reduction.
 __global__ void __launch_bounds__(1024) o_finish_norm_kernel(LayerGlueArgs a) {
+  constexpr int PT = 4;
   __shared__ float red[16];
   const int F = a.n_flows, B = a.batch, N = a.N;
   const int rpg = 64 / F, groups = (B + rpg - 1) / rpg;
   const int row = blockIdx.x, f = row / B, b = row % B;
   float *xr = a.x + (int64_t)row * N;
+  const int n4 = N / 4;
+  f32x4 v[PT], gg[PT];
+#pragma unroll
+  for (int t = 0; t < PT; ++t) {
+    const int i = threadIdx.x + 1024 * t;
+    v[t] = gg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i < n4) {
+      v[t] = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, 4 * i) + *(const f32x4 *)(xr + 4 * i);
+      gg[t] = *(const f32x4 *)(a.gain + 4 * i);
+    }
+  }
   float ss = 0.f;
-  for (int col = 4 * threadIdx.x; col < N; col += 4096) {
-    f32x4 v = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, col) + *(const f32x4 *)(xr + col);
-    *(f32x4 *)(xr + col) = v;
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+#pragma unroll
+  for (int t = 0; t < PT; ++t) {
+    const int i = threadIdx.x + 1024 * t;
+    if (i < n4) *(f32x4 *)(xr + 4 * i) = v[t];
+    ss += v[t][0] * v[t][0] + v[t][1] * v[t][1] + v[t][2] * v[t][2] + v[t][3] * v[t][3];
   }
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -82,10 +92,13 @@ __global__ void __launch_bounds__(1024) o_finish_norm_kernel(LayerGlueArgs a) {
   float tot = 0.f;
   for (int w = 0; w < 16; ++w) tot += red[w];
   const float r = 1.0f / sqrtf(tot / (float)N + a.eps);
-  for (int col = 4 * threadIdx.x; col < N; col += 4096) {
-    const f32x4 v = *(const f32x4 *)(xr + col), g = *(const f32x4 *)(a.gain + col);
-    *(u32x2 *)(a.h + xpack_offset(F, f, b, col, N)) =
-        u32x2{pack_bf16x2(v[0] * r * g[0], v[1] * r * g[1]), pack_bf16x2(v[2] * r * g[2], v[3] * r * g[3])};
+#pragma unroll
+  for (int t = 0; t < PT; ++t) {
+    const int i = threadIdx.x + 1024 * t;
+    if (i >= n4) continue;
+    *(u32x2 *)(a.h + xpack_offset(F, f, b, 4 * i, N)) =
+        u32x2{pack_bf16x2(v[t][0] * r * gg[t][0], v[t][1] * r * gg[t][1]),
+              pack_bf16x2(v[t][2] * r * gg[t][2], v[t][3] * r * gg[t][3])};
   }
 }
 

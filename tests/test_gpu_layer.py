@@ -197,6 +197,16 @@ def test_layer_two_row_groups(seed):
     assert np.array_equal(y1[0], y[0])
 
 
+@pytest.mark.parametrize("heads,block", [((32, 2), 16), ((8, 2), 8)])
+def test_layer_vector_attention_path(heads, block):
+    # 32 query rows per KV head (both flows, GQA 16), or 8-token blocks: the attention runs on
+    # the vector path
+    c = gen.layer_case(807, batch=3, context=100, hidden=256, num_q_heads=heads[0], num_kv_heads=heads[1],
+                       head_dim=64, intermediate=256, block_size=block, w_std=0.05)
+    y, _, _ = check_layer_chain(c)
+    layer_close(y, run_oracle(c)[0])
+
+
 def test_layer_primary_only_chain():
     c = gen.layer_case(806, **SMALL)
     check_layer_chain(c, flows=1)
