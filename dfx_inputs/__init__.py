@@ -27,6 +27,7 @@ TID_Q1, TID_Q2, TID_A, TID_K, TID_V, TID_CTX, TID_PERM = 1, 2, 3, 4, 5, 6, 7
 TID_X1, TID_X2, TID_WQKV, TID_WO, TID_WGU, TID_WD = 11, 12, 13, 14, 15, 16
 TID_G1, TID_G2, TID_B, TID_C = 17, 18, 19, 20
 TID_LIN_X, TID_LIN_W, TID_LIN_CPL, TID_LIN_RES = 21, 22, 23, 24
+TID_TOK, TID_E1, TID_E2 = 31, 32, 33
 
 
 def stream(seed: int, tid: int, *idx: int) -> np.random.Generator:
@@ -281,6 +282,31 @@ def layer_case(seed: int, batch: int, context: int, hidden: int, num_q_heads: in
 
 
 # ------------------------------------------------------------- named workloads
+
+@dataclass
+class StepCase:
+    """A stack of dual-flow layers with their own caches, both flows' token embedding tables and
+    the token ids at the generated position."""
+    seed: int
+    tokens: np.ndarray          # int32 [B]
+    embed_primary: np.ndarray   # uint16 [vocab][hidden]
+    embed_aux: np.ndarray       # uint16 [vocab][hidden]: the auxiliary flow's own table
+    layers: list                # LayerCase per layer (its residual rows x are unused)
+
+
+def step_case(seed: int, n_layers: int, vocab: int, batch: int, context: int, hidden: int,
+              num_q_heads: int, num_kv_heads: int, head_dim: int, intermediate: int,
+              w_std: float = 0.02, couple: bool = True, workers: Optional[int] = None) -> StepCase:
+    """Layer l is layer_case(seed * 1000 + l, ...) (its own weights and cache, the same context
+    lengths); embeddings ~ N(0, 1) bf16; tokens uniform in [0, vocab)."""
+    tokens = stream(seed, TID_TOK).integers(0, vocab, size=batch).astype(np.int32)
+    e1 = f32_to_bf16_bits(_normal(seed, TID_E1, (), (vocab, hidden)))
+    e2 = f32_to_bf16_bits(_normal(seed, TID_E2, (), (vocab, hidden)))
+    layers = [layer_case(seed * 1000 + l, batch=batch, context=context, hidden=hidden, num_q_heads=num_q_heads,
+                         num_kv_heads=num_kv_heads, head_dim=head_dim, intermediate=intermediate,
+                         w_std=w_std, couple=couple, workers=workers) for l in range(n_layers)]
+    return StepCase(seed, tokens, e1, e2, layers)
+
 
 def config_attention(idx: int, workers: Optional[int] = None, **over) -> AttnCase:
     """The four attention workloads (seed 101 * idx)."""

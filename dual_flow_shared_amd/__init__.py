@@ -18,7 +18,7 @@ from ._abi import (DFX_BF16, DFX_F32, DFX_W_PACKED, DFX_W_ROW_MAJOR, DfxError, K
 __all__ = ["DfxError", "KVCache", "LayerWeights", "decode_attn", "decode_attn_plan",
            "kv_append_primary", "grouped_linear", "pack_weight", "rmsnorm", "swiglu_couple",
            "dual_flow_decode_layer", "layer_workspace_size", "copy_bytes", "read_bytes", "fill_bytes",
-           "layer_taps", "Workspace", "version"]
+           "layer_taps", "dual_flow_decode_step", "step_workspace_size", "Workspace", "version"]
 
 
 def version() -> int:
@@ -293,6 +293,44 @@ def dual_flow_decode_layer(x: torch.Tensor, weights: LayerWeights, cache: KVCach
     ws = _workspace(workspace, x.device, "layer").get(need)
     check(lib().dfx_dual_flow_decode_layer(ctypes.byref(w), ctypes.byref(c), _ptr(context_lens), B,
                                            max_context, F, _ptr(x), _ptr(ws), need, _stream(stream)))
+    return x
+
+
+def _structs(layers, caches):
+    if len(layers) != len(caches) or not layers:
+        raise ValueError("one cache per layer, at least one layer")
+    ws = (LayerWeightsStruct * len(layers))(*[w.struct() for w in layers])
+    cs = (KVCacheStruct * len(caches))(*[c.struct() for c in caches])
+    return ws, cs
+
+
+def step_workspace_size(layers, caches, batch: int, n_flows: int, max_context: int) -> int:
+    n = ctypes.c_size_t()
+    ws, cs = _structs(layers, caches)
+    check(lib().dfx_dual_flow_decode_step_workspace_size(ws, cs, len(layers), batch, n_flows, max_context,
+                                                          ctypes.byref(n)))
+    return n.value
+
+
+def dual_flow_decode_step(tokens: torch.Tensor, embed_primary: torch.Tensor, embed_aux: Optional[torch.Tensor],
+                          layers, caches, context_lens: torch.Tensor, max_context: int, n_flows: int = 2,
+                          out: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None,
+                          stream=None) -> torch.Tensor:
+    """One decode step of a layer stack: token ids [B] int32 -> residual rows [F][B][hidden]
+    fp32 after the last layer (each layer appends the primary's K/V row to its own cache)."""
+    tokens = _contig(tokens, "tokens")
+    if tokens.dtype != torch.int32:
+        raise TypeError("tokens must be int32")
+    B = tokens.numel()
+    vocab, H = embed_primary.shape
+    x = out if out is not None else torch.empty(n_flows, B, H, dtype=torch.float32, device=tokens.device)
+    ws, cs = _structs(layers, caches)
+    need = step_workspace_size(layers, caches, B, n_flows, max_context)
+    buf = _workspace(workspace, tokens.device, "step").get(need)
+    check(lib().dfx_dual_flow_decode_step(ws, cs, len(layers), _ptr(tokens), vocab, _ptr(_contig(embed_primary, "embed_primary")),
+                                          None if embed_aux is None else _ptr(_contig(embed_aux, "embed_aux")),
+                                          _ptr(context_lens), B, max_context, n_flows, _ptr(x), _ptr(buf), need,
+                                          _stream(stream)))
     return x
 
 

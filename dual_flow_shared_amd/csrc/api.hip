@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "common.h"
 
 using namespace dfx;
@@ -473,6 +475,72 @@ dfx_status layer_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_
   return DFX_OK;
 }
 
+
+// Workspace regions large enough for every layer of a stack (same hidden size): each region
+// the largest any layer needs, so all layers share one layout.
+dfx_status step_plan(const dfx_layer_weights *layers, const dfx_kv_cache *caches, int32_t n_layers,
+                     int32_t batch, int32_t n_flows, int32_t max_context, LayerPlan *pl) {
+  if (n_layers < 1 || !layers || !caches) return fail(DFX_EINVAL, "n_layers %d / layers / caches", n_layers);
+  LayerPlan m{};
+  for (int l = 0; l < n_layers; ++l) {
+    LayerPlan q;
+    dfx_status st = layer_plan(&layers[l], &caches[l], batch, n_flows, max_context, &q);
+    if (st) return st;
+    if (layers[l].hidden != layers[0].hidden) return fail(DFX_EINVAL, "layer %d hidden %d != %d", l, layers[l].hidden, layers[0].hidden);
+    m.tiles = std::max(m.tiles, q.tiles); m.h1 = std::max(m.h1, q.h1); m.qkv = std::max(m.qkv, q.qkv);
+    m.o = std::max(m.o, q.o); m.h2 = std::max(m.h2, q.h2); m.inter = std::max(m.inter, q.inter);
+    m.attn_ws = std::max(m.attn_ws, q.attn_ws);
+  }
+  m.total = m.tiles + m.h1 + m.qkv + m.o + m.h2 + m.inter + m.attn_ws;
+  *pl = m;
+  return DFX_OK;
+}
+
+// One layer on a workspace laid out by the region sizes of `p`. norm_in: normalize x into h1
+// first (else h1 already holds this layer's normed rows). next: finish the down projection
+// into the next layer's normed rows (in h1) instead of a plain residual update.
+dfx_status run_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv, const int32_t *context_lens, int B,
+                     int max_context, int F, float *x, const LayerPlan &p, char *base, hipStream_t s,
+                     bool norm_in, const dfx_layer_weights *next) {
+  const int H = w->hidden, D = w->head_dim, Hq = w->num_q_heads;
+  const int Hkv = w->num_kv_heads, Nqkv = (Hq + 2 * Hkv) * D, I = w->intermediate;
+  float *tiles = (float *)base;
+  uint16_t *h1 = (uint16_t *)(base + p.tiles);
+  float *qkv = (float *)((char *)h1 + p.h1);
+  uint16_t *ob = (uint16_t *)((char *)qkv + p.qkv);
+  uint16_t *h2 = (uint16_t *)((char *)ob + p.o);
+  uint16_t *inter = (uint16_t *)((char *)h2 + p.h2);
+  void *aws = (char *)inter + p.inter;
+  dfx_status r;
+  LayerGlueArgs g{};
+  g.n_flows = F; g.batch = B; g.tiles = tiles; g.x = x; g.eps = w->rms_eps;
+  g.kv = *kv; g.ctx = context_lens; g.num_q_heads = Hq; g.head_dim = D;
+  auto ksplit = [&](int K, int N) { return gemm_plan(F, B, K, N).ksplit; };
+  // attention block: norm, shared Q/K/V projection, primary-only append, dual attention
+  if (norm_in && (r = hip_status(launch_rmsnorm(F * B, H, x, w->attn_norm_gain, w->rms_eps, h1, s, F), "rmsnorm launch")))
+    return r;
+  if ((r = run_linear_parts(F, B, H, Nqkv, 2, h1, w->w_qkv, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  g.N = Nqkv; g.ksplit = ksplit(H, Nqkv); g.out = qkv;
+  if ((r = hip_status(launch_layer_glue(kGlueQkv, g, s), "qkv finish launch"))) return r;
+  // attention writes its rows already rounded to bf16, in W_o's fragment order
+  AttnCall c{kv, context_lens, B, max_context, Hq, DFX_F32, qkv, F == 2 ? qkv + (size_t)B * Nqkv : nullptr,
+             Nqkv, F == 2 ? w->couple_a : nullptr, 0, 0.f, (float *)ob,
+             F == 2 ? (float *)ob : nullptr, nullptr, 0, aws, p.attn_ws, 2};
+  if ((r = run_attn(c, s))) return r;
+  // output projection + residual, then the MLP norm
+  if ((r = run_linear_parts(F, B, Hq * D, H, 2, ob, w->w_o, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  g.N = H; g.ksplit = ksplit(Hq * D, H); g.gain = w->mlp_norm_gain; g.h = h2;
+  if ((r = hip_status(launch_layer_glue(kGlueONorm, g, s), "o finish launch"))) return r;
+  // MLP: shared gate/up projection, SwiGLU with b coupling, shared down projection with
+  // c coupling and the residual (and the next layer's norm)
+  if ((r = run_gate_up_swiglu(F, B, H, I, h2, w->w_gate_up, w->couple_b, inter, s))) return r;
+  if ((r = run_linear_parts(F, B, I, H, 2, inter, w->w_down, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
+  g.N = H; g.ksplit = ksplit(I, H); g.couple = F == 2 ? w->couple_c : nullptr;
+  if (!next) return hip_status(launch_layer_glue(kGlueDown, g, s), "down finish launch");
+  g.gain = next->attn_norm_gain; g.eps = next->rms_eps; g.h = h1;
+  return hip_status(launch_layer_glue(kGlueDownNorm, g, s), "down finish + norm launch");
+}
+
 }  // namespace
 
 dfx_status dfx_dual_flow_decode_layer_workspace_size(const dfx_layer_weights *w,
@@ -502,43 +570,60 @@ dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_c
   if (!workspace || workspace_bytes < p.total)
     return fail(DFX_EWORKSPACE, "layer needs %zu workspace bytes, got %zu", p.total, workspace_bytes);
   if (batch == 0) return DFX_OK;
+  return run_layer(w, kv, context_lens, batch, max_context, n_flows, x, p, (char *)workspace,
+                   (hipStream_t)stream, true, nullptr);
+  DFX_END
+}
+
+dfx_status dfx_dual_flow_decode_step_workspace_size(const dfx_layer_weights *layers,
+                                                    const dfx_kv_cache *caches, int32_t n_layers,
+                                                    int32_t batch, int32_t n_flows,
+                                                    int32_t max_context, size_t *bytes) {
+  DFX_BEGIN
+  LayerPlan p;
+  dfx_status st = step_plan(layers, caches, n_layers, batch, n_flows, max_context, &p);
+  if (st) return st;
+  if (!bytes) return fail(DFX_EINVAL, "bytes is NULL");
+  *bytes = p.total;
+  return DFX_OK;
+  DFX_END
+}
+
+dfx_status dfx_dual_flow_decode_step(const dfx_layer_weights *layers, const dfx_kv_cache *caches,
+                                     int32_t n_layers, const int32_t *tokens, int32_t vocab,
+                                     const uint16_t *embed_primary, const uint16_t *embed_aux,
+                                     const int32_t *context_lens, int32_t batch, int32_t max_context,
+                                     int32_t n_flows, float *x, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  DFX_BEGIN
+  LayerPlan p;
+  dfx_status st = step_plan(layers, caches, n_layers, batch, n_flows, max_context, &p);
+  if (st) return st;
+  if (vocab < 1) return fail(DFX_EINVAL, "vocab %d", vocab);
+  if (!embed_primary || (n_flows == 2 && !embed_aux))
+    return fail(DFX_EINVAL, "embedding table is NULL (the auxiliary flow has its own)");
+  if (((uintptr_t)embed_primary & 7) || (embed_aux && ((uintptr_t)embed_aux & 7)))
+    return fail(DFX_EINVAL, "embedding tables must be 8-byte aligned");
+  if (batch > 0 && (!context_lens || !x || !tokens)) return fail(DFX_EINVAL, "tokens / context_lens / x is NULL");
+  if (!aligned16(x)) return fail(DFX_EINVAL, "x not 16-byte aligned");
+  if (!workspace || workspace_bytes < p.total)
+    return fail(DFX_EWORKSPACE, "decode step needs %zu workspace bytes, got %zu", p.total, workspace_bytes);
+  if (batch == 0) return DFX_OK;
   hipStream_t s = (hipStream_t)stream;
-  const int F = n_flows, B = batch, H = w->hidden, D = w->head_dim, Hq = w->num_q_heads;
-  const int Hkv = w->num_kv_heads, Nqkv = (Hq + 2 * Hkv) * D, I = w->intermediate;
-  char *base = (char *)workspace;
-  float *tiles = (float *)base;
-  uint16_t *h1 = (uint16_t *)(base + p.tiles);
-  float *qkv = (float *)((char *)h1 + p.h1);
-  uint16_t *ob = (uint16_t *)((char *)qkv + p.qkv);
-  uint16_t *h2 = (uint16_t *)((char *)ob + p.o);
-  uint16_t *inter = (uint16_t *)((char *)h2 + p.h2);
-  void *aws = (char *)inter + p.inter;
-  const int rows = F * B;
-  dfx_status r;
-  LayerGlueArgs g{};
-  g.n_flows = F; g.batch = B; g.tiles = tiles; g.x = x; g.eps = w->rms_eps;
-  g.kv = *kv; g.ctx = context_lens; g.num_q_heads = Hq; g.head_dim = D;
-  auto ksplit = [&](int K, int N) { return gemm_plan(F, B, K, N).ksplit; };
-  // attention block: norm, shared Q/K/V projection, primary-only append, dual attention
-  if ((r = hip_status(launch_rmsnorm(rows, H, x, w->attn_norm_gain, w->rms_eps, h1, s, F), "rmsnorm launch"))) return r;
-  if ((r = run_linear_parts(F, B, H, Nqkv, 2, h1, w->w_qkv, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
-  g.N = Nqkv; g.ksplit = ksplit(H, Nqkv); g.out = qkv;
-  if ((r = hip_status(launch_layer_glue(kGlueQkv, g, s), "qkv finish launch"))) return r;
-  // attention writes its rows already rounded to bf16, in W_o's fragment order
-  AttnCall c{kv, context_lens, B, max_context, Hq, DFX_F32, qkv, F == 2 ? qkv + (size_t)B * Nqkv : nullptr,
-             Nqkv, F == 2 ? w->couple_a : nullptr, 0, 0.f, (float *)ob,
-             F == 2 ? (float *)ob : nullptr, nullptr, 0, aws, p.attn_ws, 2};
-  if ((r = run_attn(c, s))) return r;
-  // output projection + residual, then the MLP norm
-  if ((r = run_linear_parts(F, B, Hq * D, H, 2, ob, w->w_o, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
-  g.N = H; g.ksplit = ksplit(Hq * D, H); g.gain = w->mlp_norm_gain; g.h = h2;
-  if ((r = hip_status(launch_layer_glue(kGlueONorm, g, s), "o finish launch"))) return r;
-  // MLP: shared gate/up projection, SwiGLU with b coupling, shared down projection with
-  // c coupling and the residual
-  if ((r = run_gate_up_swiglu(F, B, H, I, h2, w->w_gate_up, w->couple_b, inter, s))) return r;
-  if ((r = run_linear_parts(F, B, I, H, 2, inter, w->w_down, 1, 0, nullptr, nullptr, nullptr, tiles, s, 1))) return r;
-  g.N = H; g.ksplit = ksplit(I, H); g.couple = F == 2 ? w->couple_c : nullptr;
-  return hip_status(launch_layer_glue(kGlueDown, g, s), "down finish launch");
+  const dfx_layer_weights &w0 = layers[0];
+  // both flows' embedding rows and layer 0's normed rows, in one kernel
+  dfx_status r = hip_status(launch_embed_norm(n_flows, batch, w0.hidden, tokens, vocab, embed_primary, embed_aux,
+                                              w0.attn_norm_gain, w0.rms_eps, x,
+                                              (uint16_t *)((char *)workspace + p.tiles), s),
+                            "embedding launch");
+  if (r) return r;
+  // each layer but the last finishes its down projection into the next layer's normed rows
+  for (int l = 0; l < n_layers; ++l) {
+    r = run_layer(&layers[l], &caches[l], context_lens, batch, max_context, n_flows, x, p, (char *)workspace, s,
+                  false, l + 1 < n_layers ? &layers[l + 1] : nullptr);
+    if (r) return r;
+  }
+  return DFX_OK;
   DFX_END
 }
 

@@ -83,6 +83,39 @@ __device__ __forceinline__ f32x4 sum_split_tiles(const float *tiles, int ksplit,
   return s;
 }
 
+// RMSNorm of one row by a 1024-thread work-group: thread t owns the float4 slices
+// t + 1024 u (u < kNormSlices; zero past the row, dim <= 16384). The reduction order is fixed
+// (each thread's slices in order, the wave butterfly, then the 16 waves in order), so every
+// kernel that normalizes a row through these helpers rounds identical rows identically.
+constexpr int kNormSlices = 4;
+
+__device__ __forceinline__ float norm_scale(const f32x4 *v, int dim, float eps, float *red) {
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < kNormSlices; ++u) ss += v[u][0] * v[u][0] + v[u][1] * v[u][1] + v[u][2] * v[u][2] + v[u][3] * v[u][3];
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < 16; ++w) tot += red[w];
+  return 1.0f / sqrtf(tot / (float)dim + eps);
+}
+
+// y = bf16(v * r * gain) for this thread's slices of row (f, b) (row index `row` when
+// row-major); packed_flows > 0 writes the fragment order of xpack_offset.
+__device__ __forceinline__ void norm_store(const f32x4 *v, const f32x4 *gg, float r, int dim, uint16_t *y,
+                                           int packed_flows, int f, int b, int64_t row) {
+#pragma unroll
+  for (int u = 0; u < kNormSlices; ++u) {
+    const int i = threadIdx.x + 1024 * u;
+    if (4 * i >= dim) continue;
+    const u32x2 o{pack_bf16x2(v[u][0] * r * gg[u][0], v[u][1] * r * gg[u][1]),
+                  pack_bf16x2(v[u][2] * r * gg[u][2], v[u][3] * r * gg[u][3])};
+    const int64_t at = packed_flows ? xpack_offset(packed_flows, f, b, 4 * i, dim) : row * dim + 4 * i;
+    *(u32x2 *)(y + at) = o;
+  }
+}
+
 // ---- launch-time parameter blocks --------------------------------------------------
 
 struct AttnArgs {
@@ -140,7 +173,7 @@ __device__ __forceinline__ float *attn_out(const AttnArgs &p, int f, int b, int 
 }
 
 // Arguments of the kernels that finish a projection of the decode layer.
-enum { kGlueQkv = 0, kGlueONorm = 1, kGlueDown = 3 };
+enum { kGlueQkv = 0, kGlueONorm = 1, kGlueDown = 3, kGlueDownNorm = 4 };
 struct LayerGlueArgs {
   int32_t n_flows, batch, N, ksplit;
   const float *tiles;  // [ksplit][groups][64][N]
@@ -170,6 +203,11 @@ hipError_t launch_layer_glue(int which, const LayerGlueArgs &a, hipStream_t s);
 // flows x batch); 0: row-major.
 hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
                           uint16_t *y, hipStream_t s, int packed_flows = 0);
+// x[f][b] = widen(embed_f[tokens[b]]) (token ids clamped to the table) and h1 = bf16(rmsnorm
+// (x) * gain) in the fragment order of xpack_offset, for flows f < n_flows.
+hipError_t launch_embed_norm(int32_t n_flows, int32_t batch, int32_t dim, const int32_t *tokens,
+                             int32_t vocab, const uint16_t *embed0, const uint16_t *embed1,
+                             const float *gain, float eps, float *x, uint16_t *h1, hipStream_t s);
 hipError_t launch_swiglu(int32_t n_flows, int32_t rows, int32_t dim, const float *gu,
                          const float *b, uint16_t *out, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);

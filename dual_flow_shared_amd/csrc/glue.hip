@@ -5,44 +5,65 @@
 namespace dfx {
 
 // One work-group of 1024 threads per row; thread t owns float4 slices t, t + 1024, ... of the
-// row (at most 4: dim <= 16384), held in registers, and its gain slices are loaded up front,
-// so the kernel makes one round trip to memory before the reduction.
+// row (norm_scale), held in registers, and its gain slices are loaded up front, so the kernel
+// makes one round trip to memory before the reduction.
 // packed_flows > 0: row r = f * batch + b is written in the fragment order of xpack_offset.
 __global__ void __launch_bounds__(1024) rmsnorm_kernel(int32_t dim, const float *x,
                                                        const float *gain, float eps, uint16_t *y,
                                                        int packed_flows, int batch) {
-  constexpr int PT = 4;
   __shared__ float red[16];
   const int64_t row = blockIdx.x;
   const f32x4 *xr = (const f32x4 *)(x + row * dim);
   const f32x4 *g4 = (const f32x4 *)gain;
   const int n4 = dim / 4;
-  f32x4 v[PT], gg[PT];
+  f32x4 v[kNormSlices], gg[kNormSlices];
 #pragma unroll
-  for (int t = 0; t < PT; ++t) {
-    const int i = threadIdx.x + 1024 * t;
-    v[t] = i < n4 ? xr[i] : f32x4{0.f, 0.f, 0.f, 0.f};
-    gg[t] = i < n4 ? g4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < kNormSlices; ++u) {
+    const int i = threadIdx.x + 1024 * u;
+    v[u] = i < n4 ? xr[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    gg[u] = i < n4 ? g4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float ss = 0.f;
-#pragma unroll
-  for (int t = 0; t < PT; ++t) ss += v[t][0] * v[t][0] + v[t][1] * v[t][1] + v[t][2] * v[t][2] + v[t][3] * v[t][3];
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
-  for (int w = 0; w < 16; ++w) tot += red[w];
-  const float r = 1.0f / sqrtf(tot / (float)dim + eps);
+  const float r = norm_scale(v, dim, eps, red);
   const int f = packed_flows ? (int)(row / batch) : 0, b = packed_flows ? (int)(row % batch) : 0;
+  norm_store(v, gg, r, dim, y, packed_flows, f, b, row);
+}
+
+// Embedding gather of both flows (each from its own table) plus the first layer's RMSNorm:
+// one work-group of 1024 threads per (flow, sequence) row.
+__global__ void __launch_bounds__(1024) embed_norm_kernel(int32_t F, int32_t B, int32_t dim,
+                                                          const int32_t *tokens, int32_t vocab,
+                                                          const uint16_t *e0, const uint16_t *e1,
+                                                          const float *gain, float eps, float *x,
+                                                          uint16_t *h1) {
+  __shared__ float red[16];
+  const int row = blockIdx.x, f = row / B, b = row % B;
+  const int tok = min(max(tokens[b], 0), vocab - 1);
+  const uint16_t *er = (f == 0 ? e0 : e1) + (int64_t)tok * dim;
+  float *xr = x + (int64_t)row * dim;
+  const int n4 = dim / 4;
+  f32x4 v[kNormSlices], gg[kNormSlices];
 #pragma unroll
-  for (int t = 0; t < PT; ++t) {
-    const int i = threadIdx.x + 1024 * t;
-    if (i >= n4) continue;
-    const u32x2 o{pack_bf16x2(v[t][0] * r * gg[t][0], v[t][1] * r * gg[t][1]),
-                  pack_bf16x2(v[t][2] * r * gg[t][2], v[t][3] * r * gg[t][3])};
-    const int64_t at = packed_flows ? xpack_offset(packed_flows, f, b, 4 * i, dim) : row * dim + 4 * i;
-    *(u32x2 *)(y + at) = o;
+  for (int u = 0; u < kNormSlices; ++u) {
+    const int i = threadIdx.x + 1024 * u;
+    v[u] = gg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i < n4) {
+      const u32x2 w = *(const u32x2 *)(er + 4 * i);
+      v[u] = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+      gg[u] = *(const f32x4 *)(gain + 4 * i);
+      *(f32x4 *)(xr + 4 * i) = v[u];
+    }
   }
+  const float r = norm_scale(v, dim, eps, red);
+  norm_store(v, gg, r, dim, h1, F, f, b, row);
+}
+
+hipError_t launch_embed_norm(int32_t n_flows, int32_t batch, int32_t dim, const int32_t *tokens,
+                             int32_t vocab, const uint16_t *embed0, const uint16_t *embed1,
+                             const float *gain, float eps, float *x, uint16_t *h1, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  embed_norm_kernel<<<n_flows * batch, 1024, 0, s>>>(n_flows, batch, dim, tokens, vocab, embed0, embed1,
+                                                     gain, eps, x, h1);
+  return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,

@@ -59,47 +59,62 @@ __global__ void __launch_bounds__(256) qkv_finish_kernel(LayerGlueArgs a) {
 
 // x += sum of the W_o tiles (in place), then h = bf16(rmsnorm(x) * gain) in the fragment
 // order of the next projection (xpack_offset). One work-group of 1024 threads per
-// (flow, row); thread t owns float4 slices t, t + 1024, ... (at most 4: N <= 16384), held in
-// registers, and every load (tiles, residual, gain) is issued before the reduction.
+// (flow, row); its slices (norm_scale) are held in registers, and every load (tiles,
+// residual, gain) is issued before the reduction.
 __global__ void __launch_bounds__(1024) o_finish_norm_kernel(LayerGlueArgs a) {
-  constexpr int PT = 4;
   __shared__ float red[16];
   const int F = a.n_flows, B = a.batch, N = a.N;
   const int rpg = 64 / F, groups = (B + rpg - 1) / rpg;
   const int row = blockIdx.x, f = row / B, b = row % B;
   float *xr = a.x + (int64_t)row * N;
   const int n4 = N / 4;
-  f32x4 v[PT], gg[PT];
+  f32x4 v[kNormSlices], gg[kNormSlices];
 #pragma unroll
-  for (int t = 0; t < PT; ++t) {
-    const int i = threadIdx.x + 1024 * t;
-    v[t] = gg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < kNormSlices; ++u) {
+    const int i = threadIdx.x + 1024 * u;
+    v[u] = gg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (i < n4) {
-      v[t] = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, 4 * i) + *(const f32x4 *)(xr + 4 * i);
-      gg[t] = *(const f32x4 *)(a.gain + 4 * i);
+      v[u] = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, 4 * i) + *(const f32x4 *)(xr + 4 * i);
+      gg[u] = *(const f32x4 *)(a.gain + 4 * i);
+      *(f32x4 *)(xr + 4 * i) = v[u];
     }
   }
-  float ss = 0.f;
+  const float r = norm_scale(v, N, a.eps, red);
+  norm_store(v, gg, r, N, a.h, F, f, b, row);
+}
+
+// The last projection of a layer finishing into the next layer: m = summed W_down tiles,
+// flow 1 += c * flow 0, x += m (in place), then the next layer's h1 = bf16(rmsnorm(x) *
+// gain) in W_qkv's fragment order. The same arithmetic, in the same order, as down_finish
+// followed by the RMSNorm kernel. One work-group of 1024 threads per (flow, row).
+__global__ void __launch_bounds__(1024) down_finish_norm_kernel(LayerGlueArgs a) {
+  __shared__ float red[16];
+  const int F = a.n_flows, B = a.batch, N = a.N;
+  const int rpg = 64 / F, groups = (B + rpg - 1) / rpg;
+  const int row = blockIdx.x, f = row / B, b = row % B;
+  float *xr = a.x + (int64_t)row * N;
+  const int n4 = N / 4;
+  f32x4 v[kNormSlices], gg[kNormSlices];
 #pragma unroll
-  for (int t = 0; t < PT; ++t) {
-    const int i = threadIdx.x + 1024 * t;
-    if (i < n4) *(f32x4 *)(xr + 4 * i) = v[t];
-    ss += v[t][0] * v[t][0] + v[t][1] * v[t][1] + v[t][2] * v[t][2] + v[t][3] * v[t][3];
+  for (int u = 0; u < kNormSlices; ++u) {
+    const int i = threadIdx.x + 1024 * u;
+    v[u] = gg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i < n4) {
+      const int col = 4 * i;
+      f32x4 m = sum_tiles(a.tiles, a.ksplit, groups, N, f, b, rpg, col);
+      if (f == 1 && a.couple) {
+        const f32x4 prim = sum_tiles(a.tiles, a.ksplit, groups, N, 0, b, rpg, col);
+        const f32x4 c = *(const f32x4 *)(a.couple + col);
+        m = f32x4{fmaf(c[0], prim[0], m[0]), fmaf(c[1], prim[1], m[1]), fmaf(c[2], prim[2], m[2]),
+                  fmaf(c[3], prim[3], m[3])};
+      }
+      v[u] = *(const f32x4 *)(xr + col) + m;
+      gg[u] = *(const f32x4 *)(a.gain + col);
+      *(f32x4 *)(xr + col) = v[u];
+    }
   }
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
-  for (int w = 0; w < 16; ++w) tot += red[w];
-  const float r = 1.0f / sqrtf(tot / (float)N + a.eps);
-#pragma unroll
-  for (int t = 0; t < PT; ++t) {
-    const int i = threadIdx.x + 1024 * t;
-    if (i >= n4) continue;
-    *(u32x2 *)(a.h + xpack_offset(F, f, b, 4 * i, N)) =
-        u32x2{pack_bf16x2(v[t][0] * r * gg[t][0], v[t][1] * r * gg[t][1]),
-              pack_bf16x2(v[t][2] * r * gg[t][2], v[t][3] * r * gg[t][3])};
-  }
+  const float r = norm_scale(v, N, a.eps, red);
+  norm_store(v, gg, r, N, a.h, F, f, b, row);
 }
 
 // m = summed W_down tiles; flow 1 += c * flow 0; x += m (in place). One thread per 4
@@ -135,6 +150,9 @@ hipError_t launch_layer_glue(int which, const LayerGlueArgs &a, hipStream_t s) {
       break;
     case kGlueONorm:
       o_finish_norm_kernel<<<F * B, 1024, 0, s>>>(a);
+      break;
+    case kGlueDownNorm:
+      down_finish_norm_kernel<<<F * B, 1024, 0, s>>>(a);
       break;
     default:
       threads = (int64_t)B * (a.N / 4);

@@ -287,6 +287,40 @@ dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_c
                                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * One decode step of a stack of dual-flow layers, from token ids to the residual rows
+ * after the last layer (Sintesi Tecnica: Dual-Flow Transformers, "Architettura Core": at
+ * every generated position the auxiliary flow runs beside the primary; the two flows use
+ * separate token embeddings and share every layer's matrices; only the primary writes each
+ * layer's cache):
+ *   x[0][b] = embed_primary[tokens[b]],  x[1][b] = embed_aux[tokens[b]]   (bf16 rows, widened)
+ *   for l < n_layers:  x = layer_l(x)   (exactly dfx_dual_flow_decode_layer with layers[l],
+ *                                        caches[l], the same context_lens and max_context)
+ *  layers, caches  host arrays of n_layers structs (device pointers inside); every layer has
+ *                  the same hidden size; layer l appends to caches[l] only.
+ *  tokens          device int32 [batch]: the token at the generated position (ids are
+ *                  clamped to [0, vocab)).
+ *  embed_primary, embed_aux  device bf16 [vocab][hidden], 8-byte aligned; embed_aux is the
+ *                  auxiliary flow's own table (may be NULL when n_flows = 1).
+ *  x               device fp32 [n_flows][batch][hidden], output.
+ *  workspace       >= dfx_dual_flow_decode_step_workspace_size bytes, no initial contents.
+ * Results equal n_layers dfx_dual_flow_decode_layer calls on the embedded rows bit for bit
+ * (each layer's down projection finishes straight into the next layer's norm, with the same
+ * arithmetic). The call allocates nothing and never synchronizes, so a caller may capture it
+ * in a graph (max_context then fixes the attention plan for every replay).
+ */
+dfx_status dfx_dual_flow_decode_step_workspace_size(const dfx_layer_weights *layers,
+                                                    const dfx_kv_cache *caches, int32_t n_layers,
+                                                    int32_t batch, int32_t n_flows,
+                                                    int32_t max_context, size_t *bytes);
+
+dfx_status dfx_dual_flow_decode_step(const dfx_layer_weights *layers, const dfx_kv_cache *caches,
+                                     int32_t n_layers, const int32_t *tokens, int32_t vocab,
+                                     const uint16_t *embed_primary, const uint16_t *embed_aux,
+                                     const int32_t *context_lens, int32_t batch, int32_t max_context,
+                                     int32_t n_flows, float *x, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
  * Where a completed dfx_dual_flow_decode_layer call with the same sizes leaves its
  * intermediates in the workspace: byte offsets of
  *   h1     bf16 normed rows entering W_qkv            [hidden columns]

@@ -22,8 +22,11 @@ Functions and their pins (tests/test_oracle_*.py):
   cache.kv_append            -- hand-computed slot addresses, bit patterns
   layer.dual_flow_layer      -- textbook pre-norm decoder layer in torch.nn.functional
                                (primary flow), aux = primary identities, cache diff
+  step.embed                 -- one-hot matrix product of the tables
+  step.dual_flow_step        -- composition of the pinned layer; shared-table / uncoupled
+                               aux = primary; primary and caches blind to the aux table
 The placement of the b and c coupling vectors is a reading of the pages (they
 name the levels, not the formula); it is pinned only by the identities above:
 "parity unpinned" beyond this reading.
 """
-from . import numerics, attention, linear, cache, layer  # noqa: F401
+from . import numerics, attention, linear, cache, layer, step  # noqa: F401

@@ -21,7 +21,7 @@ def declared():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = _abi.lib()
     names = declared()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, n
@@ -174,3 +174,33 @@ def test_layer_taps_are_disjoint_regions_of_the_workspace():
             assert start + size <= nxt, (F, B, name)
     assert lib.dfx_dual_flow_decode_layer_taps(ctypes.byref(w), ctypes.byref(k), 32, 3, 8192, ctypes.byref(t)) == 1
     assert lib.dfx_dual_flow_decode_layer_taps(ctypes.byref(w), ctypes.byref(k), 32, 2, 8192, None) == 1
+
+
+def test_step_rejects():
+    lib = _abi.lib()
+    W = _abi.LayerWeightsStruct * 2
+    K = _abi.KVCacheStruct * 2
+    ws, ks = W(), K()
+    for w in ws:
+        w.hidden, w.num_q_heads, w.num_kv_heads, w.head_dim, w.intermediate, w.rms_eps = 256, 8, 2, 64, 512, 1e-5
+        for f in ("attn_norm_gain", "w_qkv", "w_o", "mlp_norm_gain", "w_gate_up", "w_down"):
+            setattr(w, f, FAKE)
+    ks[0], ks[1] = kv(heads=2, D=64, mb=16, nb=64), kv(heads=2, D=64, mb=16, nb=64)
+    n = ctypes.c_size_t()
+    assert lib.dfx_dual_flow_decode_step_workspace_size(ws, ks, 2, 4, 2, 200, ctypes.byref(n)) == 0
+    n1 = ctypes.c_size_t()
+    assert lib.dfx_dual_flow_decode_layer_workspace_size(ctypes.byref(ws[0]), ctypes.byref(ks[0]), 4, 2, 200, ctypes.byref(n1)) == 0
+    assert n.value == n1.value                       # equal layers share one layout
+    args = lambda **o: dict(dict(nl=2, tok=FAKE, vocab=10, e1=FAKE, e2=FAKE, ctx=FAKE, x=FAKE, w=FAKE, wb=n.value), **o)
+    def call(**o):
+        a = args(**o)
+        return lib.dfx_dual_flow_decode_step(ws, ks, a["nl"], a["tok"], a["vocab"], a["e1"], a["e2"], a["ctx"], 4, 200,
+                                             2, a["x"], a["w"], a["wb"], None)
+    assert call(nl=0) == 1
+    assert call(vocab=0) == 1
+    assert call(e2=None) == 1                       # the auxiliary flow needs its own table
+    assert call(e1=FAKE + 4) == 1                   # tables 8-byte aligned
+    assert call(tok=None) == 1
+    assert call(wb=n.value - 1) == 3
+    ws[1].hidden = 512
+    assert lib.dfx_dual_flow_decode_step_workspace_size(ws, ks, 2, 4, 2, 200, ctypes.byref(n)) == 1

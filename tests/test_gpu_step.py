@@ -1,0 +1,96 @@
+"""GPU parity of the multi-layer decode step (dfx_dual_flow_decode_step)."""
+import numpy as np
+import pytest
+import torch
+
+import dfx_inputs as gen
+import dual_flow_shared_amd as dfx
+from gpu_util import cache_of, dev, host_bits
+from oracle.step import dual_flow_step
+from test_gpu_layer import layer_close, weights_of
+
+pytestmark = pytest.mark.gpu
+
+KW = dict(vocab=300, batch=5, context=150, hidden=256, num_q_heads=8, num_kv_heads=2, head_dim=64,
+          intermediate=512, w_std=0.05)
+
+
+def inputs(c):
+    layers = [weights_of(L) for L in c.layers]
+    caches = [cache_of(L.cache) for L in c.layers]
+    ctx = dev(c.layers[0].cache.context_lens + 1)
+    return layers, caches, ctx, int(ctx.max()), dev(c.tokens), dev(c.embed_primary), dev(c.embed_aux)
+
+
+def test_step_equals_layer_calls_bit_for_bit():
+    """Embedding + norm in one kernel and each layer's down projection finished straight into
+    the next layer's norm give exactly what one layer call per layer gives on the embedded rows."""
+    c = gen.step_case(901, 3, **KW)
+    layers, caches, ctx, maxc, tokens, e1, e2 = inputs(c)
+    x = dfx.dual_flow_decode_step(tokens, e1, e2, layers, caches, ctx, maxc)
+    ref_caches = [cache_of(L.cache) for L in c.layers]
+    xr = torch.stack([e1[tokens.long()].float(), e2[tokens.long()].float()]).contiguous()
+    for w, kv in zip(layers, ref_caches):
+        dfx.dual_flow_decode_layer(xr, w, kv, ctx, maxc)
+    torch.cuda.synchronize()
+    assert torch.equal(x, xr)
+    for a, b in zip(caches, ref_caches):      # bit patterns: the pools hold NaN poison
+        assert np.array_equal(host_bits(a.k), host_bits(b.k)) and np.array_equal(host_bits(a.v), host_bits(b.v))
+
+
+def test_step_primary_only_and_against_the_oracle():
+    c = gen.step_case(902, 2, **KW)
+    layers, caches, ctx, maxc, tokens, e1, e2 = inputs(c)
+    x = dfx.dual_flow_decode_step(tokens, e1, e2, layers, caches, ctx, maxc)
+    k_dual = [host_bits(kv.k) for kv in caches]
+    caches1 = [cache_of(L.cache) for L in c.layers]
+    x1 = dfx.dual_flow_decode_step(tokens, e1, None, layers, caches1, ctx, maxc, n_flows=1)
+    torch.cuda.synchronize()
+    # the auxiliary flow changes neither the primary rows nor any cache byte
+    assert torch.equal(x1[0], x[0])
+    for a, kv in zip(k_dual, caches1):
+        assert np.array_equal(a, host_bits(kv.k))
+    want, pools = dual_flow_step(c.tokens, c.embed_primary, c.embed_aux, c.layers, c.layers[0].cache.context_lens)
+    layer_close(x.cpu().numpy(), want)
+    for (wk, _), got, L in zip(pools, k_dual, c.layers):
+        # each layer's pool changes exactly at the primary's new slots, the oracle's too
+        changed = np.argwhere(np.any(got != L.cache.k_pool, axis=-1))
+        assert len(changed) == c.tokens.shape[0] * L.num_kv_heads
+        assert np.array_equal(changed, np.argwhere(np.any(wk != L.cache.k_pool, axis=-1)))
+    # layer 0 appends bf16 roundings of fp32 (GPU) and fp64 (oracle) projections of the same
+    # normed rows: the same bits except next to a rounding midpoint
+    assert (k_dual[0] != pools[0][0]).mean() < 1e-4
+
+
+def test_step_graph_replays_match_eager():
+    """The step allocates nothing and never synchronizes: captured once in a graph, every
+    replay (with eager work and synchronizations in between) reproduces the eager result."""
+    c = gen.step_case(903, 2, **KW)
+    layers, caches, ctx, maxc, tokens, e1, e2 = inputs(c)
+    B, H = c.tokens.shape[0], KW["hidden"]
+    out = torch.empty(2, B, H, dtype=torch.float32, device="cuda")
+    ws = dfx.Workspace()
+    ws.get(dfx.step_workspace_size(layers, caches, B, 2, maxc))
+
+    def step():
+        dfx.dual_flow_decode_step(tokens, e1, e2, layers, caches, ctx, maxc, out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    k_eager = [host_bits(kv.k) for kv in caches]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        for kv, k in zip(caches, k_eager):
+            assert np.array_equal(host_bits(kv.k), k)
