@@ -34,7 +34,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="layer",
-                   choices=["layer", "attn-b16", "attn-ragged", "attn-long", "attn-fp32"])
+                   choices=["layer", "attn-b16", "attn-ragged", "attn-long", "attn-fp32", "step"])
+    p.add_argument("--layers", type=int, default=8, help="layers of the 'step' workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--splits", type=int, default=0, help="attention context splits (0 = plan)")
     p.add_argument("--kernel-reps", type=int, default=20)
@@ -131,6 +132,8 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     extra = {}
+    if args.workload == "step":
+        return bench_step(args)
     if args.copy_calibration:
         n = args.copy_calibration - args.copy_calibration % 16
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -267,6 +270,86 @@ def main():
             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": cfg, "roofline": roofline, "cpu_baseline": cpu, **extra}
+    print(json.dumps(line))
+
+
+def bench_step(args):
+    """A decode step of a stack of args.layers dual-flow layers of the one-layer workload's shape
+    (batch 32, context 8192, hidden 4096, 32/8 heads x 128, SwiGLU 14336, paged bf16 caches),
+    from token ids through both flows' embeddings: eager launches and one HIP-graph replay per
+    step. Weights, caches and embeddings are drawn on the GPU (synthetic: the timing needs
+    shapes, not values; parity is the GPU tests' job)."""
+    import torch
+
+    import dual_flow_shared_amd as dfx
+    torch.cuda.set_device(0)
+    gen_ = torch.Generator(device="cuda").manual_seed(2024)
+    B, H, Hq, Hkv, D, I, ctx_len, bs, vocab = 32, 4096, 32, 8, 128, 14336, 8192, 16, 32000
+    nl = args.layers
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=gen_, device="cuda") * std).to(torch.bfloat16)
+
+    def gains(n):
+        return torch.rand(n, generator=gen_, device="cuda") * 0.2 + 0.9
+
+    def unif(n):
+        return torch.rand(n, generator=gen_, device="cuda") * 2 - 1
+
+    layers, caches = [], []
+    nblk = B * ctx_len // bs
+    for _ in range(nl):
+        w = dfx.LayerWeights.from_row_major(gains(H), randn((Hq + 2 * Hkv) * D, H, std=0.02), randn(H, Hq * D, std=0.02),
+                                            gains(H), randn(2 * I, H, std=0.02), randn(H, I, std=0.02), Hq, Hkv, D, 1e-5,
+                                            unif(D), unif(I), unif(H))
+        table = torch.randperm(nblk, generator=gen_, device="cuda").to(torch.int32).view(B, ctx_len // bs)
+        caches.append(dfx.KVCache(randn(nblk, Hkv, bs, D), randn(nblk, Hkv, bs, D), table))
+        layers.append(w)
+        torch.cuda.synchronize()
+    e1, e2 = randn(vocab, H), randn(vocab, H)
+    tokens = torch.randint(0, vocab, (B,), generator=gen_, device="cuda", dtype=torch.int32)
+    ctx = torch.full((B,), ctx_len, dtype=torch.int32, device="cuda")
+    out = torch.empty(2, B, H, dtype=torch.float32, device="cuda")
+    ws = dfx.Workspace()
+    ws.get(dfx.step_workspace_size(layers, caches, B, 2, ctx_len))
+
+    def step():
+        dfx.dual_flow_decode_step(tokens, e1, e2, layers, caches, ctx, ctx_len, out=out, workspace=ws)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    eager_ms = timed(step, args.steps, stream)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = timed(graph.replay, args.steps, stream)
+    w_bytes = 2 * (Hq + 2 * Hkv) * D * H + 2 * H * Hq * D + 2 * 2 * I * H + 2 * H * I
+    kv_bytes = 2 * B * ctx_len * Hkv * D * 2
+    step_bytes = nl * (w_bytes + kv_bytes) + 2 * B * H * 2
+    ms = min(eager_ms, graph_ms)
+    line = {"metric": "dual-flow multi-layer decode steps/s at batch x ctx", "value": round(1000.0 / graph_ms, 2),
+            "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(graph_ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"dual-flow decode step: {nl} layers, batch {B} x context {ctx_len}, hidden {H}, "
+                                   f"{Hq}/{Hkv} heads x {D}, SwiGLU {I}, vocab {vocab}, both flows, HIP-graph replay",
+                       "layers": nl, "batch": B, "context": ctx_len, "hidden": H, "flows": 2},
+            "roofline": {"bound": "hbm", "achieved": round(step_bytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "traffic": None, "kernel": "whole step (weights + KV of every layer, read once)",
+                         "bytes_per_launch": int(step_bytes)},
+            "cpu_baseline": None, "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
+            "tokens_per_s": round(B * 1000.0 / graph_ms, 1), "ms_per_layer": round(graph_ms / nl, 4)}
     print(json.dumps(line))
 
 
