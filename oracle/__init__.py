@@ -25,8 +25,12 @@ Functions and their pins (tests/test_oracle_*.py):
   step.embed                 -- one-hot matrix product of the tables
   step.dual_flow_step        -- composition of the pinned layer; shared-table / uncoupled
                                aux = primary; primary and caches blind to the aux table
+  head.softmax / mixture /   -- torch softmax and argmax; alpha in [1/2, 1], certain primary
+       next_token / output_head  -> alpha = 1, flat -> (1 + 1/V) / 2, monotone; Gumbel-max
+                               frequencies; torch linear for the projection
 The placement of the b and c coupling vectors is a reading of the pages (they
 name the levels, not the formula); it is pinned only by the identities above:
-"parity unpinned" beyond this reading.
+"parity unpinned" beyond this reading. So is the mixture weight alpha_t = (1 + c_t) / 2
+(the pages fix only that it follows the primary's collision probability and stays >= 1/2).
 """
-from . import numerics, attention, linear, cache, layer, step  # noqa: F401
+from . import numerics, attention, linear, cache, layer, step, head  # noqa: F401
