@@ -28,6 +28,7 @@ TID_X1, TID_X2, TID_WQKV, TID_WO, TID_WGU, TID_WD = 11, 12, 13, 14, 15, 16
 TID_G1, TID_G2, TID_B, TID_C = 17, 18, 19, 20
 TID_LIN_X, TID_LIN_W, TID_LIN_CPL, TID_LIN_RES = 21, 22, 23, 24
 TID_TOK, TID_E1, TID_E2 = 31, 32, 33
+TID_HX, TID_HG, TID_WOUT, TID_NOISE = 41, 42, 43, 44
 
 
 def stream(seed: int, tid: int, *idx: int) -> np.random.Generator:
@@ -216,6 +217,21 @@ def linear_case(seed: int, n_flows: int, rows: int, in_features: int, out_featur
                       w, cpl, res)
 
 
+def _bf16_matrix(seed, tid, n, k, std, workers):
+    """[n][k] bf16 bits ~ N(0, std), in row blocks of 512 with sub-streams (seed, tid, first
+    row) so that large matrices fill in parallel."""
+    out = np.empty((n, k), dtype=np.uint16)
+    step = 512
+
+    def one(r0):
+        r1 = min(n, r0 + step)
+        out[r0:r1] = f32_to_bf16_bits(_normal(seed, tid, (r0,), (r1 - r0, k), std))
+
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, range(0, n, step)))
+    return out
+
+
 @dataclass
 class LayerCase:
     """One dual-flow decode layer: weights, coupling vectors, residual rows and a paged cache."""
@@ -256,17 +272,7 @@ def layer_case(seed: int, batch: int, context: int, hidden: int, num_q_heads: in
     x = np.stack([_normal(seed, TID_X1, (), (batch, hidden)), _normal(seed, TID_X2, (), (batch, hidden))])
 
     def wmat(tid, n, k):
-        # row-blocked sub-streams so large matrices fill in parallel
-        out = np.empty((n, k), dtype=np.uint16)
-        step = 512
-
-        def one(r0):
-            r1 = min(n, r0 + step)
-            out[r0:r1] = f32_to_bf16_bits(_normal(seed, tid, (r0,), (r1 - r0, k), w_std))
-
-        with ThreadPoolExecutor(workers) as ex:
-            list(ex.map(one, range(0, n, step)))
-        return out
+        return _bf16_matrix(seed, tid, n, k, w_std, workers)
 
     w_qkv = wmat(TID_WQKV, (Hq + 2 * Hkv) * D, hidden)
     w_o = wmat(TID_WO, hidden, Hq * D)
@@ -306,6 +312,31 @@ def step_case(seed: int, n_layers: int, vocab: int, batch: int, context: int, hi
                          num_kv_heads=num_kv_heads, head_dim=head_dim, intermediate=intermediate,
                          w_std=w_std, couple=couple, workers=workers) for l in range(n_layers)]
     return StepCase(seed, tokens, e1, e2, layers)
+
+
+@dataclass
+class HeadCase:
+    """Inputs of the shared output head: both flows' final residual rows, the final norm gain,
+    the shared vocabulary matrix and uniform noise for a Gumbel-max draw."""
+    seed: int
+    eps: float
+    x: np.ndarray       # float32 [F][B][hidden]
+    gain: np.ndarray    # float32 [hidden]
+    w_out: np.ndarray   # uint16 [vocab][hidden]
+    noise: np.ndarray   # float32 [B][vocab], uniform in (0, 1)
+
+
+def head_case(seed: int, n_flows: int, batch: int, hidden: int, vocab: int, w_std: float = 0.02,
+              x_std: float = 1.0, eps: float = 1e-5, workers: Optional[int] = None) -> HeadCase:
+    """Residual rows ~ N(0, x_std), gain ~ U(0.9, 1.1), W_out ~ N(0, w_std) bf16, noise ~
+    U(0, 1) with exact 0 moved to the smallest positive fp32 (so every log is finite)."""
+    workers = workers or _workers()
+    x = _normal(seed, TID_HX, (), (n_flows, batch, hidden), x_std)
+    g = _uniform(seed, TID_HG, (), (hidden,), 0.9, 1.1)
+    w = _bf16_matrix(seed, TID_WOUT, vocab, hidden, w_std, workers)
+    u = stream(seed, TID_NOISE).random((batch, vocab), dtype=np.float32)
+    u[u <= 0] = np.float32(np.finfo(np.float32).tiny)
+    return HeadCase(seed, eps, x, g, w, u)
 
 
 def config_attention(idx: int, workers: Optional[int] = None, **over) -> AttnCase:

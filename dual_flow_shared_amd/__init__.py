@@ -18,7 +18,8 @@ from ._abi import (DFX_BF16, DFX_F32, DFX_W_PACKED, DFX_W_ROW_MAJOR, DfxError, K
 __all__ = ["DfxError", "KVCache", "LayerWeights", "decode_attn", "decode_attn_plan",
            "kv_append_primary", "grouped_linear", "pack_weight", "rmsnorm", "swiglu_couple",
            "dual_flow_decode_layer", "layer_workspace_size", "copy_bytes", "read_bytes", "fill_bytes",
-           "layer_taps", "dual_flow_decode_step", "step_workspace_size", "Workspace", "version"]
+           "layer_taps", "dual_flow_decode_step", "step_workspace_size", "output_head",
+           "output_head_workspace_size", "output_head_taps", "Workspace", "version"]
 
 
 def version() -> int:
@@ -343,6 +344,49 @@ def layer_taps(weights: LayerWeights, cache: KVCache, batch: int, n_flows: int,
     check(lib().dfx_dual_flow_decode_layer_taps(ctypes.byref(w), ctypes.byref(c), batch, n_flows,
                                                 max_context, ctypes.byref(t)))
     return {name: getattr(t, name) for name, _ in t._fields_}
+
+
+def output_head_workspace_size(n_flows: int, batch: int, hidden: int, vocab: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib().dfx_dual_flow_output_head_workspace_size(n_flows, batch, hidden, vocab, ctypes.byref(n)))
+    return n.value
+
+
+def output_head_taps(n_flows: int, batch: int, hidden: int, vocab: int) -> dict:
+    """Byte offsets of the head's normed rows (fragment order) and fp32 logits in its workspace."""
+    h, lg = ctypes.c_size_t(), ctypes.c_size_t()
+    check(lib().dfx_dual_flow_output_head_taps(n_flows, batch, hidden, vocab, ctypes.byref(h), ctypes.byref(lg)))
+    return {"h": h.value, "logits": lg.value}
+
+
+def output_head(x: torch.Tensor, norm_gain: torch.Tensor, eps: float, w_out_packed: torch.Tensor,
+                uniform_noise: Optional[torch.Tensor] = None, *, want_p_mix: bool = False,
+                workspace: Optional[Workspace] = None, stream=None):
+    """Shared output head and flow mixture: x [F][B][hidden] fp32 after the last layer ->
+    (next_token [B] int32, alpha [B] fp32, p_mix [B][V] fp32 or None). w_out_packed: the
+    [vocab][hidden] bf16 matrix in packed layout (pack_weight). uniform_noise [B][V] fp32 in
+    (0, 1) makes the token a Gumbel-max draw from p_mix; None is greedy."""
+    x = _contig(x, "x")
+    if x.dim() != 3 or x.dtype != torch.float32:
+        raise ValueError("x must be fp32 [n_flows][batch][hidden]")
+    F, B, H = x.shape
+    V = w_out_packed.numel() // H
+    if w_out_packed.numel() != V * H:
+        raise ValueError("w_out_packed size is not a multiple of hidden")
+    dev = x.device
+    tok = torch.empty(B, dtype=torch.int32, device=dev)
+    alpha = torch.empty(B, dtype=torch.float32, device=dev)
+    p_mix = torch.empty(B, V, dtype=torch.float32, device=dev) if want_p_mix else None
+    if uniform_noise is not None:
+        uniform_noise = _contig(uniform_noise, "uniform_noise")
+        if uniform_noise.shape != (B, V) or uniform_noise.dtype != torch.float32:
+            raise ValueError("uniform_noise must be fp32 [batch][vocab]")
+    need = output_head_workspace_size(F, B, H, V)
+    buf = _workspace(workspace, dev, "head").get(need)
+    check(lib().dfx_dual_flow_output_head(F, B, H, V, _ptr(x), _ptr(_contig(norm_gain, "norm_gain")), eps,
+                                          _ptr(_contig(w_out_packed, "w_out_packed")), _ptr(uniform_noise),
+                                          _ptr(tok), _ptr(alpha), _ptr(p_mix), _ptr(buf), need, _stream(stream)))
+    return tok, alpha, p_mix
 
 
 def copy_bytes(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

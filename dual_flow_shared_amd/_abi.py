@@ -61,6 +61,9 @@ SIGNATURES = {
     "dfx_dual_flow_decode_layer_taps": (I32, [LWP, KVP, I32, I32, I32, ctypes.POINTER(LayerTapsStruct)]),
     "dfx_dual_flow_decode_step_workspace_size": (I32, [LWP, KVP, I32, I32, I32, I32, PSZ]),
     "dfx_dual_flow_decode_step": (I32, [LWP, KVP, I32, P, I32, P, P, P, I32, I32, I32, P, P, SZ, P]),
+    "dfx_dual_flow_output_head_workspace_size": (I32, [I32, I32, I32, I32, PSZ]),
+    "dfx_dual_flow_output_head_taps": (I32, [I32, I32, I32, I32, PSZ, PSZ]),
+    "dfx_dual_flow_output_head": (I32, [I32, I32, I32, I32, P, P, F32, P, P, P, P, P, P, SZ, P]),
     "dfx_copy_bytes": (I32, [P, P, SZ, P]),
     "dfx_read_bytes": (I32, [P, SZ, P, P]),
     "dfx_fill_bytes": (I32, [P, SZ, U32, P]),

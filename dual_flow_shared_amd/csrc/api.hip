@@ -644,6 +644,91 @@ dfx_status dfx_dual_flow_decode_layer_taps(const dfx_layer_weights *w, const dfx
   DFX_END
 }
 
+namespace {
+
+// Workspace of the output head: normed rows (bf16, the projection's fragment order), fp32
+// logits [F][B][V], the projection's split-K partials, the mixture's per-chunk statistics.
+struct HeadPlan {
+  size_t h, logits, partial, stats, total;
+};
+
+dfx_status head_plan(int32_t F, int32_t B, int32_t H, int32_t V, HeadPlan *hp) {
+  if ((F != 1 && F != 2) || B < 0 || B > 65535) return fail(DFX_EINVAL, "n_flows %d batch %d", F, B);
+  if (H < 32 || H % 32 || H > 16384) return fail(DFX_EUNSUPPORTED, "hidden %d (a multiple of 32, at most 16384)", H);
+  if (V < 16 || V % 16) return fail(DFX_EUNSUPPORTED, "vocab %d is not a positive multiple of 16", V);
+  auto a256 = [](size_t x) { return round_up(x, 256); };
+  HeadPlan p{};
+  const size_t prow = (size_t)(B + 64 / F - 1) / (64 / F) * 64;
+  p.h = a256(prow * H * 2);
+  p.logits = a256((size_t)F * B * V * 4);
+  p.partial = B > 0 ? a256(gemm_plan(F, B, H, V).total()) : 0;
+  p.stats = a256(mixture_stats_bytes(B, V));
+  p.total = p.h + p.logits + p.partial + p.stats;
+  *hp = p;
+  return DFX_OK;
+}
+
+}  // namespace
+
+dfx_status dfx_dual_flow_output_head_workspace_size(int32_t n_flows, int32_t batch, int32_t hidden,
+                                                    int32_t vocab, size_t *bytes) {
+  DFX_BEGIN
+  HeadPlan p;
+  dfx_status st = head_plan(n_flows, batch, hidden, vocab, &p);
+  if (st) return st;
+  if (!bytes) return fail(DFX_EINVAL, "bytes is NULL");
+  *bytes = p.total;
+  return DFX_OK;
+  DFX_END
+}
+
+dfx_status dfx_dual_flow_output_head_taps(int32_t n_flows, int32_t batch, int32_t hidden, int32_t vocab,
+                                          size_t *h_offset, size_t *logits_offset) {
+  DFX_BEGIN
+  HeadPlan p;
+  dfx_status st = head_plan(n_flows, batch, hidden, vocab, &p);
+  if (st) return st;
+  if (!h_offset || !logits_offset) return fail(DFX_EINVAL, "offset pointer is NULL");
+  *h_offset = 0;
+  *logits_offset = p.h;
+  return DFX_OK;
+  DFX_END
+}
+
+dfx_status dfx_dual_flow_output_head(int32_t n_flows, int32_t batch, int32_t hidden, int32_t vocab,
+                                     const float *x, const float *norm_gain, float eps,
+                                     const uint16_t *w_out, const float *uniform_noise,
+                                     int32_t *next_token, float *alpha, float *p_mix, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  DFX_BEGIN
+  HeadPlan p;
+  dfx_status st = head_plan(n_flows, batch, hidden, vocab, &p);
+  if (st) return st;
+  if (!(eps >= 0.f)) return fail(DFX_EINVAL, "eps");
+  if (batch > 0 && (!x || !norm_gain || !w_out || !next_token))
+    return fail(DFX_EINVAL, "x / norm_gain / w_out / next_token is NULL");
+  if (!aligned16(x) || !aligned16(norm_gain) || !aligned16(w_out) || !aligned16(uniform_noise) || !aligned16(p_mix) ||
+      ((uintptr_t)next_token & 3) || ((uintptr_t)alpha & 3))
+    return fail(DFX_EINVAL, "misaligned pointer");
+  if (batch == 0) return DFX_OK;
+  if (!workspace || workspace_bytes < p.total)
+    return fail(DFX_EWORKSPACE, "output head needs %zu workspace bytes, got %zu", p.total, workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char *base = (char *)workspace;
+  uint16_t *h = (uint16_t *)base;
+  float *logits = (float *)(base + p.h);
+  float *partial = (float *)(base + p.h + p.logits);
+  float *stats = (float *)(base + p.h + p.logits + p.partial);
+  dfx_status r = hip_status(launch_rmsnorm(n_flows * batch, hidden, x, norm_gain, eps, h, s, n_flows), "rmsnorm launch");
+  if (r) return r;
+  // one pass over the shared vocabulary matrix for both flows' rows
+  if ((r = run_linear_parts(n_flows, batch, hidden, vocab, 2, h, w_out, 1, 0, logits, nullptr, nullptr, partial, s)))
+    return r;
+  return hip_status(launch_mixture(n_flows, batch, vocab, logits, uniform_noise, stats, next_token, alpha, p_mix, s),
+                    "mixture launch");
+  DFX_END
+}
+
 dfx_status dfx_copy_bytes(void *dst, const void *src, size_t bytes, void *stream) {
   DFX_BEGIN
   if (bytes % 16 || !aligned16(dst) || !aligned16(src) || (bytes && (!dst || !src)))

@@ -208,6 +208,9 @@ hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float
 hipError_t launch_embed_norm(int32_t n_flows, int32_t batch, int32_t dim, const int32_t *tokens,
                              int32_t vocab, const uint16_t *embed0, const uint16_t *embed1,
                              const float *gain, float eps, float *x, uint16_t *h1, hipStream_t s);
+size_t mixture_stats_bytes(int32_t batch, int32_t vocab);
+hipError_t launch_mixture(int32_t n_flows, int32_t batch, int32_t vocab, const float *logits, const float *noise,
+                          float *stats, int32_t *token, float *alpha, float *p_mix, hipStream_t s);
 hipError_t launch_swiglu(int32_t n_flows, int32_t rows, int32_t dim, const float *gu,
                          const float *b, uint16_t *out, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);

@@ -340,6 +340,51 @@ dfx_status dfx_dual_flow_decode_layer_taps(const dfx_layer_weights *w, const dfx
                                            struct dfx_layer_taps *taps);
 
 /*
+ * The shared output head and the mixture of the two flows' predictions (Sintesi Tecnica:
+ * Dual-Flow Transformers, "Architettura Core": both flows share the output matrix;
+ * "Meccanismi Chiave", mixture objective: the prediction mixes the flows' distributions with
+ * a weight alpha_t on the primary that follows the primary's collision probability and is
+ * never below one half):
+ *   h_f       = bf16(rmsnorm(x_f) * norm_gain)               (one gain for both flows)
+ *   logits_f  = h_f W_out^T                                   (one pass over W_out, both rows)
+ *   p_f       = softmax(logits_f)
+ *   c         = sum_i p_0,i^2                                 (collision probability)
+ *   alpha     = (1 + c) / 2          -- the pages give no formula; this is the reading taken:
+ *                                       monotone in c, 1/2 only as c -> 0, 1 for a certain primary
+ *   p_mix     = alpha p_0 + (1 - alpha) p_1                   (n_flows = 1: alpha = 1, p_mix = p_0)
+ *   token     = argmax_i p_mix,i                              (uniform_noise NULL: greedy)
+ *             = argmax_i log p_mix,i - log(-log u_i)          (u = uniform_noise: a Gumbel-max
+ *                                                              draw from p_mix)
+ * Ties go to the lowest index. Softmax, mixture and argmax run in fp32.
+ *  x             device fp32 [n_flows][batch][hidden]: the residual rows after the last layer.
+ *  norm_gain     device fp32 [hidden]. hidden: a multiple of 32, at most 16384.
+ *  w_out         device bf16 [vocab][hidden] in DFX_W_PACKED layout; vocab a multiple of 16.
+ *  uniform_noise device fp32 [batch][vocab] with values in (0, 1), or NULL (greedy). The
+ *                library draws no random numbers.
+ *  next_token    device int32 [batch], output.
+ *  alpha         device fp32 [batch], output, or NULL.
+ *  p_mix         device fp32 [batch][vocab], output, or NULL.
+ *  workspace     >= dfx_dual_flow_output_head_workspace_size bytes, no initial contents; after
+ *                the call it holds h at byte h_offset (the activation fragment order of
+ *                dfx_dual_flow_decode_layer_taps, hidden columns) and the fp32 logits
+ *                [n_flows][batch][vocab] at logits_offset (dfx_dual_flow_output_head_taps,
+ *                host-only). Calls sharing a workspace must not overlap.
+ * x, norm_gain, w_out, uniform_noise and p_mix are 16-byte aligned. The call allocates
+ * nothing and never synchronizes.
+ */
+dfx_status dfx_dual_flow_output_head_workspace_size(int32_t n_flows, int32_t batch, int32_t hidden,
+                                                    int32_t vocab, size_t *bytes);
+
+dfx_status dfx_dual_flow_output_head_taps(int32_t n_flows, int32_t batch, int32_t hidden, int32_t vocab,
+                                          size_t *h_offset, size_t *logits_offset);
+
+dfx_status dfx_dual_flow_output_head(int32_t n_flows, int32_t batch, int32_t hidden, int32_t vocab,
+                                     const float *x, const float *norm_gain, float eps,
+                                     const uint16_t *w_out, const float *uniform_noise,
+                                     int32_t *next_token, float *alpha, float *p_mix, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
  * Measurement helpers (not part of the method): a plain device copy of
  * `bytes` (multiple of 16, both pointers 16-byte aligned) used to calibrate
  * hardware traffic counters, a read of `bytes` (achievable read bandwidth;

@@ -21,7 +21,7 @@ def declared():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = _abi.lib()
     names = declared()
-    assert len(names) == 18
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, n
@@ -204,3 +204,28 @@ def test_step_rejects():
     assert call(wb=n.value - 1) == 3
     ws[1].hidden = 512
     assert lib.dfx_dual_flow_decode_step_workspace_size(ws, ks, 2, 4, 2, 200, ctypes.byref(n)) == 1
+
+
+def test_output_head_plan_and_rejects():
+    lib = _abi.lib()
+    n, h, lg = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    for F, B, H, V in ((2, 32, 4096, 128256), (1, 1, 64, 16), (2, 40, 256, 1040)):
+        assert lib.dfx_dual_flow_output_head_workspace_size(F, B, H, V, ctypes.byref(n)) == 0
+        assert lib.dfx_dual_flow_output_head_taps(F, B, H, V, ctypes.byref(h), ctypes.byref(lg)) == 0
+        rows = -(-B // (64 // F)) * 64
+        assert h.value == 0 and lg.value >= rows * H * 2 and lg.value % 256 == 0
+        assert lg.value + F * B * V * 4 <= n.value
+    assert lib.dfx_dual_flow_output_head_workspace_size(3, 4, 64, 64, ctypes.byref(n)) == 1
+    assert lib.dfx_dual_flow_output_head_workspace_size(2, 4, 48, 64, ctypes.byref(n)) == 2    # hidden % 32
+    assert lib.dfx_dual_flow_output_head_workspace_size(2, 4, 64, 24, ctypes.byref(n)) == 2    # vocab % 16
+    assert lib.dfx_dual_flow_output_head_workspace_size(2, 70000, 64, 64, ctypes.byref(n)) == 1
+    assert lib.dfx_dual_flow_output_head_workspace_size(2, 4, 64, 64, None) == 1
+    assert lib.dfx_dual_flow_output_head_workspace_size(2, 4, 64, 64, ctypes.byref(n)) == 0
+    need = n.value
+    call = lambda x=FAKE, tok=FAKE, noise=None, ws=FAKE, wb=need, eps=1e-5: lib.dfx_dual_flow_output_head(
+        2, 4, 64, 64, x, FAKE, eps, FAKE, noise, tok, None, None, ws, wb, None)
+    assert call(ws=None) == 3 and "workspace" in lib.dfx_last_error().decode()
+    assert call(wb=need - 1) == 3
+    assert call(x=None) == 1 and call(tok=None) == 1
+    assert call(x=FAKE + 4) == 1 and call(noise=FAKE + 8) == 1 and call(tok=FAKE + 2) == 1
+    assert call(eps=-1.0) == 1
