@@ -1,6 +1,7 @@
 """Benchmark of the dual-flow decode step on one MI355X.
 
-python bench.py [--steps K] [--warmup W] [--workload layer|attn-b16|attn-ragged|attn-long|attn-fp32]
+python bench.py [--steps K] [--warmup W]
+                [--workload layer|attn-b16|attn-ragged|attn-long|attn-fp32|step|head]
 
 A step of the default workload is one full dual-flow decode layer (both flows, batch
 32, context 8192, hidden 4096, 32/8 heads x 128, SwiGLU 14336, paged bf16 cache of
@@ -13,6 +14,10 @@ position for all 32 sequences of both flows).
 Also measured in the same run: the dominant kernel (the dual-query attention call)
 timed with HIP events on the stream it runs on, its algorithmic HBM bytes, and the
 CPU oracle timed on the host cores (a reported baseline, not a target).
+
+`step` times a whole decode step of a layer stack (token ids -> embeddings -> layers ->
+shared output head -> next token), eagerly and as a HIP-graph replay; `head` the output
+head alone (final norm, shared vocabulary projection, mixture, greedy token).
 """
 import argparse
 import hashlib
@@ -34,8 +39,10 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="layer",
-                   choices=["layer", "attn-b16", "attn-ragged", "attn-long", "attn-fp32", "step"])
+                   choices=["layer", "attn-b16", "attn-ragged", "attn-long", "attn-fp32", "step", "head"])
     p.add_argument("--layers", type=int, default=8, help="layers of the 'step' workload")
+    p.add_argument("--vocab", type=int, default=128256,
+                   help="vocabulary of the 'step' and 'head' workloads (0: the step ends at the last layer)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--splits", type=int, default=0, help="attention context splits (0 = plan)")
     p.add_argument("--kernel-reps", type=int, default=20)
@@ -134,6 +141,8 @@ def main():
     extra = {}
     if args.workload == "step":
         return bench_step(args)
+    if args.workload == "head":
+        return bench_head(args)
     if args.copy_calibration:
         n = args.copy_calibration - args.copy_calibration % 16
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -284,7 +293,9 @@ def bench_step(args):
     import dual_flow_shared_amd as dfx
     torch.cuda.set_device(0)
     gen_ = torch.Generator(device="cuda").manual_seed(2024)
-    B, H, Hq, Hkv, D, I, ctx_len, bs, vocab = 32, 4096, 32, 8, 128, 14336, 8192, 16, 32000
+    B, H, Hq, Hkv, D, I, ctx_len, bs = 32, 4096, 32, 8, 128, 14336, 8192, 16
+    vocab = args.vocab if args.vocab > 0 else 32000
+    with_head = args.vocab > 0
     nl = args.layers
 
     def randn(*shape, std=1.0):
@@ -312,9 +323,18 @@ def bench_step(args):
     out = torch.empty(2, B, H, dtype=torch.float32, device="cuda")
     ws = dfx.Workspace()
     ws.get(dfx.step_workspace_size(layers, caches, B, 2, ctx_len))
+    hws = dfx.Workspace()
+    if with_head:
+        w_out = dfx.pack_weight(randn(vocab, H, std=0.02))
+        g_out = gains(H)
+        hws.get(dfx.output_head_workspace_size(2, B, H, vocab))
 
     def step():
         dfx.dual_flow_decode_step(tokens, e1, e2, layers, caches, ctx, ctx_len, out=out, workspace=ws)
+        if with_head:
+            # greedy next token of the mixture, fed back as the next step's input
+            nxt, _, _ = dfx.output_head(out, g_out, 1e-5, w_out, workspace=hws)
+            tokens.copy_(nxt)
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -336,20 +356,65 @@ def bench_step(args):
     graph_ms = timed(graph.replay, args.steps, stream)
     w_bytes = 2 * (Hq + 2 * Hkv) * D * H + 2 * H * Hq * D + 2 * 2 * I * H + 2 * H * I
     kv_bytes = 2 * B * ctx_len * Hkv * D * 2
-    step_bytes = nl * (w_bytes + kv_bytes) + 2 * B * H * 2
+    step_bytes = nl * (w_bytes + kv_bytes) + 2 * B * H * 2 + (2 * vocab * H if with_head else 0)
     ms = min(eager_ms, graph_ms)
     line = {"metric": "dual-flow multi-layer decode steps/s at batch x ctx", "value": round(1000.0 / graph_ms, 2),
             "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(graph_ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"dual-flow decode step: {nl} layers, batch {B} x context {ctx_len}, hidden {H}, "
-                                   f"{Hq}/{Hkv} heads x {D}, SwiGLU {I}, vocab {vocab}, both flows, HIP-graph replay",
-                       "layers": nl, "batch": B, "context": ctx_len, "hidden": H, "flows": 2},
+                                   f"{Hq}/{Hkv} heads x {D}, SwiGLU {I}, vocab {vocab}, both flows"
+                                   + (", shared output head + mixture + greedy token" if with_head else "")
+                                   + ", HIP-graph replay",
+                       "layers": nl, "batch": B, "context": ctx_len, "hidden": H, "flows": 2,
+                       "vocab": vocab, "output_head": with_head},
             "roofline": {"bound": "hbm", "achieved": round(step_bytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                         "traffic": None, "kernel": "whole step (weights + KV of every layer, read once)",
+                         "traffic": None,
+                         "kernel": "whole step (weights + KV of every layer, and the output matrix, read once)",
                          "bytes_per_launch": int(step_bytes)},
             "cpu_baseline": None, "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
             "tokens_per_s": round(B * 1000.0 / graph_ms, 1), "ms_per_layer": round(graph_ms / nl, 4)}
+    print(json.dumps(line))
+
+
+def bench_head(args):
+    """The shared output head alone: final norm, one pass over a [vocab][4096] bf16 matrix for
+    both flows' rows at batch 32, the mixture and the greedy token (synthetic GPU-drawn inputs:
+    W_out ~ N(0, 0.02), rows ~ N(0, 1)). The timed launches read the whole matrix each time; at
+    1 GiB it is four times the last-level cache, so no launch finds it cached."""
+    import torch
+
+    import dual_flow_shared_amd as dfx
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cuda").manual_seed(77)
+    B, F, H, V = 32, 2, 4096, args.vocab
+    x = torch.randn(F, B, H, generator=g, device="cuda")
+    gain = torch.rand(H, generator=g, device="cuda") * 0.2 + 0.9
+    w = dfx.pack_weight((torch.randn(V, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16))
+    ws = dfx.Workspace()
+    ws.get(dfx.output_head_workspace_size(F, B, H, V))
+    stream = torch.cuda.current_stream()
+
+    def call():
+        dfx.output_head(x, gain, 1e-5, w, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = timed(call, args.steps, stream)
+    alg = 2 * V * H + F * B * H * 4 + 4 * H + B * 8     # W_out, rows, gain, token + alpha
+    gbps = alg / (ms * 1e-3) / 1e9
+    line = {"metric": "dual-flow output head (shared vocab projection + mixture) tokens/s", "value": round(B * 1000.0 / ms, 1),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"shared output head: batch {B}, both flows, hidden {H}, vocab {V}, "
+                                   "final RMSNorm + projection + softmax mixture + greedy token",
+                       "batch": B, "hidden": H, "vocab": V, "flows": F},
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "kernel": "whole head call (5 launches); algorithmic bytes = W_out + rows + gain + outputs",
+                         "bytes_per_launch": int(alg)},
+            "cpu_baseline": None}
     print(json.dumps(line))
 
 
