@@ -29,6 +29,7 @@ TID_G1, TID_G2, TID_B, TID_C = 17, 18, 19, 20
 TID_LIN_X, TID_LIN_W, TID_LIN_CPL, TID_LIN_RES = 21, 22, 23, 24
 TID_TOK, TID_E1, TID_E2 = 31, 32, 33
 TID_HX, TID_HG, TID_WOUT, TID_NOISE = 41, 42, 43, 44
+TID_MX, TID_MG, TID_WR, TID_WEGU, TID_WED, TID_MB, TID_MC = 51, 52, 53, 54, 55, 56, 57
 
 
 def stream(seed: int, tid: int, *idx: int) -> np.random.Generator:
@@ -337,6 +338,39 @@ def head_case(seed: int, n_flows: int, batch: int, hidden: int, vocab: int, w_st
     u = stream(seed, TID_NOISE).random((batch, vocab), dtype=np.float32)
     u[u <= 0] = np.float32(np.finfo(np.float32).tiny)
     return HeadCase(seed, eps, x, g, w, u)
+
+
+@dataclass
+class MoeCase:
+    """Inputs of the mixture-of-experts MLP block: residual rows of both flows, the norm gain,
+    the shared router, every expert's gate/up and down matrices and the coupling vectors."""
+    seed: int
+    eps: float
+    x: np.ndarray          # float32 [2][B][hidden]
+    gain: np.ndarray       # float32 [hidden]
+    w_router: np.ndarray   # uint16 [E][hidden]
+    w_gate_up: np.ndarray  # uint16 [E][2I][hidden]: gate rows, then up rows
+    w_down: np.ndarray     # uint16 [E][hidden][I]
+    b: Optional[np.ndarray]  # float32 [I] or None
+    c: Optional[np.ndarray]  # float32 [hidden] or None
+
+
+def moe_case(seed: int, batch: int, hidden: int, num_experts: int, intermediate: int,
+             w_std: float = 0.02, router_std: float = 0.02, couple: bool = True, eps: float = 1e-5,
+             workers: Optional[int] = None) -> MoeCase:
+    """Rows ~ N(0, 1), gain ~ U(0.9, 1.1), expert matrices ~ N(0, w_std) and the router ~
+    N(0, router_std) in bf16 (expert e's matrices from sub-streams keyed by e), coupling
+    vectors ~ U(-1, 1)."""
+    workers = workers or _workers()
+    E, I = num_experts, intermediate
+    x = _normal(seed, TID_MX, (), (2, batch, hidden))
+    g = _uniform(seed, TID_MG, (), (hidden,), 0.9, 1.1)
+    wr = _bf16_matrix(seed, TID_WR, E, hidden, router_std, workers)
+    wgu = np.stack([_bf16_matrix(seed * 1000 + e, TID_WEGU, 2 * I, hidden, w_std, workers) for e in range(E)])
+    wd = np.stack([_bf16_matrix(seed * 1000 + e, TID_WED, hidden, I, w_std, workers) for e in range(E)])
+    b = _uniform(seed, TID_MB, (), (I,), -1.0, 1.0) if couple else None
+    c = _uniform(seed, TID_MC, (), (hidden,), -1.0, 1.0) if couple else None
+    return MoeCase(seed, eps, x, g, wr, wgu, wd, b, c)
 
 
 def config_attention(idx: int, workers: Optional[int] = None, **over) -> AttnCase:

@@ -28,9 +28,14 @@ Functions and their pins (tests/test_oracle_*.py):
   head.softmax / mixture /   -- torch softmax and argmax; alpha in [1/2, 1], certain primary
        next_token / output_head  -> alpha = 1, flat -> (1 + 1/V) / 2, monotone; Gumbel-max
                                frequencies; torch linear for the projection
+  moe.route / moe_mlp        -- torch topk + softmax; equal experts = the dense SwiGLU block
+                               composed from the pinned primitives (with b, c and k2 > k1);
+                               aux reuses the primary's choice; primary blind to the aux row
 The placement of the b and c coupling vectors is a reading of the pages (they
 name the levels, not the formula); it is pinned only by the identities above:
 "parity unpinned" beyond this reading. So is the mixture weight alpha_t = (1 + c_t) / 2
-(the pages fix only that it follows the primary's collision probability and stays >= 1/2).
+(the pages fix only that it follows the primary's collision probability and stays >= 1/2),
+and so are the router-replay readings of moe.py (shared router, the auxiliary's top-k2 taken
+from the primary's ranking, softmax over the selected experts, b on shared experts only).
 """
-from . import numerics, attention, linear, cache, layer, step, head  # noqa: F401
+from . import numerics, attention, linear, cache, layer, step, head, moe  # noqa: F401
