@@ -13,13 +13,14 @@ from typing import Optional
 import torch
 
 from ._abi import (DFX_BF16, DFX_F32, DFX_W_PACKED, DFX_W_ROW_MAJOR, DfxError, KVCacheStruct,
-                   LayerTapsStruct, LayerWeightsStruct, check, lib)
+                   LayerTapsStruct, LayerWeightsStruct, MoeTapsStruct, MoeWeightsStruct, check, lib)
 
 __all__ = ["DfxError", "KVCache", "LayerWeights", "decode_attn", "decode_attn_plan",
            "kv_append_primary", "grouped_linear", "pack_weight", "rmsnorm", "swiglu_couple",
            "dual_flow_decode_layer", "layer_workspace_size", "copy_bytes", "read_bytes", "fill_bytes",
            "layer_taps", "dual_flow_decode_step", "step_workspace_size", "output_head",
-           "output_head_workspace_size", "output_head_taps", "Workspace", "version"]
+           "output_head_workspace_size", "output_head_taps", "MoeWeights", "moe_mlp", "moe_workspace_size",
+           "moe_taps", "Workspace", "version"]
 
 
 def version() -> int:
@@ -387,6 +388,71 @@ def output_head(x: torch.Tensor, norm_gain: torch.Tensor, eps: float, w_out_pack
                                           _ptr(_contig(w_out_packed, "w_out_packed")), _ptr(uniform_noise),
                                           _ptr(tok), _ptr(alpha), _ptr(p_mix), _ptr(buf), need, _stream(stream)))
     return tok, alpha, p_mix
+
+
+@dataclass
+class MoeWeights:
+    """Device weights of a mixture-of-experts MLP block: router bf16 [E][hidden] row-major;
+    per-expert gate/up [E][2I][hidden] and down [E][hidden][I] bf16 in packed fragment order
+    (``MoeWeights.from_row_major``); vectors fp32."""
+    norm_gain: torch.Tensor
+    w_router: torch.Tensor
+    w_gate_up: torch.Tensor
+    w_down: torch.Tensor
+    top_k_primary: int
+    top_k_aux: int
+    eps: float = 1e-5
+    couple_b: Optional[torch.Tensor] = None
+    couple_c: Optional[torch.Tensor] = None
+
+    @classmethod
+    def from_row_major(cls, norm_gain, w_router, w_gate_up, w_down, top_k_primary, top_k_aux, eps=1e-5,
+                       couple_b=None, couple_c=None) -> "MoeWeights":
+        """Pack every expert's row-major matrices once (dfx_pack_weight per expert)."""
+        gu = torch.stack([pack_weight(w_gate_up[e]) for e in range(w_gate_up.shape[0])])
+        dn = torch.stack([pack_weight(w_down[e]) for e in range(w_down.shape[0])])
+        return cls(norm_gain, _contig(w_router, "w_router"), gu, dn, top_k_primary, top_k_aux, eps,
+                   couple_b, couple_c)
+
+    def struct(self) -> MoeWeightsStruct:
+        s = MoeWeightsStruct()
+        s.num_experts, s.hidden, s.intermediate = self.w_down.shape
+        s.top_k_primary, s.top_k_aux, s.rms_eps = self.top_k_primary, self.top_k_aux, self.eps
+        for name in ("norm_gain", "w_router", "w_gate_up", "w_down", "couple_b", "couple_c"):
+            t = getattr(self, name)
+            setattr(s, name, None if t is None else _contig(t, name).data_ptr())
+        return s
+
+
+def moe_workspace_size(weights: MoeWeights, batch: int, n_flows: int) -> int:
+    n = ctypes.c_size_t()
+    w = weights.struct()
+    check(lib().dfx_dual_flow_moe_mlp_workspace_size(ctypes.byref(w), batch, n_flows, ctypes.byref(n)))
+    return n.value
+
+
+def moe_taps(weights: MoeWeights, batch: int, n_flows: int) -> dict:
+    """Byte offsets of the MoE block's intermediates in its workspace (include/dfx.h)."""
+    t = MoeTapsStruct()
+    w = weights.struct()
+    check(lib().dfx_dual_flow_moe_mlp_taps(ctypes.byref(w), batch, n_flows, ctypes.byref(t)))
+    return {name: getattr(t, name) for name, _ in t._fields_}
+
+
+def moe_mlp(x: torch.Tensor, weights: MoeWeights, workspace: Optional[Workspace] = None,
+            stream=None) -> torch.Tensor:
+    """The mixture-of-experts MLP block with router replay, in place on x [F][B][hidden] fp32."""
+    x = _contig(x, "x")
+    if x.dim() != 3 or x.dtype != torch.float32:
+        raise ValueError("x must be fp32 [n_flows][batch][hidden]")
+    F, B, H = x.shape
+    w = weights.struct()
+    if w.hidden != H:
+        raise ValueError("x and the weights disagree on hidden")
+    need = moe_workspace_size(weights, B, F)
+    buf = _workspace(workspace, x.device, "moe").get(need)
+    check(lib().dfx_dual_flow_moe_mlp(ctypes.byref(w), B, F, _ptr(x), _ptr(buf), need, _stream(stream)))
+    return x
 
 
 def copy_bytes(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

@@ -40,7 +40,19 @@ class LayerTapsStruct(ctypes.Structure):
                 ("h2", ctypes.c_size_t), ("inter", ctypes.c_size_t)]
 
 
+class MoeWeightsStruct(ctypes.Structure):
+    _fields_ = [("hidden", I32), ("num_experts", I32), ("intermediate", I32), ("top_k_primary", I32),
+                ("top_k_aux", I32), ("rms_eps", F32), ("norm_gain", P), ("w_router", P), ("w_gate_up", P),
+                ("w_down", P), ("couple_b", P), ("couple_c", P)]
+
+
+class MoeTapsStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("h", "logits", "ids", "weights", "counts", "seqs", "inter",
+                                               "inter_stride")]
+
+
 KVP = ctypes.POINTER(KVCacheStruct)
+MWP = ctypes.POINTER(MoeWeightsStruct)
 LWP = ctypes.POINTER(LayerWeightsStruct)
 PSZ = ctypes.POINTER(ctypes.c_size_t)
 PI32 = ctypes.POINTER(ctypes.c_int32)
@@ -64,6 +76,9 @@ SIGNATURES = {
     "dfx_dual_flow_output_head_workspace_size": (I32, [I32, I32, I32, I32, PSZ]),
     "dfx_dual_flow_output_head_taps": (I32, [I32, I32, I32, I32, PSZ, PSZ]),
     "dfx_dual_flow_output_head": (I32, [I32, I32, I32, I32, P, P, F32, P, P, P, P, P, P, SZ, P]),
+    "dfx_dual_flow_moe_mlp_workspace_size": (I32, [MWP, I32, I32, PSZ]),
+    "dfx_dual_flow_moe_mlp_taps": (I32, [MWP, I32, I32, ctypes.POINTER(MoeTapsStruct)]),
+    "dfx_dual_flow_moe_mlp": (I32, [MWP, I32, I32, P, P, SZ, P]),
     "dfx_copy_bytes": (I32, [P, P, SZ, P]),
     "dfx_read_bytes": (I32, [P, SZ, P, P]),
     "dfx_fill_bytes": (I32, [P, SZ, U32, P]),

@@ -729,6 +729,145 @@ dfx_status dfx_dual_flow_output_head(int32_t n_flows, int32_t batch, int32_t hid
   DFX_END
 }
 
+namespace {
+
+// Workspace of the MoE block, in this order: normed rows, router logits, selections, expert
+// lists, gathered rows, intermediates, the down projection's tiles.
+struct MoePlan {
+  size_t h, logits, ids, wts, pos, counts, seqs, xg, inter, tiles, total;
+  int max_groups, ksplit, kper;
+};
+
+dfx_status moe_plan(const dfx_moe_weights *w, int32_t B, int32_t F, MoePlan *mp) {
+  if (!w) return fail(DFX_EINVAL, "weights is NULL");
+  if ((F != 1 && F != 2) || B < 0 || B > 65535) return fail(DFX_EINVAL, "n_flows %d batch %d", F, B);
+  const int H = w->hidden, E = w->num_experts, I = w->intermediate;
+  if (H < 32 || H % 32 || H > 16384) return fail(DFX_EUNSUPPORTED, "hidden %d (a multiple of 32, at most 16384)", H);
+  if (E < 1 || E > kMoeMaxExperts) return fail(DFX_EUNSUPPORTED, "num_experts %d (1 .. %d)", E, kMoeMaxExperts);
+  if (I < 32 || I % 32) return fail(DFX_EUNSUPPORTED, "intermediate %d is not a positive multiple of 32", I);
+  const int kcap = E < kMoeMaxK ? E : kMoeMaxK;
+  if (w->top_k_primary < 1 || w->top_k_primary > kcap) return fail(DFX_EINVAL, "top_k_primary %d", w->top_k_primary);
+  if (F == 2 && (w->top_k_aux < 1 || w->top_k_aux > kcap)) return fail(DFX_EINVAL, "top_k_aux %d", w->top_k_aux);
+  if ((size_t)E * ((B + 31) / 32) > 16384) return fail(DFX_EUNSUPPORTED, "num_experts * ceil(batch / 32) above 16384");
+  if (!(w->rms_eps >= 0.f)) return fail(DFX_EINVAL, "rms_eps");
+  if (!w->norm_gain || !w->w_router || !w->w_gate_up || !w->w_down) return fail(DFX_EINVAL, "a weight pointer is NULL");
+  if (!aligned16(w->norm_gain) || !aligned16(w->w_router) || !aligned16(w->w_gate_up) || !aligned16(w->w_down) ||
+      !aligned16(w->couple_b) || !aligned16(w->couple_c))
+    return fail(DFX_EINVAL, "misaligned weight pointer");
+  auto a256 = [](size_t x) { return round_up(x, 256); };
+  MoePlan p{};
+  const int rpg = 64 / F;
+  p.max_groups = B > 0 ? (B + rpg - 1) / rpg : 0;
+  // down projection: about 256 work-groups over all experts
+  const int nks = I / 32, tiles = (H + 127) / 128;
+  int ks = kTargetGemmGroups / (tiles * E);
+  const int max_ks = nks / kMinGemmSteps > 1 ? nks / kMinGemmSteps : 1;
+  ks = std::max(1, std::min(std::min(ks, max_ks), 16));
+  int per = (nks + ks - 1) / ks;
+  if (ks > 1) per = (per + 3) / 4 * 4;
+  p.kper = per;
+  p.ksplit = (nks + per - 1) / per;
+  const size_t rows64 = (size_t)p.max_groups * 64;
+  p.h = a256((size_t)F * B * H * 2);
+  p.logits = a256((size_t)F * B * E * 4);
+  p.ids = p.wts = p.pos = a256((size_t)F * B * kMoeMaxK * 4);
+  p.counts = a256((size_t)E * 4);
+  p.seqs = a256((size_t)E * B * 4);
+  p.xg = a256((size_t)E * rows64 * H * 2);
+  p.inter = a256((size_t)E * rows64 * I * 2);
+  p.tiles = a256((size_t)E * p.ksplit * rows64 * H * 4);
+  p.total = p.h + p.logits + p.ids + p.wts + p.pos + p.counts + p.seqs + p.xg + p.inter + p.tiles;
+  *mp = p;
+  return DFX_OK;
+}
+
+}  // namespace
+
+dfx_status dfx_dual_flow_moe_mlp_workspace_size(const dfx_moe_weights *w, int32_t batch, int32_t n_flows,
+                                                size_t *bytes) {
+  DFX_BEGIN
+  MoePlan p;
+  dfx_status st = moe_plan(w, batch, n_flows, &p);
+  if (st) return st;
+  if (!bytes) return fail(DFX_EINVAL, "bytes is NULL");
+  *bytes = p.total;
+  return DFX_OK;
+  DFX_END
+}
+
+dfx_status dfx_dual_flow_moe_mlp_taps(const dfx_moe_weights *w, int32_t batch, int32_t n_flows,
+                                      dfx_moe_taps *taps) {
+  DFX_BEGIN
+  MoePlan p;
+  dfx_status st = moe_plan(w, batch, n_flows, &p);
+  if (st) return st;
+  if (!taps) return fail(DFX_EINVAL, "taps is NULL");
+  taps->h = 0;
+  taps->logits = p.h;
+  taps->ids = taps->logits + p.logits;
+  taps->weights = taps->ids + p.ids;
+  taps->counts = taps->weights + p.wts + p.pos;
+  taps->seqs = taps->counts + p.counts;
+  taps->inter = taps->seqs + p.seqs + p.xg;
+  taps->inter_stride = (size_t)p.max_groups * 64 * w->intermediate;
+  return DFX_OK;
+  DFX_END
+}
+
+dfx_status dfx_dual_flow_moe_mlp(const dfx_moe_weights *w, int32_t batch, int32_t n_flows, float *x,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  DFX_BEGIN
+  MoePlan p;
+  dfx_status st = moe_plan(w, batch, n_flows, &p);
+  if (st) return st;
+  if (batch == 0) return DFX_OK;
+  if (!x) return fail(DFX_EINVAL, "x is NULL");
+  if (!aligned16(x)) return fail(DFX_EINVAL, "x not 16-byte aligned");
+  if (!workspace || workspace_bytes < p.total)
+    return fail(DFX_EWORKSPACE, "MoE block needs %zu workspace bytes, got %zu", p.total, workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  const int F = n_flows, B = batch, H = w->hidden, E = w->num_experts, I = w->intermediate;
+  char *c = (char *)workspace;
+  MoeArgs a{};
+  a.F = F; a.B = B; a.H = H; a.E = E; a.k1 = w->top_k_primary; a.k2 = F == 2 ? w->top_k_aux : 0;
+  a.max_groups = p.max_groups; a.ksplit = p.ksplit;
+  a.h = (const uint16_t *)c;                     c += p.h;
+  a.w_router = w->w_router;
+  a.logits = (float *)c;                          c += p.logits;
+  a.ids = (int32_t *)c;                           c += p.ids;
+  a.wts = (float *)c;                             c += p.wts;
+  a.pos = (int32_t *)c;                           c += p.pos;
+  a.counts = (int32_t *)c;                        c += p.counts;
+  a.seqs = (int32_t *)c;                          c += p.seqs;
+  a.xg = (uint16_t *)c;                           c += p.xg;
+  uint16_t *inter = (uint16_t *)c;                c += p.inter;
+  float *tiles = (float *)c;
+  a.tiles = tiles; a.couple_c = F == 2 ? w->couple_c : nullptr; a.x = x;
+  dfx_status r = hip_status(launch_rmsnorm(F * B, H, x, w->norm_gain, w->rms_eps, (uint16_t *)a.h, s, 0),
+                            "rmsnorm launch");
+  if (r) return r;
+  if ((r = hip_status(launch_moe(kMoeRoute, a, s), "route launch"))) return r;
+  if ((r = hip_status(launch_moe(kMoeLists, a, s), "expert lists launch"))) return r;
+  if ((r = hip_status(launch_moe(kMoeGather, a, s), "gather launch"))) return r;
+  const size_t rows64 = (size_t)p.max_groups * 64;
+  GemmArgs g{};
+  g.n_flows = F; g.rows = B; g.x_packed = 1; g.w_packed = 1;
+  g.expert_rows = a.counts; g.experts = E; g.max_groups = p.max_groups;
+  // gate/up with SwiGLU and the b coupling, per expert
+  g.K = H; g.N = 2 * I; g.x = a.xg; g.w = w->w_gate_up; g.y = inter;
+  g.couple = F == 2 ? w->couple_b : nullptr; g.ksplit = 1; g.kper = H / 32; g.swiglu = 1;
+  g.x_estride = (int64_t)rows64 * H; g.w_estride = (int64_t)2 * I * H; g.y_estride = (int64_t)rows64 * I;
+  if ((r = hip_status(launch_grouped_linear(g, s), "expert gate/up launch"))) return r;
+  // down projection tiles, per expert
+  g.K = I; g.N = H; g.x = inter; g.w = w->w_down; g.y = nullptr; g.couple = nullptr; g.swiglu = 0;
+  g.ksplit = p.ksplit; g.kper = p.kper; g.partial = tiles; g.tiles_only = 1;
+  g.x_estride = (int64_t)rows64 * I; g.w_estride = (int64_t)H * I; g.y_estride = 0;
+  g.p_estride = (int64_t)p.ksplit * rows64 * H;
+  if ((r = hip_status(launch_grouped_linear(g, s), "expert down launch"))) return r;
+  return hip_status(launch_moe(kMoeCombine, a, s), "combine launch");
+  DFX_END
+}
+
 dfx_status dfx_copy_bytes(void *dst, const void *src, size_t bytes, void *stream) {
   DFX_BEGIN
   if (bytes % 16 || !aligned16(dst) || !aligned16(src) || (bytes && (!dst || !src)))

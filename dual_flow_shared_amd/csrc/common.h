@@ -157,6 +157,14 @@ struct GemmArgs {
   // features c.. c+15 with up features I + c..; y receives bf16 silu(gate) * up, flow 1
   // plus couple * flow 0, in the fragment order of xpack_offset with K = I
   int32_t swiglu;
+  // expert mode (blockIdx.z = expert e): the rows of expert e are expert_rows[e] (read on the
+  // device, so an expert with no rows reads none of its weights), at most max_groups groups;
+  // x, w, y and partial of expert e start e * x_estride, w_estride, y_estride, p_estride
+  // elements in, and the partial tiles of an expert use max_groups as their group count
+  // (x bf16 in fragment order; gate/up mode or tiles_only); grid z = experts
+  const int32_t *expert_rows;
+  int32_t experts, max_groups;
+  int64_t x_estride, w_estride, y_estride, p_estride;
 };
 
 // Destination of attention output (flow f, sequence b, column c = head * D + d): rows
@@ -199,6 +207,28 @@ hipError_t launch_grouped_linear(const GemmArgs &g, hipStream_t s);
 hipError_t launch_pack_weight(int32_t N, int32_t K, const uint16_t *w, uint16_t *packed,
                               hipStream_t s);
 hipError_t launch_layer_glue(int which, const LayerGlueArgs &a, hipStream_t s);
+
+// Mixture-of-experts block (router replay). Selections are stored kMoeMaxK per (flow,
+// sequence), ranks past the flow's fan-out hold id -1 and weight 0.
+constexpr int kMoeMaxK = 16;
+constexpr int kMoeMaxExperts = 256;
+enum { kMoeRoute = 0, kMoeLists = 1, kMoeGather = 2, kMoeCombine = 3 };
+struct MoeArgs {
+  int32_t F, B, H, E, k1, k2, max_groups, ksplit;
+  const uint16_t *h;         // bf16 [F][B][H] normed rows, row-major
+  const uint16_t *w_router;  // bf16 [E][H]
+  float *logits;             // [F][B][E]
+  int32_t *ids;              // [F][B][kMoeMaxK]
+  float *wts;                // [F][B][kMoeMaxK]
+  int32_t *pos;              // [F][B][kMoeMaxK]: row of the sequence in its expert's list
+  int32_t *counts;           // [E]
+  int32_t *seqs;             // [E][B]
+  uint16_t *xg;              // [E][max_groups * 64 * H] bf16, fragment order
+  const float *tiles;        // [E][ksplit][max_groups][64][H]
+  const float *couple_c;     // [H] or NULL
+  float *x;                  // [F][B][H] residual rows, updated in place
+};
+hipError_t launch_moe(int which, const MoeArgs &a, hipStream_t s);
 // packed_flows > 0: y in the fragment order of xpack_offset for that many flows (rows =
 // flows x batch); 0: row-major.
 hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,

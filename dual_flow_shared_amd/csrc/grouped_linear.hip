@@ -92,9 +92,23 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
   const int tile = blockIdx.x, ks = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
-  const int F = p.n_flows, rows = p.rows, K = p.K, N = p.N;
+  const int F = p.n_flows, K = p.K, N = p.N;
   const int rpg = 64 / F;  // rows of each flow in one group
+  int rows = p.rows;
+  const void *px = p.x;
+  const uint16_t *pw = p.w;
+  void *py = p.y;
+  float *ppart = p.partial;
+  if (p.expert_rows) {
+    const int e = blockIdx.z;
+    rows = min(p.expert_rows[e], p.max_groups * rpg);
+    px = (const uint16_t *)p.x + e * p.x_estride;
+    pw = p.w + e * p.w_estride;
+    py = (uint16_t *)p.y + e * p.y_estride;
+    ppart = p.partial ? p.partial + e * p.p_estride : nullptr;
+  }
   const int groups = (rows + rpg - 1) / rpg;
+  const int tgroups = p.expert_rows ? p.max_groups : groups;  // group count of the tile layout
   const int nks = K / 32, ng = N / 16;
   const int kbeg = ks * p.kper;
   const int nk = min(p.kper, nks - kbeg);  // >= 1: the plan leaves no split empty
@@ -108,11 +122,11 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
   const uint16_t *wa, *wb;
   int64_t wstep;
   if constexpr (WPACKED) {  // [K/32][N/16][64][8]: the column groups of a k-step are adjacent
-    wa = p.w + (((int64_t)kbeg * ng + cga) * 64 + lane) * 8;
+    wa = pw + (((int64_t)kbeg * ng + cga) * 64 + lane) * 8;
     wb = wa + (int64_t)(cgb - cga) * 512;
     wstep = (int64_t)ng * 512;
   } else {                  // row-major: 64 B of each of 16 rows per k-step
-    wa = p.w + (int64_t)(16 * cga + n) * K + 8 * j + 32 * kbeg;
+    wa = pw + (int64_t)(16 * cga + n) * K + 8 * j + 32 * kbeg;
     wb = wa + (int64_t)16 * (cgb - cga) * K;
     wstep = 32;
   }
@@ -147,7 +161,7 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
       da = __builtin_nontemporal_load((const u32x4 *)(wa + o));
       db = __builtin_nontemporal_load((const u32x4 *)(wb + o));
     };
-    auto xload = [&](int kk, XFrag<XF32> &d) { d.load(p.x, xoff + (int64_t)min(kk, nk - 1) * xstep); };
+    auto xload = [&](int kk, XFrag<XF32> &d) { d.load(px, xoff + (int64_t)min(kk, nk - 1) * xstep); };
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (u < kPipeX) xload(u, xr[u]);
@@ -204,7 +218,7 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = fmaf(c[i], pr[i], v[i]);
         }
-        *(u32x2 *)((uint16_t *)p.y + xpack_offset(F, f, rr, col, I)) =
+        *(u32x2 *)((uint16_t *)py + xpack_offset(F, f, rr, col, I)) =
             u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
       continue;
@@ -217,7 +231,7 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
         // partial tile [ks][grp][64 rows][N]
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          float *dst = p.partial + (((int64_t)ks * groups + grp) * 64 + 16 * nb + n) * N + col;
+          float *dst = ppart + (((int64_t)ks * tgroups + grp) * 64 + 16 * nb + n) * N + col;
           *(f32x4 *)dst = acc[h][nb];
         }
         continue;
@@ -266,7 +280,8 @@ __global__ void __launch_bounds__(256) grouped_linear_reduce_kernel(GemmArgs p) 
 }
 
 hipError_t launch_grouped_linear(const GemmArgs &g, hipStream_t s) {
-  const dim3 grid(g.swiglu ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128, g.ksplit), block(256);
+  const dim3 grid(g.swiglu ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128, g.ksplit, g.expert_rows ? g.experts : 1),
+      block(256);
 #define DFX_GL(XF, XP, WP) grouped_linear_kernel<XF, XP, WP><<<grid, block, 0, s>>>(g)
   if (g.x_packed) {
     if (g.w_packed) DFX_GL(false, true, true); else DFX_GL(false, true, false);
@@ -277,7 +292,7 @@ hipError_t launch_grouped_linear(const GemmArgs &g, hipStream_t s) {
   }
 #undef DFX_GL
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || g.ksplit == 1 || g.tiles_only || g.swiglu) return e;
+  if (e != hipSuccess || g.ksplit == 1 || g.tiles_only || g.swiglu || g.expert_rows) return e;
   const int rpg = 64 / g.n_flows;
   const int groups = (g.rows + rpg - 1) / rpg;
   const int64_t threads = (int64_t)groups * rpg * (g.N / 4);

@@ -385,6 +385,71 @@ dfx_status dfx_dual_flow_output_head(int32_t n_flows, int32_t batch, int32_t hid
                                      size_t workspace_bytes, void *stream);
 
 /*
+ * Mixture-of-experts MLP block with router replay (Sintesi Tecnica: Dual-Flow Transformers,
+ * "Meccanismi Chiave", router replay: the auxiliary flow uses the experts chosen by the
+ * primary's router with mixture weights of its own; "Contributi Chiave" item 3: the two
+ * flows' expert fan-outs are set independently). In place on the residual rows x:
+ *   h_f      = bf16(rmsnorm(x_f) * norm_gain)
+ *   l_f      = h_f W_router^T                     (fp32; one shared router for both flows)
+ *   ranking  = experts by descending l_0, the lower id first on equal logits
+ *   S_0      = first top_k_primary of the ranking; S_1 = first top_k_aux of the SAME ranking
+ *   w_f,e    = softmax over S_f of l_f            (each flow its own weights)
+ *   i_f,e    = silu(h_f Wg_e^T) * (h_f Wu_e^T);  i_1,e += b * i_0,e  (i_0,e = 0 if e not in S_0);
+ *              rounded to bf16
+ *   m_f      = sum over e in S_f, in ranking order, of w_f,e * (i_f,e Wd_e^T)
+ *   m_1     += c * m_0;   x_f += m_f
+ * (the readings where the pages give no formula: the shared router, the auxiliary's experts as
+ * the head of the primary's ranking, the softmax over the selected experts, b on experts both
+ * flows ran, c on the block output). Every expert used by at least one row is read once for
+ * all rows of both flows that use it; an expert no row uses is not read.
+ */
+typedef struct dfx_moe_weights {
+  int32_t hidden;          /* a multiple of 32, at most 16384 */
+  int32_t num_experts;     /* 1 .. 256 */
+  int32_t intermediate;    /* per expert; a multiple of 32 */
+  int32_t top_k_primary;   /* 1 .. min(num_experts, 16) */
+  int32_t top_k_aux;       /* 1 .. min(num_experts, 16); ignored when n_flows = 1 */
+  float rms_eps;
+  const float *norm_gain;      /* [hidden] */
+  const uint16_t *w_router;    /* bf16 [num_experts][hidden], row-major */
+  const uint16_t *w_gate_up;   /* num_experts packed [2*intermediate][hidden] matrices, back to back */
+  const uint16_t *w_down;      /* num_experts packed [hidden][intermediate] matrices, back to back */
+  const float *couple_b;       /* [intermediate] or NULL */
+  const float *couple_c;       /* [hidden] or NULL */
+} dfx_moe_weights;
+
+/* Byte offsets in the workspace of a completed dfx_dual_flow_moe_mlp call:
+ *   h       bf16 [n_flows][batch][hidden] normed rows, row-major
+ *   logits  fp32 [n_flows][batch][num_experts] router logits
+ *   ids     int32 [n_flows][batch][16] expert ids in ranking order (-1 past the fan-out)
+ *   weights fp32 [n_flows][batch][16] mixture weights (0 past the fan-out)
+ *   counts  int32 [num_experts] sequences using each expert (by either flow)
+ *   seqs    int32 [num_experts][batch] those sequences, ascending
+ *   inter   bf16 intermediates per expert: expert e's row r (flow f, sequence seqs[e][r]) at
+ *           e * inter_stride elements plus the fragment-order offset of
+ *           dfx_dual_flow_decode_layer_taps with K = intermediate (inter_stride in elements).
+ * Host-only: no GPU work. */
+typedef struct dfx_moe_taps {
+  size_t h, logits, ids, weights, counts, seqs, inter, inter_stride;
+} dfx_moe_taps;
+
+dfx_status dfx_dual_flow_moe_mlp_workspace_size(const dfx_moe_weights *w, int32_t batch, int32_t n_flows,
+                                                size_t *bytes);
+
+dfx_status dfx_dual_flow_moe_mlp_taps(const dfx_moe_weights *w, int32_t batch, int32_t n_flows,
+                                      dfx_moe_taps *taps);
+
+/*
+ *  x          device fp32 [n_flows][batch][hidden], 16-byte aligned, updated in place.
+ *  batch      0 .. 65535, with num_experts * ceil(batch / 32) <= 16384.
+ *  workspace  >= dfx_dual_flow_moe_mlp_workspace_size bytes, no initial contents.
+ * All vectors and matrices 16-byte aligned. The call allocates nothing and never synchronizes;
+ * calls sharing a workspace must not overlap.
+ */
+dfx_status dfx_dual_flow_moe_mlp(const dfx_moe_weights *w, int32_t batch, int32_t n_flows, float *x,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Measurement helpers (not part of the method): a plain device copy of
  * `bytes` (multiple of 16, both pointers 16-byte aligned) used to calibrate
  * hardware traffic counters, a read of `bytes` (achievable read bandwidth;

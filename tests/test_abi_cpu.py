@@ -21,7 +21,7 @@ def declared():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = _abi.lib()
     names = declared()
-    assert len(names) == 21
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, n
@@ -229,3 +229,46 @@ def test_output_head_plan_and_rejects():
     assert call(x=None) == 1 and call(tok=None) == 1
     assert call(x=FAKE + 4) == 1 and call(noise=FAKE + 8) == 1 and call(tok=FAKE + 2) == 1
     assert call(eps=-1.0) == 1
+
+
+def moe_weights(H=4096, E=8, I=14336, k1=2, k2=2):
+    w = _abi.MoeWeightsStruct()
+    w.hidden, w.num_experts, w.intermediate, w.top_k_primary, w.top_k_aux, w.rms_eps = H, E, I, k1, k2, 1e-5
+    for f in ("norm_gain", "w_router", "w_gate_up", "w_down"):
+        setattr(w, f, FAKE)
+    return w
+
+
+def test_moe_plan_and_rejects():
+    lib = _abi.lib()
+    n, t = ctypes.c_size_t(), _abi.MoeTapsStruct()
+    for F, B, E, I in ((2, 32, 8, 14336), (1, 32, 8, 14336), (2, 40, 2, 128), (2, 3, 16, 2048)):
+        w = moe_weights(H=256 if I < 4096 else 4096, E=E, I=I)
+        H = w.hidden
+        assert lib.dfx_dual_flow_moe_mlp_workspace_size(ctypes.byref(w), B, F, ctypes.byref(n)) == 0
+        assert lib.dfx_dual_flow_moe_mlp_taps(ctypes.byref(w), B, F, ctypes.byref(t)) == 0
+        groups = -(-B // (64 // F))
+        assert t.inter_stride == groups * 64 * I
+        offs = [t.h, t.logits, t.ids, t.weights, t.counts, t.seqs, t.inter]
+        sizes = [F * B * H * 2, F * B * E * 4, F * B * 64, F * B * 64, E * 4, E * B * 4, E * t.inter_stride * 2]
+        assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+        for o, s, nxt in zip(offs, sizes, offs[1:] + [n.value]):
+            assert o + s <= nxt
+    bad = [dict(E=0), dict(E=257), dict(k1=0), dict(k1=17, E=32), dict(k1=9, E=8), dict(k2=0), dict(I=48), dict(H=48)]
+    for kw in bad:
+        w = moe_weights(**kw)
+        assert lib.dfx_dual_flow_moe_mlp_workspace_size(ctypes.byref(w), 4, 2, ctypes.byref(n)) != 0, kw
+    w = moe_weights(k2=0)
+    assert lib.dfx_dual_flow_moe_mlp_workspace_size(ctypes.byref(w), 4, 1, ctypes.byref(n)) == 0   # k2 unused
+    w = moe_weights(E=256)
+    assert lib.dfx_dual_flow_moe_mlp_workspace_size(ctypes.byref(w), 2048, 2, ctypes.byref(n)) == 0
+    assert lib.dfx_dual_flow_moe_mlp_workspace_size(ctypes.byref(w), 2049, 2, ctypes.byref(n)) == 2  # LDS bitmap
+    w = moe_weights()
+    w.w_router = FAKE + 8
+    assert lib.dfx_dual_flow_moe_mlp_workspace_size(ctypes.byref(w), 4, 2, ctypes.byref(n)) == 1
+    w = moe_weights()
+    assert lib.dfx_dual_flow_moe_mlp_workspace_size(ctypes.byref(w), 4, 2, ctypes.byref(n)) == 0
+    assert lib.dfx_dual_flow_moe_mlp(ctypes.byref(w), 4, 2, FAKE, None, 0, None) == 3
+    assert lib.dfx_dual_flow_moe_mlp(ctypes.byref(w), 4, 2, FAKE + 4, FAKE, n.value, None) == 1
+    assert lib.dfx_dual_flow_moe_mlp(ctypes.byref(w), 4, 2, None, FAKE, n.value, None) == 1
+    assert lib.dfx_dual_flow_moe_mlp(None, 4, 2, FAKE, FAKE, n.value, None) == 1
