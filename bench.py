@@ -1,7 +1,7 @@
 """Benchmark of the dual-flow decode step on one MI355X.
 
 python bench.py [--steps K] [--warmup W]
-                [--workload layer|attn-b16|attn-ragged|attn-long|attn-fp32|step|head]
+                [--workload layer|attn-b16|attn-ragged|attn-long|attn-fp32|step|head|moe]
 
 A step of the default workload is one full dual-flow decode layer (both flows, batch
 32, context 8192, hidden 4096, 32/8 heads x 128, SwiGLU 14336, paged bf16 cache of
@@ -17,7 +17,8 @@ CPU oracle timed on the host cores (a reported baseline, not a target).
 
 `step` times a whole decode step of a layer stack (token ids -> embeddings -> layers ->
 shared output head -> next token), eagerly and as a HIP-graph replay; `head` the output
-head alone (final norm, shared vocabulary projection, mixture, greedy token).
+head alone (final norm, shared vocabulary projection, mixture, greedy token); `moe` the
+mixture-of-experts MLP block with router replay.
 """
 import argparse
 import hashlib
@@ -39,7 +40,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="layer",
-                   choices=["layer", "attn-b16", "attn-ragged", "attn-long", "attn-fp32", "step", "head"])
+                   choices=["layer", "attn-b16", "attn-ragged", "attn-long", "attn-fp32", "step", "head", "moe"])
     p.add_argument("--layers", type=int, default=8, help="layers of the 'step' workload")
     p.add_argument("--vocab", type=int, default=128256,
                    help="vocabulary of the 'step' and 'head' workloads (0: the step ends at the last layer)")
@@ -143,6 +144,8 @@ def main():
         return bench_step(args)
     if args.workload == "head":
         return bench_head(args)
+    if args.workload == "moe":
+        return bench_moe(args)
     if args.copy_calibration:
         n = args.copy_calibration - args.copy_calibration % 16
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -415,6 +418,71 @@ def bench_head(args):
                          "kernel": "whole head call (5 launches); algorithmic bytes = W_out + rows + gain + outputs",
                          "bytes_per_launch": int(alg)},
             "cpu_baseline": None}
+    print(json.dumps(line))
+
+
+def bench_moe(args):
+    """The mixture-of-experts MLP block with router replay: batch 32, both flows, hidden 4096,
+    8 experts of intermediate 14336 (a SwiGLU expert of the one-layer workload's MLP shape),
+    primary fan-out 2, auxiliary fan-out 2 (and 4 as a second reading: more decode experts at
+    the same prefill cost), synthetic GPU-drawn weights. Algorithmic bytes: the router, the
+    matrices of every expert some row uses (each read once), the residual rows in and out."""
+    import torch
+
+    import dual_flow_shared_amd as dfx
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cuda").manual_seed(91)
+    B, H, E, I = 32, 4096, 8, 14336
+
+    def randn(*shape, std=0.02):
+        return (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+
+    gain = torch.rand(H, generator=g, device="cuda") * 0.2 + 0.9
+    wr = randn(E, H)
+    gu = torch.stack([dfx.pack_weight(randn(2 * I, H)) for _ in range(E)])
+    dn = torch.stack([dfx.pack_weight(randn(H, I)) for _ in range(E)])
+    bvec = torch.rand(I, generator=g, device="cuda") * 2 - 1
+    cvec = torch.rand(H, generator=g, device="cuda") * 2 - 1
+    x0 = torch.randn(2, B, H, generator=g, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for F, k2 in ((2, 2), (2, 4), (1, 2)):
+        w = dfx.MoeWeights(gain, wr, gu, dn, 2, k2, 1e-5, bvec, cvec)
+        ws = dfx.Workspace()
+        x = x0[:F].clone()
+        dfx.moe_mlp(x, w, workspace=ws)
+        torch.cuda.synchronize()
+        t = dfx.moe_taps(w, B, F)
+        counts = ws.buf[t["counts"]: t["counts"] + 4 * E].view(torch.int32).cpu()
+        used = int((counts > 0).sum())
+
+        def call():
+            x.copy_(x0[:F])
+            dfx.moe_mlp(x, w, workspace=ws)
+
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        ms = timed(call, args.steps, stream)
+        alg = used * 3 * I * H * 2 + E * H * 2 + 2 * F * B * H * 4 + 4 * H
+        res[(F, k2)] = (ms, alg, used)
+    ms, alg, used = res[(2, 2)]
+    gbps = alg / (ms * 1e-3) / 1e9
+    line = {"metric": "dual-flow MoE block (router replay) tokens/s", "value": round(B * 1000.0 / ms, 1),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"MoE MLP block with router replay: batch {B}, both flows, hidden {H}, {E} experts "
+                                   f"x SwiGLU {I}, fan-out primary 2 / auxiliary 2",
+                       "batch": B, "hidden": H, "experts": E, "intermediate": I, "top_k_primary": 2, "top_k_aux": 2},
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "kernel": "whole block call (7 launches, timed with the residual reset copy); algorithmic "
+                                   "bytes = router + used experts' matrices once + rows",
+                         "bytes_per_launch": int(alg), "experts_used": used},
+            "cpu_baseline": None,
+            "aux_fanout_4": {"ms": round(res[(2, 4)][0], 4), "experts_used": res[(2, 4)][2]},
+            "primary_only": {"ms": round(res[(1, 2)][0], 4), "experts_used": res[(1, 2)][2]},
+            "dual_over_single": round(ms / res[(1, 2)][0], 3)}
     print(json.dumps(line))
 
 
