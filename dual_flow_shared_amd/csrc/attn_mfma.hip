@@ -356,6 +356,13 @@ hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s) {
 }
 
 // ---- split merge: O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), lse = M + log2 sum
+// One wave per output row. With up to kMergeBatch splits every partial of the row is loaded
+// in one round trip (indices past the last split re-read it and are masked), together with
+// the context length that decides how many splits hold data; more splits take the same sums
+// in two passes. Either way M is the max over the valid splits and the sums run in split
+// order, so the arithmetic does not depend on the path taken.
+constexpr int kMergeBatch = 8;
+
 template <int D>
 __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs p) {
   constexpr int PER = D / 64;
@@ -364,20 +371,45 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs p) {
   if (row >= rows) return;
   const int Hq = p.num_q_heads;
   const int h = row % Hq, b = (row / Hq) % p.batch, f = row / (Hq * p.batch);
-  const int ctx = min(max(p.ctx[b], 0), p.max_context);
-  const int nvalid = min((ctx + p.chunk - 1) / p.chunk, p.num_splits);
   const int64_t stride = (int64_t)p.n_flows * p.batch * Hq;  // rows per split
-  float M = -INFINITY;
-  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, p.part_lse[s * stride + row]);
-  float L = 0.f, O[PER];
+  const int S = p.num_splits;
+  float M = -INFINITY, L = 0.f, O[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) O[k] = 0.f;
-  for (int s = 0; s < nvalid; ++s) {
-    const float c = exp2f(p.part_lse[s * stride + row] - M);
-    L += c;
-    const float *po = p.part_o + (s * stride + row) * D;
+  int nvalid;
+  if (S <= kMergeBatch) {
+    float lse[kMergeBatch], po[kMergeBatch][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) O[k] += c * po[lane + 64 * k];
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int64_t r = (int64_t)min(u, S - 1) * stride + row;
+      lse[u] = p.part_lse[r];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) po[u][k] = p.part_o[r * D + lane + 64 * k];
+    }
+    const int ctx = min(max(p.ctx[b], 0), p.max_context);
+    nvalid = min((ctx + p.chunk - 1) / p.chunk, S);
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (u < nvalid) M = fmaxf(M, lse[u]);
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (u < nvalid) {
+        const float c = exp2f(lse[u] - M);
+        L += c;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) O[k] += c * po[u][k];
+      }
+  } else {
+    const int ctx = min(max(p.ctx[b], 0), p.max_context);
+    nvalid = min((ctx + p.chunk - 1) / p.chunk, S);
+    for (int s = 0; s < nvalid; ++s) M = fmaxf(M, p.part_lse[s * stride + row]);
+    for (int s = 0; s < nvalid; ++s) {
+      const float c = exp2f(p.part_lse[s * stride + row] - M);
+      L += c;
+      const float *po = p.part_o + (s * stride + row) * D;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) O[k] += c * po[lane + 64 * k];
+    }
   }
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
