@@ -140,7 +140,8 @@ def attention_case(seed: int, batch: int, num_q_heads: int, num_kv_heads: int, h
     (or per (head, head_dim) when ``a_per_head``). Paged pools take a seeded
     permutation of the block ids, each sequence a consecutive slice of it;
     table entries past a sequence's last block and every unreferenced slot are
-    filled with poison (NaN values; a spare poisoned block id in the table).
+    filled with poison (NaN values; a spare poisoned block id in the table). With
+    ``capacity`` every sequence owns the blocks of that many tokens.
     """
     ctx = np.asarray(context_lens, dtype=np.int32).reshape(batch)
     D, Hkv = head_dim, num_kv_heads
@@ -148,7 +149,10 @@ def attention_case(seed: int, batch: int, num_q_heads: int, num_kv_heads: int, h
     el = np.float32 if dtype == "f32" else np.uint16
     fill = (np.float32(np.nan) if dtype == "f32" else np.uint16(BF16_QNAN)) if poison else 0
     if paged:
-        nblk = [-(-int(n) // block_size) for n in ctx]
+        # every sequence owns the blocks of its context, or of ``capacity`` tokens if that is
+        # more (room for appends; those slots hold poison until written)
+        nblk = [max(-(-int(n) // block_size), 0 if capacity is None else -(-capacity // block_size))
+                for n in ctx]
         need = sum(nblk)
         nb = num_blocks if num_blocks is not None else need + 1
         if nb < need:
@@ -260,16 +264,18 @@ class LayerCase:
 def layer_case(seed: int, batch: int, context: int, hidden: int, num_q_heads: int,
                num_kv_heads: int, head_dim: int, intermediate: int, couple: bool = True,
                num_blocks: Optional[int] = None, block_size: int = 16, w_std: float = 0.02,
-               eps: float = 1e-5, workers: Optional[int] = None) -> LayerCase:
+               eps: float = 1e-5, workers: Optional[int] = None,
+               capacity: Optional[int] = None) -> LayerCase:
     """Seeded config of one layer: weights ~ N(0, w_std) bf16, residual rows ~ N(0, 1),
     norm gains ~ U(0.9, 1.1), coupling vectors ~ U(-1, 1); the cache holds
     ``context - 1`` pre-filled tokens per sequence so the step's append makes
-    ``context`` attended positions."""
+    ``context`` attended positions. ``capacity`` (default ``context``) sizes each sequence's
+    blocks, so a prompt chunk can be appended past the pre-filled tokens."""
     workers = workers or _workers()
     D, I, Hq, Hkv = head_dim, intermediate, num_q_heads, num_kv_heads
     cache = attention_case(seed, batch, Hq, Hkv, D, np.full(batch, context - 1, np.int32), "bf16",
                            paged=True, block_size=block_size, num_blocks=num_blocks,
-                           capacity=context, workers=workers)
+                           capacity=capacity or context, workers=workers)
     x = np.stack([_normal(seed, TID_X1, (), (batch, hidden)), _normal(seed, TID_X2, (), (batch, hidden))])
 
     def wmat(tid, n, k):

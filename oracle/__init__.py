@@ -31,6 +31,9 @@ Functions and their pins (tests/test_oracle_*.py):
   moe.route / moe_mlp        -- torch topk + softmax; equal experts = the dense SwiGLU block
                                composed from the pinned primitives (with b, c and k2 > k1);
                                aux reuses the primary's choice; primary blind to the aux row
+  prefill.prefill_attention  -- torch causal SDPA (GQA, cached prefix); prefill_layer = the
+       / prefill_layer /       pinned decode layer token by token; chunking invariance; the
+       prefill_step            aux started at the last prompt position = aux at every position
 The placement of the b and c coupling vectors is a reading of the pages (they
 name the levels, not the formula); it is pinned only by the identities above:
 "parity unpinned" beyond this reading. So is the mixture weight alpha_t = (1 + c_t) / 2
@@ -38,4 +41,4 @@ name the levels, not the formula); it is pinned only by the identities above:
 and so are the router-replay readings of moe.py (shared router, the auxiliary's top-k2 taken
 from the primary's ranking, softmax over the selected experts, b on shared experts only).
 """
-from . import numerics, attention, linear, cache, layer, step, head, moe  # noqa: F401
+from . import numerics, attention, linear, cache, layer, step, head, moe, prefill  # noqa: F401

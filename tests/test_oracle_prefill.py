@@ -1,0 +1,97 @@
+"""Pins for the oracle's primary-only prefill and the auxiliary flow's start (CPU only).
+
+Checked against torch's causal scaled-dot-product attention, against the token-by-token
+recurrence of the separately pinned decode layer (prefilling T tokens at once must equal T
+single-token decode steps of the primary), chunking invariance, and the property that makes
+skipping the auxiliary during prefill lossless: the auxiliary keeps no state of its own, so
+its row at the last prompt position is the same whether or not it ran at earlier positions."""
+import numpy as np
+import pytest
+import torch
+
+import dfx_inputs as gen
+from oracle.layer import dual_flow_layer
+from oracle.numerics import widen
+from oracle.prefill import prefill_attention, prefill_layer, prefill_step
+from oracle.step import dual_flow_step
+
+SMALL = dict(hidden=64, num_q_heads=4, num_kv_heads=2, head_dim=32, intermediate=64, w_std=0.1)
+
+
+def test_prefill_attention_matches_torch_causal_sdpa():
+    B, T, Hq, Hkv, D, P = 2, 9, 4, 2, 32, 5            # 5 tokens already cached, 9 new ones
+    c = gen.attention_case(31, B, Hq, Hkv, D, np.full(B, P + T, np.int32), "f32", paged=True, block_size=4)
+    q = np.random.default_rng(1).standard_normal((B, T, Hq, D))
+    o, lse = prefill_attention(q, c.k_pool, c.v_pool, c.block_table, np.full(B, P))
+    for b in range(B):
+        blocks = c.block_table[b, : -(-(P + T) // 4)]
+        K = torch.from_numpy(widen(c.k_pool[blocks]).transpose(1, 0, 2, 3).reshape(Hkv, -1, D)[:, : P + T])
+        V = torch.from_numpy(widen(c.v_pool[blocks]).transpose(1, 0, 2, 3).reshape(Hkv, -1, D)[:, : P + T])
+        K, V = K.repeat_interleave(Hq // Hkv, 0), V.repeat_interleave(Hq // Hkv, 0)
+        Q = torch.from_numpy(q[b].transpose(1, 0, 2))                   # [Hq][T][D]
+        mask = torch.arange(P + T)[None, :] <= (P + torch.arange(T))[:, None]
+        want = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask).numpy()
+        assert np.allclose(o[b].transpose(1, 0, 2), want, rtol=0, atol=1e-12)
+    assert np.all(np.isfinite(lse))
+
+
+def prefill_case(seed, B=2, start=3, T=6):
+    return gen.layer_case(seed, batch=B, context=start + 1, capacity=start + T + 1, block_size=4, **SMALL)
+
+
+def test_prefill_layer_equals_token_by_token_decode():
+    start, T = 3, 6
+    c = prefill_case(41, start=start, T=T)
+    xs = np.random.default_rng(2).standard_normal((2, T, c.hidden)).astype(np.float32)
+    kv = c.cache
+    st = np.full(2, start)
+    got, kp, vp, _ = prefill_layer(xs, c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.eps,
+                                   kv.k_pool, kv.v_pool, kv.block_table, st, c.num_q_heads, c.num_kv_heads,
+                                   c.head_dim)
+    kq, vq = kv.k_pool, kv.v_pool
+    for t in range(T):
+        y, kq, vq, _ = dual_flow_layer(xs[None, :, t], c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down,
+                                       None, None, None, c.eps, kq, vq, kv.block_table, st + t,
+                                       c.num_q_heads, c.num_kv_heads, c.head_dim)
+        assert np.allclose(got[:, t], y[0], rtol=0, atol=1e-9)
+    assert np.array_equal(kp, kq) and np.array_equal(vp, vq)
+
+
+def test_chunked_prefill_equals_one_chunk():
+    c = prefill_case(42, start=2, T=7)
+    xs = np.random.default_rng(3).standard_normal((2, 7, c.hidden)).astype(np.float32)
+    kv = c.cache
+    args = (c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.eps)
+    heads = (c.num_q_heads, c.num_kv_heads, c.head_dim)
+    whole, kw, vw, _ = prefill_layer(xs, *args, kv.k_pool, kv.v_pool, kv.block_table, np.full(2, 2), *heads)
+    a, ka, va, _ = prefill_layer(xs[:, :3], *args, kv.k_pool, kv.v_pool, kv.block_table, np.full(2, 2), *heads)
+    b, kb, vb, _ = prefill_layer(xs[:, 3:], *args, ka, va, kv.block_table, np.full(2, 5), *heads)
+    assert np.allclose(np.concatenate([a, b], 1), whole, rtol=0, atol=1e-9)
+    assert np.array_equal(kb, kw) and np.array_equal(vb, vw)
+
+
+def test_aux_starts_at_the_last_prompt_position_without_loss():
+    """Prompt of n tokens: prefill of n - 1 tokens by the primary, then one dual step at
+    position n - 1. Running both flows at every position instead gives the same rows at the
+    last position and the same caches: the auxiliary writes no cache and carries no state."""
+    n, B, start = 5, 2, 0
+    layers = [prefill_case(50 + l, B=B, start=start, T=n) for l in range(2)]
+    rng = np.random.default_rng(4)
+    vocab = 11
+    e1 = gen.f32_to_bf16_bits(rng.standard_normal((vocab, SMALL["hidden"])).astype(np.float32))
+    e2 = gen.f32_to_bf16_bits(rng.standard_normal((vocab, SMALL["hidden"])).astype(np.float32))
+    tokens = rng.integers(0, vocab, (B, n))
+    # the method: primary-only prefill, then the auxiliary starts
+    _, pools = prefill_step(tokens[:, : n - 1], e1, layers, np.full(B, start))
+    for L, (kp, vp) in zip(layers, pools):
+        L.cache.k_pool, L.cache.v_pool = kp, vp
+    x_last, pools_last = dual_flow_step(tokens[:, n - 1], e1, e2, layers, np.full(B, start + n - 1))
+    # both flows at every position
+    fresh = [prefill_case(50 + l, B=B, start=start, T=n) for l in range(2)]
+    for t in range(n):
+        x_all, pools_all = dual_flow_step(tokens[:, t], e1, e2, fresh, np.full(B, start + t))
+        for L, (kp, vp) in zip(fresh, pools_all):
+            L.cache.k_pool, L.cache.v_pool = kp, vp
+    assert np.allclose(x_all, x_last, rtol=0, atol=1e-9)
+    for (ka, va), (kb, vb) in zip(pools_all, pools_last):
+        assert np.array_equal(ka, kb) and np.array_equal(va, vb)
