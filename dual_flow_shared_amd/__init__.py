@@ -20,7 +20,7 @@ __all__ = ["DfxError", "KVCache", "LayerWeights", "decode_attn", "decode_attn_pl
            "dual_flow_decode_layer", "layer_workspace_size", "copy_bytes", "read_bytes", "fill_bytes",
            "layer_taps", "dual_flow_decode_step", "step_workspace_size", "output_head",
            "output_head_workspace_size", "output_head_taps", "MoeWeights", "moe_mlp", "moe_workspace_size",
-           "moe_taps", "Workspace", "version"]
+           "moe_taps", "prefill_attn", "prefill_layer", "prefill_step", "Workspace", "version"]
 
 
 def version() -> int:
@@ -452,6 +452,59 @@ def moe_mlp(x: torch.Tensor, weights: MoeWeights, workspace: Optional[Workspace]
     need = moe_workspace_size(weights, B, F)
     buf = _workspace(workspace, x.device, "moe").get(need)
     check(lib().dfx_dual_flow_moe_mlp(ctypes.byref(w), B, F, _ptr(x), _ptr(buf), need, _stream(stream)))
+    return x
+
+
+def prefill_attn(q: torch.Tensor, cache: KVCache, start_pos: torch.Tensor, max_context: int,
+                 want_lse: bool = False, stream=None):
+    """Causal attention of a prompt chunk, q fp32 [B][T][Hq][D] (keys and values of the chunk
+    already in the cache at start_pos[b] + t) -> o fp32 [B][T][Hq][D] (and lse [B][T][Hq])."""
+    q = _contig(q, "q")
+    if q.dim() != 4 or q.dtype != torch.float32:
+        raise ValueError("q must be fp32 [batch][chunk][heads][head_dim]")
+    B, T, Hq, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(B, T, Hq, dtype=torch.float32, device=q.device) if want_lse else None
+    c = cache.struct()
+    check(lib().dfx_prefill_attn(ctypes.byref(c), _ptr(start_pos), B, T, max_context, Hq, _ptr(q), 0, _ptr(o),
+                                 _ptr(lse), _stream(stream)))
+    return (o, lse) if want_lse else o
+
+
+def prefill_layer(x: torch.Tensor, weights: LayerWeights, cache: KVCache, start_pos: torch.Tensor,
+                  max_context: int, workspace: Optional[Workspace] = None, stream=None) -> torch.Tensor:
+    """One layer of the primary over a prompt chunk, in place on x [B][T][hidden] fp32."""
+    x = _contig(x, "x")
+    if x.dim() != 3 or x.dtype != torch.float32:
+        raise ValueError("x must be fp32 [batch][chunk][hidden]")
+    B, T, _ = x.shape
+    w, c = weights.struct(), cache.struct()
+    n = ctypes.c_size_t()
+    check(lib().dfx_prefill_layer_workspace_size(ctypes.byref(w), ctypes.byref(c), B, T, max_context,
+                                                 ctypes.byref(n)))
+    buf = _workspace(workspace, x.device, "prefill").get(n.value)
+    check(lib().dfx_prefill_layer(ctypes.byref(w), ctypes.byref(c), _ptr(start_pos), B, T, max_context, _ptr(x),
+                                  _ptr(buf), n.value, _stream(stream)))
+    return x
+
+
+def prefill_step(tokens: torch.Tensor, embed_primary: torch.Tensor, layers, caches, start_pos: torch.Tensor,
+                 max_context: int, out: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None,
+                 stream=None) -> torch.Tensor:
+    """A prompt chunk through the primary's embeddings and every layer: tokens int32 [B][T] ->
+    residual rows [B][T][hidden] fp32 (each layer appends the chunk's keys and values)."""
+    tokens = _contig(tokens, "tokens")
+    if tokens.dim() != 2 or tokens.dtype != torch.int32:
+        raise ValueError("tokens must be int32 [batch][chunk]")
+    B, T = tokens.shape
+    vocab, H = embed_primary.shape
+    x = out if out is not None else torch.empty(B, T, H, dtype=torch.float32, device=tokens.device)
+    ws, cs = _structs(layers, caches)
+    n = ctypes.c_size_t()
+    check(lib().dfx_prefill_step_workspace_size(ws, cs, len(layers), B, T, max_context, ctypes.byref(n)))
+    buf = _workspace(workspace, tokens.device, "prefill").get(n.value)
+    check(lib().dfx_prefill_step(ws, cs, len(layers), _ptr(tokens), vocab, _ptr(_contig(embed_primary, "embed_primary")),
+                                 _ptr(start_pos), B, T, max_context, _ptr(x), _ptr(buf), n.value, _stream(stream)))
     return x
 
 

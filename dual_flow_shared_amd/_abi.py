@@ -79,6 +79,11 @@ SIGNATURES = {
     "dfx_dual_flow_moe_mlp_workspace_size": (I32, [MWP, I32, I32, PSZ]),
     "dfx_dual_flow_moe_mlp_taps": (I32, [MWP, I32, I32, ctypes.POINTER(MoeTapsStruct)]),
     "dfx_dual_flow_moe_mlp": (I32, [MWP, I32, I32, P, P, SZ, P]),
+    "dfx_prefill_attn": (I32, [KVP, P, I32, I32, I32, I32, P, I64, P, P, P]),
+    "dfx_prefill_layer_workspace_size": (I32, [LWP, KVP, I32, I32, I32, PSZ]),
+    "dfx_prefill_layer": (I32, [LWP, KVP, P, I32, I32, I32, P, P, SZ, P]),
+    "dfx_prefill_step_workspace_size": (I32, [LWP, KVP, I32, I32, I32, I32, PSZ]),
+    "dfx_prefill_step": (I32, [LWP, KVP, I32, P, I32, P, P, I32, I32, I32, P, P, SZ, P]),
     "dfx_copy_bytes": (I32, [P, P, SZ, P]),
     "dfx_read_bytes": (I32, [P, SZ, P, P]),
     "dfx_fill_bytes": (I32, [P, SZ, U32, P]),

@@ -868,6 +868,205 @@ dfx_status dfx_dual_flow_moe_mlp(const dfx_moe_weights *w, int32_t batch, int32_
   DFX_END
 }
 
+namespace {
+
+// ---- prefill (primary only)
+
+dfx_status check_prefill(const dfx_kv_cache *kv, int32_t B, int32_t T, int32_t max_context, int32_t hq) {
+  dfx_status st = check_kv(kv, B < 0 ? 0 : B);
+  if (st) return st;
+  if (B < 0 || B > 65535 || T < 0) return fail(DFX_EINVAL, "batch %d chunk %d", B, T);
+  if ((int64_t)B * T > (int64_t)1 << 22) return fail(DFX_EUNSUPPORTED, "batch * chunk above 2^22 rows");
+  if (kv->dtype != DFX_BF16) return fail(DFX_EUNSUPPORTED, "prefill needs a bf16 cache");
+  if (kv->block_table && kv->block_size < 16)
+    return fail(DFX_EUNSUPPORTED, "prefill needs paged blocks of >= 16 tokens (got %d)", kv->block_size);
+  if (hq < 4 || hq % 4 || hq % kv->num_kv_heads)
+    return fail(DFX_EUNSUPPORTED, "num_q_heads %d (a multiple of 4 and of num_kv_heads)", hq);
+  if (max_context < 1 || max_context > capacity(kv))
+    return fail(DFX_EINVAL, "max_context %d outside [1, capacity %lld]", max_context, (long long)capacity(kv));
+  return DFX_OK;
+}
+
+AttnArgs prefill_attn_args(const dfx_kv_cache *kv, const int32_t *start, int32_t B, int32_t T, int32_t max_context,
+                           int32_t hq, const float *q, int64_t q_stride, float *o, int o_packed, float *lse) {
+  AttnArgs a{};
+  a.k = kv->k; a.v = kv->v; a.table = kv->block_table; a.num_blocks = kv->num_blocks;
+  a.max_blocks = kv->max_blocks_per_seq; a.block_size = kv->block_size;
+  a.block_shift = kv->block_table ? (int)__builtin_ctz((unsigned)kv->block_size) : -1;
+  a.num_kv_heads = kv->num_kv_heads; a.head_dim = kv->head_dim; a.group = hq / kv->num_kv_heads;
+  a.num_q_heads = hq; a.n_flows = 1; a.batch = B; a.ctx = start; a.max_context = max_context;
+  a.q1 = q; a.q_bstride = q_stride; a.kv_bf16 = 1;
+  a.scale_log2 = kLog2e / sqrtf((float)kv->head_dim);
+  a.o1 = o; a.o_packed = o_packed; a.o_bf16 = o_packed; a.lse = lse; a.num_splits = 1;
+  a.prefill_T = T;
+  return a;
+}
+
+struct PrefillPlan {
+  size_t h1, qkv, o, h2, inter, total;
+};
+
+dfx_status prefill_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_t B, int32_t T,
+                        int32_t max_context, PrefillPlan *pp) {
+  if (!w) return fail(DFX_EINVAL, "weights is NULL");
+  dfx_status st = check_prefill(kv, B, T, max_context, w->num_q_heads);
+  if (st) return st;
+  if (w->head_dim != kv->head_dim || w->num_kv_heads != kv->num_kv_heads)
+    return fail(DFX_EINVAL, "weights and cache disagree on head_dim / num_kv_heads");
+  if (w->hidden < 32 || w->hidden % 32 || w->hidden > 16384) return fail(DFX_EUNSUPPORTED, "hidden %d", w->hidden);
+  if (w->intermediate < 32 || w->intermediate % 32) return fail(DFX_EUNSUPPORTED, "intermediate %d", w->intermediate);
+  if (!(w->rms_eps >= 0.f)) return fail(DFX_EINVAL, "rms_eps");
+  if (!w->attn_norm_gain || !w->w_qkv || !w->w_o || !w->mlp_norm_gain || !w->w_gate_up || !w->w_down)
+    return fail(DFX_EINVAL, "a weight pointer is NULL");
+  const int H = w->hidden, D = w->head_dim, Hq = w->num_q_heads, I = w->intermediate;
+  const size_t rows = (size_t)B * T, prow = (rows + 63) / 64 * 64;
+  auto a256 = [](size_t x) { return round_up(x, 256); };
+  PrefillPlan p{};
+  p.h1 = a256(prow * H * 2);
+  p.qkv = a256(rows * (Hq + 2 * w->num_kv_heads) * D * 4);
+  p.o = a256(prow * Hq * D * 2);
+  p.h2 = a256(prow * H * 2);
+  p.inter = a256(prow * I * 2);
+  p.total = p.h1 + p.qkv + p.o + p.h2 + p.inter;
+  *pp = p;
+  return DFX_OK;
+}
+
+// One projection of the prefill rows (one flow, one split, every 64-row group its own
+// work-group slice): fp32 out (optionally plus residual, in place), or SwiGLU bf16 rows.
+dfx_status prefill_linear(int32_t rows, int32_t K, int32_t N, const uint16_t *x_packed, const uint16_t *w,
+                          void *y, const float *residual, int swiglu, hipStream_t s) {
+  GemmArgs g{};
+  g.n_flows = 1; g.rows = rows; g.K = K; g.N = N; g.x_packed = 1; g.x = x_packed; g.w = w; g.w_packed = 1;
+  g.y = y; g.residual = residual; g.ksplit = 1; g.kper = K / 32; g.swiglu = swiglu;
+  g.group_split = (rows + 63) / 64;
+  return hip_status(launch_grouped_linear(g, s), "prefill projection launch");
+}
+
+dfx_status run_prefill_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv, const int32_t *start, int B, int T,
+                             int max_context, float *x, const PrefillPlan &p, char *base, hipStream_t s,
+                             bool norm_in) {
+  const int H = w->hidden, D = w->head_dim, Hq = w->num_q_heads;
+  const int Nqkv = (Hq + 2 * w->num_kv_heads) * D, I = w->intermediate, rows = B * T;
+  uint16_t *h1 = (uint16_t *)base;
+  float *qkv = (float *)(base + p.h1);
+  uint16_t *ob = (uint16_t *)((char *)qkv + p.qkv);
+  uint16_t *h2 = (uint16_t *)((char *)ob + p.o);
+  uint16_t *inter = (uint16_t *)((char *)h2 + p.h2);
+  dfx_status r;
+  if (norm_in && (r = hip_status(launch_rmsnorm(rows, H, x, w->attn_norm_gain, w->rms_eps, h1, s, 1), "rmsnorm launch")))
+    return r;
+  if ((r = prefill_linear(rows, H, Nqkv, h1, w->w_qkv, qkv, nullptr, 0, s))) return r;
+  PrefillGlueArgs ga{B, T, Nqkv, Hq, D, qkv, *kv, start};
+  if ((r = hip_status(launch_prefill_append(ga, s), "prefill append launch"))) return r;
+  AttnArgs a = prefill_attn_args(kv, start, B, T, max_context, Hq, qkv, Nqkv, (float *)ob, 1, nullptr);
+  if ((r = hip_status(launch_prefill_attn(a, s), "prefill attention launch"))) return r;
+  if ((r = prefill_linear(rows, Hq * D, H, ob, w->w_o, x, x, 0, s))) return r;
+  if ((r = hip_status(launch_rmsnorm(rows, H, x, w->mlp_norm_gain, w->rms_eps, h2, s, 1), "rmsnorm launch"))) return r;
+  if ((r = prefill_linear(rows, H, 2 * I, h2, w->w_gate_up, inter, nullptr, 1, s))) return r;
+  return prefill_linear(rows, I, H, inter, w->w_down, x, x, 0, s);
+}
+
+}  // namespace
+
+dfx_status dfx_prefill_attn(const dfx_kv_cache *kv, const int32_t *start_pos, int32_t batch, int32_t chunk,
+                            int32_t max_context, int32_t num_q_heads, const float *q, int64_t q_row_stride,
+                            float *o, float *lse, void *stream) {
+  DFX_BEGIN
+  dfx_status st = check_prefill(kv, batch, chunk, max_context, num_q_heads);
+  if (st) return st;
+  const int64_t row = (int64_t)num_q_heads * kv->head_dim;
+  if (q_row_stride == 0) q_row_stride = row;
+  if (q_row_stride < row || q_row_stride % 4) return fail(DFX_EINVAL, "q_row_stride %lld", (long long)q_row_stride);
+  if (batch == 0 || chunk == 0) return DFX_OK;
+  if (!start_pos || !q || !o) return fail(DFX_EINVAL, "start_pos / q / o is NULL");
+  if (!aligned16(q) || !aligned16(o) || ((uintptr_t)lse & 3)) return fail(DFX_EINVAL, "misaligned pointer");
+  AttnArgs a = prefill_attn_args(kv, start_pos, batch, chunk, max_context, num_q_heads, q, q_row_stride, o, 0, lse);
+  return hip_status(launch_prefill_attn(a, (hipStream_t)stream), "prefill attention launch");
+  DFX_END
+}
+
+dfx_status dfx_prefill_layer_workspace_size(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_t batch,
+                                            int32_t chunk, int32_t max_context, size_t *bytes) {
+  DFX_BEGIN
+  PrefillPlan p;
+  dfx_status st = prefill_plan(w, kv, batch, chunk, max_context, &p);
+  if (st) return st;
+  if (!bytes) return fail(DFX_EINVAL, "bytes is NULL");
+  *bytes = p.total;
+  return DFX_OK;
+  DFX_END
+}
+
+dfx_status dfx_prefill_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv, const int32_t *start_pos,
+                             int32_t batch, int32_t chunk, int32_t max_context, float *x, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  DFX_BEGIN
+  PrefillPlan p;
+  dfx_status st = prefill_plan(w, kv, batch, chunk, max_context, &p);
+  if (st) return st;
+  if (batch == 0 || chunk == 0) return DFX_OK;
+  if (!start_pos || !x) return fail(DFX_EINVAL, "start_pos / x is NULL");
+  if (!aligned16(x)) return fail(DFX_EINVAL, "x not 16-byte aligned");
+  if (!workspace || workspace_bytes < p.total)
+    return fail(DFX_EWORKSPACE, "prefill layer needs %zu workspace bytes, got %zu", p.total, workspace_bytes);
+  return run_prefill_layer(w, kv, start_pos, batch, chunk, max_context, x, p, (char *)workspace,
+                           (hipStream_t)stream, true);
+  DFX_END
+}
+
+dfx_status dfx_prefill_step_workspace_size(const dfx_layer_weights *layers, const dfx_kv_cache *caches,
+                                           int32_t n_layers, int32_t batch, int32_t chunk, int32_t max_context,
+                                           size_t *bytes) {
+  DFX_BEGIN
+  if (n_layers < 1 || !layers || !caches) return fail(DFX_EINVAL, "n_layers %d / layers / caches", n_layers);
+  if (!bytes) return fail(DFX_EINVAL, "bytes is NULL");
+  size_t m = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    PrefillPlan p;
+    dfx_status st = prefill_plan(&layers[l], &caches[l], batch, chunk, max_context, &p);
+    if (st) return st;
+    if (layers[l].hidden != layers[0].hidden) return fail(DFX_EINVAL, "layer %d hidden differs", l);
+    m = std::max(m, p.total);
+  }
+  *bytes = m;
+  return DFX_OK;
+  DFX_END
+}
+
+dfx_status dfx_prefill_step(const dfx_layer_weights *layers, const dfx_kv_cache *caches, int32_t n_layers,
+                            const int32_t *tokens, int32_t vocab, const uint16_t *embed_primary,
+                            const int32_t *start_pos, int32_t batch, int32_t chunk, int32_t max_context, float *x,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  DFX_BEGIN
+  size_t need = 0;
+  dfx_status st = dfx_prefill_step_workspace_size(layers, caches, n_layers, batch, chunk, max_context, &need);
+  if (st) return st;
+  if (vocab < 1 || !embed_primary) return fail(DFX_EINVAL, "vocab %d / embed_primary", vocab);
+  if ((uintptr_t)embed_primary & 7) return fail(DFX_EINVAL, "embed_primary must be 8-byte aligned");
+  if (batch == 0 || chunk == 0) return DFX_OK;
+  if (!tokens || !start_pos || !x) return fail(DFX_EINVAL, "tokens / start_pos / x is NULL");
+  if (!aligned16(x)) return fail(DFX_EINVAL, "x not 16-byte aligned");
+  if (!workspace || workspace_bytes < need)
+    return fail(DFX_EWORKSPACE, "prefill step needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  const dfx_layer_weights &w0 = layers[0];
+  // the primary's embedding rows and layer 0's normed rows, in one kernel
+  dfx_status r = hip_status(launch_embed_norm(1, batch * chunk, w0.hidden, tokens, vocab, embed_primary, nullptr,
+                                              w0.attn_norm_gain, w0.rms_eps, x, (uint16_t *)workspace, s),
+                            "embedding launch");
+  if (r) return r;
+  for (int l = 0; l < n_layers; ++l) {
+    PrefillPlan p;
+    prefill_plan(&layers[l], &caches[l], batch, chunk, max_context, &p);
+    if ((r = run_prefill_layer(&layers[l], &caches[l], start_pos, batch, chunk, max_context, x, p, (char *)workspace,
+                               s, l > 0)))
+      return r;
+  }
+  return DFX_OK;
+  DFX_END
+}
+
 dfx_status dfx_copy_bytes(void *dst, const void *src, size_t bytes, void *stream) {
   DFX_BEGIN
   if (bytes % 16 || !aligned16(dst) || !aligned16(src) || (bytes && (!dst || !src)))

@@ -25,29 +25,9 @@
 // score MFMA left them, and its M rows are head-dim d = VEC * m + mb, so one lane loads
 // VEC contiguous elements of 8 token rows (4 full rows per load instruction) and a
 // register transpose yields the V^T operand.
-#include "common.h"
+#include "attn_tiles.h"
 
 namespace dfx {
-
-template <bool BF16>
-__device__ __forceinline__ void load8(const void *base, int64_t off, float *out) {
-  if constexpr (BF16) {
-    const u32x4 w = *(const u32x4 *)((const uint16_t *)base + off);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = bf16_lo(w[i]);
-      out[2 * i + 1] = bf16_hi(w[i]);
-    }
-  } else {
-    const f32x4 a = *(const f32x4 *)((const float *)base + off);
-    const f32x4 c = *(const f32x4 *)((const float *)base + off + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[i] = a[i];
-      out[4 + i] = c[i];
-    }
-  }
-}
 
 // Writes one finished (row, d) value: final output when there is a single split,
 // otherwise the split's normalized partial and its log2-domain LSE.
@@ -68,150 +48,6 @@ __device__ __forceinline__ void store_result(const AttnArgs &p, int split, int b
     const int64_t row = (((int64_t)split * p.n_flows + f) * p.batch + b) * Hq + h;
     p.part_o[row * D + d] = o;
     if (d == 0) p.part_lse[row] = lse2;
-  }
-}
-
-constexpr int kMaxChunkBlocks = 1024;  // block ids of one split held in LDS
-
-template <int D>
-struct TileRegs {
-  u32x4 kf[2][D / 32];            // K rows of two 16-token blocks (A operand)
-  uint32_t vr[8][D / 32];         // V: D/16 elements of the 8 token rows tau(j, v)
-};
-
-// Element offsets of the first row of each 16-token half of the tile at t0 and the
-// largest in-half index that is still inside [t0, end). A half lies in one block (paged
-// blocks hold >= 16 tokens and halves start 16-aligned); a half entirely past `end`
-// reuses the first half, and rows past `end` are clamped to the last valid one (their
-// scores are masked), so every address stays inside this split's staged blocks.
-template <bool PAGED>
-__device__ __forceinline__ void half_bases(const AttnArgs &p, const int32_t *tbl, int first_blk,
-                                           int b, int g, int t0, int end, int64_t *hb, int *lastx) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int hs = t0 + 16 * h < end ? t0 + 16 * h : t0;
-    int64_t blk;
-    int slot;
-    if constexpr (PAGED) {
-      blk = tbl[(hs >> p.block_shift) - first_blk];
-      slot = hs & (p.block_size - 1);
-    } else {
-      blk = b;
-      slot = hs;
-    }
-    hb[h] = ((blk * p.num_kv_heads + g) * (int64_t)p.block_size + slot) * p.head_dim;
-    lastx[h] = end - 1 - hs;
-  }
-}
-
-#ifndef DFX_ATTN_NT
-#define DFX_ATTN_NT 1
-#endif
-// K/V loads: non-temporal by default (each line is read once per call, and the hint keeps
-// the stream from displacing the rest of L2); 0 gives plain loads for comparison.
-template <typename T>
-__device__ __forceinline__ T kv_load(const uint16_t *p) {
-  if constexpr (DFX_ATTN_NT) return __builtin_nontemporal_load((const T *)p);
-  else return *(const T *)p;
-}
-
-// Issue the K (resp. V) loads of the tile described by (hb, lastx).
-template <int D>
-__device__ __forceinline__ void load_k(const uint16_t *kp, const int64_t *hb, const int *lastx,
-                                       int n, int j, TileRegs<D> &r) {
-  constexpr int KS = D / 32;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const uint16_t *row = kp + hb[mb] + (int64_t)min(n, lastx[mb]) * D;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) r.kf[mb][s] = kv_load<u32x4>(row + 8 * (4 * s + j));
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void load_v(const uint16_t *vp, const int64_t *hb, const int *lastx,
-                                       int n, int j, TileRegs<D> &r) {
-  constexpr int VEC = D / 16;
-#pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    const int h = v >> 2, x = 4 * j + (v & 3);  // token tau(j, v) = t0 + 16 h + x
-    const uint16_t *src = vp + hb[h] + (int64_t)min(x, lastx[h]) * D + VEC * n;
-    if constexpr (VEC == 8) {
-      const u32x4 y = kv_load<u32x4>(src);
-      r.vr[v][0] = y[0]; r.vr[v][1] = y[1]; r.vr[v][2] = y[2]; r.vr[v][3] = y[3];
-    } else {
-      const u32x2 y = kv_load<u32x2>(src);
-      r.vr[v][0] = y[0]; r.vr[v][1] = y[1];
-    }
-  }
-}
-
-// Scores of one loaded tile (S^T blocks for its two 16-token halves).
-template <int D>
-__device__ __forceinline__ void tile_scores(const TileRegs<D> &r, const u32x4 *qh, const u32x4 *ql,
-                                            f32x4 *sacc) {
-  constexpr int KS = D / 32;
-  sacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      sacc[mb] = mfma16x16x32(as_bf16x8(r.kf[mb][s]), as_bf16x8(qh[s]), sacc[mb]);
-      sacc[mb] = mfma16x16x32(as_bf16x8(r.kf[mb][s]), as_bf16x8(ql[s]), sacc[mb]);
-    }
-}
-
-// Online-softmax update for query row n (the lane holds 8 of the tile's 32 tokens) and
-// P.V accumulation into O^T.
-template <int D>
-__device__ __forceinline__ void tile_softmax_pv(const AttnArgs &p, const TileRegs<D> &r,
-                                                const f32x4 *sacc, int t0, int end, int j,
-                                                float &m_run, float &l_run, f32x4 *oacc) {
-  constexpr int VEC = D / 16;
-  float sv[8];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = t0 + 16 * mb + 4 * j + i;
-      const float x = tok < end ? sacc[mb][i] * p.scale_log2 : -INFINITY;
-      sv[4 * mb + i] = x;
-      mx = fmaxf(mx, x);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m_run, mx);
-  const float alpha = exp2f(m_run - m_new);
-  float psum = 0.f;
-  uint32_t phi[8], plo[8];
-#pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    const float pv = exp2f(sv[v] - m_new);
-    psum += pv;
-    split_bf16(pv, phi[v], plo[v]);
-  }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-  u32x4 pH, pL;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    pH[w] = phi[2 * w] | (phi[2 * w + 1] << 16);
-    pL[w] = plo[2 * w] | (plo[2 * w + 1] << 16);
-  }
-#pragma unroll
-  for (int mb = 0; mb < VEC; ++mb) {
-    oacc[mb] *= alpha;
-    // V^T rows d = VEC*n + mb over tokens tau(j, 0..7): element mb of each loaded row
-    u32x4 af;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t x0 = r.vr[2 * w][mb >> 1], x1 = r.vr[2 * w + 1][mb >> 1];
-      af[w] = (mb & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-    }
-    oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pH), oacc[mb]);
-    oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pL), oacc[mb]);
   }
 }
 

@@ -137,6 +137,9 @@ struct AttnArgs {
   int32_t o_packed;  // bf16 rows in the grouped linear's fragment order, both flows in o1
   float *part_o, *part_lse;  // [S][F][B][Hq][D], [S][F][B][Hq] (log2 domain)
   int32_t num_splits, chunk;
+  // prefill (primary only): T query positions per sequence, ctx[b] = position of the first;
+  // q1 rows are (b, t) with row stride q_bstride
+  int32_t prefill_T;
 };
 
 struct GemmArgs {
@@ -165,6 +168,9 @@ struct GemmArgs {
   const int32_t *expert_rows;
   int32_t experts, max_groups;
   int64_t x_estride, w_estride, y_estride, p_estride;
+  // many row groups (prefill), one split: grid z = group_split slices of the row groups, each
+  // work-group streams its weight columns once per group of its slice
+  int32_t group_split;
 };
 
 // Destination of attention output (flow f, sequence b, column c = head * D + d): rows
@@ -229,6 +235,17 @@ struct MoeArgs {
   float *x;                  // [F][B][H] residual rows, updated in place
 };
 hipError_t launch_moe(int which, const MoeArgs &a, hipStream_t s);
+
+// Prefill (primary only): causal attention of T new positions per sequence over the cache,
+// and the Q/K/V finish that appends the chunk's keys and values.
+hipError_t launch_prefill_attn(const AttnArgs &a, hipStream_t s);
+struct PrefillGlueArgs {
+  int32_t B, T, N, num_q_heads, head_dim;
+  const float *qkv;        // [B * T][N] fp32 projection rows
+  dfx_kv_cache kv;
+  const int32_t *start;    // [B] position of each sequence's first new token
+};
+hipError_t launch_prefill_append(const PrefillGlueArgs &a, hipStream_t s);
 // packed_flows > 0: y in the fragment order of xpack_offset for that many flows (rows =
 // flows x batch); 0: row-major.
 hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,

@@ -109,6 +109,12 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
   }
   const int groups = (rows + rpg - 1) / rpg;
   const int tgroups = p.expert_rows ? p.max_groups : groups;  // group count of the tile layout
+  int g_begin = 0, g_end = groups;
+  if (!p.expert_rows && p.group_split > 1) {
+    const int per = (groups + p.group_split - 1) / p.group_split;
+    g_begin = blockIdx.z * per;
+    g_end = min(groups, g_begin + per);
+  }
   const int nks = K / 32, ng = N / 16;
   const int kbeg = ks * p.kper;
   const int nk = min(p.kper, nks - kbeg);  // >= 1: the plan leaves no split empty
@@ -131,7 +137,7 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
     wstep = 32;
   }
 
-  for (int grp = 0; grp < groups; ++grp) {
+  for (int grp = g_begin; grp < g_end; ++grp) {
     // the row fragment this lane stages: block nb = wave of the k-step, i.e. row
     // q = 16 wave + n of the group (a row past the batch reads row 0 in row-major X; its
     // outputs are never stored)
@@ -280,7 +286,8 @@ __global__ void __launch_bounds__(256) grouped_linear_reduce_kernel(GemmArgs p) 
 }
 
 hipError_t launch_grouped_linear(const GemmArgs &g, hipStream_t s) {
-  const dim3 grid(g.swiglu ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128, g.ksplit, g.expert_rows ? g.experts : 1),
+  const dim3 grid(g.swiglu ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128, g.ksplit,
+                  g.expert_rows ? g.experts : (g.group_split > 1 ? g.group_split : 1)),
       block(256);
 #define DFX_GL(XF, XP, WP) grouped_linear_kernel<XF, XP, WP><<<grid, block, 0, s>>>(g)
   if (g.x_packed) {

@@ -1,0 +1,178 @@
+// Prefill by the primary flow alone (Sintesi Tecnica: Dual-Flow Transformers, "Costi di
+// Inferenza vs. Addestramento": the auxiliary flow is skipped during prefill and the primary
+// is an ordinary causal Transformer writing the cache; the auxiliary starts at the last prompt
+// position, which is a decode step).
+//
+// prefill_append_kernel: the chunk's key and value columns of the fused projection rows go to
+// the cache at positions start_b + t (bf16, nearest even), the query columns stay in place.
+// prefill_attn_kernel: causal attention of every new position over the cache. A work-group is
+// 4 waves; wave w takes query head 4x + w and 16 consecutive positions of one sequence, and
+// streams all keys up to the tile's last position in 32-token tiles with the decode kernel's
+// MFMA tile code (attn_tiles.h); each lane masks its own row at the row's position. The waves
+// of a group of heads read the same K/V lines at about the same time, so the cache is fetched
+// from HBM about once per work-group and re-read from the CU's caches by the other waves.
+#include "attn_tiles.h"
+
+namespace dfx {
+
+// One thread per 4 key or value columns of one (sequence, position) row.
+__global__ void __launch_bounds__(256) prefill_append_kernel(PrefillGlueArgs a) {
+  const dfx_kv_cache &kv = a.kv;
+  const int kvcols = kv.num_kv_heads * kv.head_dim;
+  const int n4 = 2 * kvcols / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)a.B * a.T * n4) return;
+  const int c = (int)(idx % n4) * 4;
+  const int64_t row = idx / n4;
+  const int b = (int)(row / a.T), t = (int)(row % a.T);
+  const bool is_v = c >= kvcols;
+  const int cc = is_v ? c - kvcols : c;
+  const int g = cc / kv.head_dim, d = cc % kv.head_dim;
+  const f32x4 v = *(const f32x4 *)(a.qkv + row * a.N + a.num_q_heads * a.head_dim + c);
+  const bool paged = kv.block_table != nullptr;
+  const int64_t cap = paged ? (int64_t)kv.max_blocks_per_seq * kv.block_size : kv.block_size;
+  int64_t pos = (int64_t)a.start[b] + t;
+  pos = pos < 0 ? 0 : (pos >= cap ? cap - 1 : pos);
+  int64_t blk, slot;
+  if (paged) {
+    const uint32_t e = (uint32_t)kv.block_table[(int64_t)b * kv.max_blocks_per_seq + pos / kv.block_size];
+    blk = (uint64_t)e < (uint64_t)kv.num_blocks ? (int64_t)e : kv.num_blocks - 1;
+    slot = pos % kv.block_size;
+  } else {
+    blk = b;
+    slot = pos;
+  }
+  uint16_t *pool = (uint16_t *)(is_v ? kv.v : kv.k);
+  const int64_t dst = ((blk * kv.num_kv_heads + g) * kv.block_size + slot) * kv.head_dim + d;
+  *(u32x2 *)(pool + dst) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+hipError_t launch_prefill_append(const PrefillGlueArgs &a, hipStream_t s) {
+  const int64_t threads = (int64_t)a.B * a.T * (2 * a.kv.num_kv_heads * a.kv.head_dim / 4);
+  if (threads == 0) return hipSuccess;
+  prefill_append_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int D, bool PAGED>
+__global__ void __launch_bounds__(256) prefill_attn_kernel(AttnArgs p) {
+  constexpr int KS = D / 32, VEC = D / 16;
+  __shared__ int32_t s_tbl[kMaxChunkBlocks];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, j = lane >> 4;
+  const int h = blockIdx.x * 4 + wave, b = blockIdx.y;
+  const int tile = gridDim.z - 1 - blockIdx.z;  // the longest tiles are dispatched first
+  const int T = p.prefill_T, t0 = 16 * tile;
+  const int g = h / p.group;
+  const int cap = p.max_context;
+  const int start = min(max(p.ctx[b], 0), cap);
+  const int rows = min(16, T - t0);
+  // keys [0, kend): up to this tile's last position; each lane's row stops at its own
+  const int kend = max(min(start + t0 + rows, cap), 1);
+  const int my_end = n < rows ? min(start + t0 + n + 1, kend) : 1;
+
+  // query row n of this wave: position t0 + n of head h, split into bf16 hi + lo
+  u32x4 qh[KS], ql[KS];
+  {
+    const bool valid = n < rows;
+    const int64_t qoff = ((int64_t)b * T + t0 + (valid ? n : 0)) * p.q_bstride + (int64_t)h * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float q[8];
+      load8<false>(p.q1, qoff + 8 * (4 * s + j), q);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t h0, l0, h1, l1;
+        split_bf16(valid ? q[2 * w] : 0.f, h0, l0);
+        split_bf16(valid ? q[2 * w + 1] : 0.f, h1, l1);
+        qh[s][w] = h0 | (h1 << 16);
+        ql[s][w] = l0 | (l1 << 16);
+      }
+    }
+  }
+
+  const uint16_t *kp = (const uint16_t *)p.k;
+  const uint16_t *vp = (const uint16_t *)p.v;
+  f32x4 oacc[VEC];
+#pragma unroll
+  for (int mb = 0; mb < VEC; ++mb) oacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // keys in chunks of at most kMaxChunkBlocks staged block ids
+  const int chunk_tok = PAGED ? (kMaxChunkBlocks << p.block_shift) : kend;
+  for (int cs = 0; cs < kend; cs += chunk_tok) {
+    const int ce = min(cs + chunk_tok, kend);
+    const int first_blk = PAGED ? (cs >> p.block_shift) : 0;
+    if constexpr (PAGED) {
+      __syncthreads();  // every wave is done with the previous chunk's ids
+      const int nblk = ((ce - 1) >> p.block_shift) - first_blk + 1;
+      for (int i = threadIdx.x; i < nblk; i += 256) {
+        const uint32_t e = (uint32_t)p.table[(int64_t)b * p.max_blocks + first_blk + i];
+        s_tbl[i] = (uint64_t)e < (uint64_t)p.num_blocks ? (int32_t)e : (int32_t)(p.num_blocks - 1);
+      }
+      __syncthreads();
+    }
+    TileRegs<D> tr;
+    int64_t hb[2];
+    int lx[2];
+    f32x4 sacc[2];
+    int t = cs;
+    half_bases<PAGED>(p, s_tbl, first_blk, b, g, t, ce, hb, lx);
+    load_k<D>(kp, hb, lx, n, j, tr);
+    load_v<D>(vp, hb, lx, n, j, tr);
+    for (; t + 32 < ce; t += 32) {
+      half_bases<PAGED>(p, s_tbl, first_blk, b, g, t + 32, ce, hb, lx);
+      tile_scores<D>(tr, qh, ql, sacc);
+      load_k<D>(kp, hb, lx, n, j, tr);
+      tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, m_run, l_run, oacc);
+      load_v<D>(vp, hb, lx, n, j, tr);
+    }
+    tile_scores<D>(tr, qh, ql, sacc);
+    tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, m_run, l_run, oacc);
+  }
+
+  // row n's sum over the four lanes that hold it, then 32 consecutive head-dim values per lane
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (n >= rows) return;
+  const float inv = 1.0f / l_tot;
+  const int64_t r = (int64_t)b * T + t0 + n;
+  const int Hq = p.num_q_heads;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float o[VEC];
+#pragma unroll
+    for (int mb = 0; mb < VEC; ++mb) o[mb] = oacc[mb][i] * inv;
+    const int d0 = VEC * (4 * j + i);
+    if (p.o_packed) {
+      // bf16 rows of W_o's input in the grouped linear's fragment order (one flow)
+      uint16_t *dst = (uint16_t *)p.o1 + xpack_offset(1, 0, (int)r, h * D + d0, Hq * D);
+      if constexpr (VEC == 8)
+        *(u32x4 *)dst = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                              pack_bf16x2(o[6], o[7])};
+      else
+        *(u32x2 *)dst = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    } else {
+      float *dst = p.o1 + (r * Hq + h) * D + d0;
+#pragma unroll
+      for (int v = 0; v < VEC; v += 4) *(f32x4 *)(dst + v) = f32x4{o[v], o[v + 1], o[v + 2], o[v + 3]};
+    }
+  }
+  if (j == 0 && p.lse) p.lse[r * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
+}
+
+hipError_t launch_prefill_attn(const AttnArgs &a, hipStream_t s) {
+  if (a.batch == 0 || a.prefill_T == 0) return hipSuccess;
+  const dim3 grid(a.num_q_heads / 4, a.batch, (a.prefill_T + 15) / 16), block(256);
+  const bool paged = a.block_shift >= 0;
+  if (a.head_dim == 128) {
+    if (paged) prefill_attn_kernel<128, true><<<grid, block, 0, s>>>(a);
+    else prefill_attn_kernel<128, false><<<grid, block, 0, s>>>(a);
+  } else {
+    if (paged) prefill_attn_kernel<64, true><<<grid, block, 0, s>>>(a);
+    else prefill_attn_kernel<64, false><<<grid, block, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dfx

@@ -450,6 +450,59 @@ dfx_status dfx_dual_flow_moe_mlp(const dfx_moe_weights *w, int32_t batch, int32_
                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Prefill by the primary flow alone (Sintesi Tecnica: Dual-Flow Transformers, "Costi di
+ * Inferenza vs. Addestramento": prefill costs what a standard Transformer's does, the
+ * auxiliary flow being skipped entirely; "Architettura Core": the auxiliary flow starts at the
+ * last prompt position). A prompt of n tokens is a prefill of tokens 0 .. n-2 with these calls,
+ * then dfx_dual_flow_decode_step at position n-1 with both flows. A chunk holds `chunk` new
+ * positions of every sequence; start_pos[b] (device int32 [batch]) is the position of
+ * sequence b's first new token, and start_pos[b] + chunk <= max_context <= the cache's capacity.
+ * The cache must be bf16, paged blocks >= 16 tokens; num_q_heads a multiple of 4. Positions
+ * and block ids are clamped on the device like the decode calls'.
+ *
+ * dfx_prefill_attn: causal attention of the new positions, whose keys and values are already
+ * in the cache: query t of sequence b attends to positions [0, start_pos[b] + t].
+ *   q    device fp32 rows (b, t) of num_q_heads * head_dim values, row (b * chunk + t) at
+ *        q + row * q_row_stride (0: num_q_heads * head_dim); 16-byte aligned, stride % 4 == 0.
+ *   o    device fp32 [batch][chunk][num_q_heads][head_dim], output.
+ *   lse  device fp32 [batch][chunk][num_q_heads] natural-log sums, output, or NULL.
+ * No workspace.
+ */
+dfx_status dfx_prefill_attn(const dfx_kv_cache *kv, const int32_t *start_pos, int32_t batch, int32_t chunk,
+                            int32_t max_context, int32_t num_q_heads, const float *q, int64_t q_row_stride,
+                            float *o, float *lse, void *stream);
+
+/*
+ * dfx_prefill_layer: one layer for the new positions of the primary, in place on x (device
+ * fp32 [batch][chunk][hidden]): the decode layer's steps with one flow and every position a
+ * row -- norm, shared Q/K/V projection, the chunk's keys and values appended at start_pos[b] + t
+ * (bf16, nearest even), causal attention (rows rounded to bf16), W_o + residual, norm, gate/up
+ * with SwiGLU (no coupling: the auxiliary is off), W_down + residual. The same bf16 rounding
+ * points as the decode layer. workspace: >= dfx_prefill_layer_workspace_size bytes.
+ */
+dfx_status dfx_prefill_layer_workspace_size(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_t batch,
+                                            int32_t chunk, int32_t max_context, size_t *bytes);
+
+dfx_status dfx_prefill_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv, const int32_t *start_pos,
+                             int32_t batch, int32_t chunk, int32_t max_context, float *x, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * dfx_prefill_step: tokens (device int32 [batch][chunk], clamped to [0, vocab)) through the
+ * primary's embedding table (bf16 [vocab][hidden], 8-byte aligned) and every layer
+ * (dfx_prefill_layer with layers[l], caches[l]); x (device fp32 [batch][chunk][hidden]) is
+ * the output. The call allocates nothing and never synchronizes.
+ */
+dfx_status dfx_prefill_step_workspace_size(const dfx_layer_weights *layers, const dfx_kv_cache *caches,
+                                           int32_t n_layers, int32_t batch, int32_t chunk, int32_t max_context,
+                                           size_t *bytes);
+
+dfx_status dfx_prefill_step(const dfx_layer_weights *layers, const dfx_kv_cache *caches, int32_t n_layers,
+                            const int32_t *tokens, int32_t vocab, const uint16_t *embed_primary,
+                            const int32_t *start_pos, int32_t batch, int32_t chunk, int32_t max_context, float *x,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Measurement helpers (not part of the method): a plain device copy of
  * `bytes` (multiple of 16, both pointers 16-byte aligned) used to calibrate
  * hardware traffic counters, a read of `bytes` (achievable read bandwidth;

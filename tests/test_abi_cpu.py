@@ -21,7 +21,7 @@ def declared():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = _abi.lib()
     names = declared()
-    assert len(names) == 24
+    assert len(names) == 29
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, n
@@ -272,3 +272,35 @@ def test_moe_plan_and_rejects():
     assert lib.dfx_dual_flow_moe_mlp(ctypes.byref(w), 4, 2, FAKE + 4, FAKE, n.value, None) == 1
     assert lib.dfx_dual_flow_moe_mlp(ctypes.byref(w), 4, 2, None, FAKE, n.value, None) == 1
     assert lib.dfx_dual_flow_moe_mlp(None, 4, 2, FAKE, FAKE, n.value, None) == 1
+
+
+def test_prefill_rejects():
+    lib = _abi.lib()
+    w = _abi.LayerWeightsStruct()
+    w.hidden, w.num_q_heads, w.num_kv_heads, w.head_dim, w.intermediate, w.rms_eps = 4096, 32, 8, 128, 14336, 1e-5
+    for f in ("attn_norm_gain", "w_qkv", "w_o", "mlp_norm_gain", "w_gate_up", "w_down"):
+        setattr(w, f, FAKE)
+    k = kv(mb=512, nb=16384)
+    n = ctypes.c_size_t()
+    assert lib.dfx_prefill_layer_workspace_size(ctypes.byref(w), ctypes.byref(k), 2, 2048, 8192, ctypes.byref(n)) == 0
+    rows = 2 * 2048
+    assert n.value >= rows * (32 + 16) * 128 * 4 + 3 * rows * 4096 * 2 + rows * 14336 * 2
+    assert lib.dfx_prefill_layer_workspace_size(ctypes.byref(w), ctypes.byref(k), 2, 2048, 8193 * 8, ctypes.byref(n)) == 1
+    assert lib.dfx_prefill_layer(ctypes.byref(w), ctypes.byref(k), FAKE, 2, 2048, 8192, FAKE, None, 0, None) == 3
+    assert lib.dfx_prefill_layer(ctypes.byref(w), ctypes.byref(k), FAKE, 2, 0, 8192, FAKE, None, 0, None) == 0
+    w.num_q_heads = 6
+    assert lib.dfx_prefill_layer_workspace_size(ctypes.byref(w), ctypes.byref(k), 2, 16, 8192, ctypes.byref(n)) == 2
+    k32 = kv(dtype=0, mb=512, nb=16384)
+    assert lib.dfx_prefill_attn(ctypes.byref(k32), FAKE, 2, 16, 64, 32, FAKE, 0, FAKE, None, None) == 2
+    assert lib.dfx_prefill_attn(ctypes.byref(k), FAKE, 2, 16, 64, 32, FAKE, 100, FAKE, None, None) == 1  # stride
+    assert lib.dfx_prefill_attn(ctypes.byref(k), FAKE, 2, 16, 64, 32, FAKE + 4, 0, FAKE, None, None) == 1
+    assert lib.dfx_prefill_attn(ctypes.byref(k), FAKE, 2, 16, 64, 30, FAKE, 0, FAKE, None, None) == 2    # heads
+    assert lib.dfx_prefill_attn(ctypes.byref(k), FAKE, 1 << 16, 16, 64, 32, FAKE, 0, FAKE, None, None) == 1
+    W = _abi.LayerWeightsStruct * 1
+    K = _abi.KVCacheStruct * 1
+    ws, ks = W(), K()
+    ws[0], ks[0] = w, k
+    ws[0].num_q_heads = 32
+    assert lib.dfx_prefill_step_workspace_size(ws, ks, 1, 2, 16, 64, ctypes.byref(n)) == 0
+    assert lib.dfx_prefill_step(ws, ks, 1, FAKE, 0, FAKE, FAKE, 2, 16, 64, FAKE, FAKE, n.value, None) == 1
+    assert lib.dfx_prefill_step(ws, ks, 0, FAKE, 10, FAKE, FAKE, 2, 16, 64, FAKE, FAKE, n.value, None) == 1

@@ -1,0 +1,130 @@
+"""GPU parity of the primary-only prefill (dfx_prefill_attn, dfx_prefill_layer, dfx_prefill_step)
+and of the auxiliary flow's start at the last prompt position.
+
+Tolerances: the causal attention outputs against the oracle at max-abs 2e-3 (bf16 cache) and,
+tighter, 5e-5 (Q and P are split into two bf16 terms, so the kernel carries about 16 more bits
+than one bf16 pass); the layer and step outputs as the decode layer's (median 2e-3, max 5e-2
+after five bf16 rounding points), the appended keys and values equal bit for bit but for rare
+rounding decisions one bf16 step apart (fp32 against fp64 projections); chunked prefill
+bit-identical to one chunk."""
+import numpy as np
+import pytest
+import torch
+
+import dfx_inputs as gen
+import dual_flow_shared_amd as dfx
+from gpu_util import cache_of, dev, host_bits
+from oracle.prefill import prefill_attention, prefill_layer, prefill_step
+from oracle.step import dual_flow_step
+
+pytestmark = pytest.mark.gpu
+
+
+def layer_close(y, want):
+    err = np.abs(np.asarray(y, np.float64) - want)
+    assert np.median(err) < 2e-3 and err.max() < 5e-2, (np.median(err), err.max())
+
+
+@pytest.mark.parametrize("paged,D,Hq,Hkv,T,starts", [
+    (True, 128, 8, 2, 37, [0, 21]),        # ragged tail tile, different start per sequence
+    (True, 128, 32, 8, 16, [5, 0]),
+    (False, 64, 4, 4, 50, [3, 7]),         # contiguous cache, head_dim 64, no grouping
+    (True, 128, 8, 1, 1, [40, 0]),         # one new position (a decode-shaped chunk)
+])
+def test_prefill_attention(paged, D, Hq, Hkv, T, starts):
+    B = len(starts)
+    st = np.array(starts, np.int32)
+    ctx = st + T
+    c = gen.attention_case(600 + T, B, Hq, Hkv, D, ctx, "bf16", paged=paged, block_size=16,
+                           capacity=int(ctx.max()) + 16)
+    q = np.random.default_rng(T).standard_normal((B, T, Hq, D)).astype(np.float32)
+    cache = cache_of(c)
+    o, lse = dfx.prefill_attn(dev(q), cache, dev(st), int(ctx.max()) + 16, want_lse=True)
+    torch.cuda.synchronize()
+    want, wl = prefill_attention(q, c.k_pool, c.v_pool, c.block_table, st)
+    err = np.abs(o.cpu().numpy() - want).max()
+    assert err < 2e-3 and err < 5e-5, err
+    assert np.abs(lse.cpu().numpy() - wl).max() < 1e-4
+
+
+SMALL = dict(hidden=256, num_q_heads=8, num_kv_heads=2, head_dim=128, intermediate=512, w_std=0.05)
+
+
+def weights_of(c):
+    return dfx.LayerWeights.from_row_major(dev(c.g_attn), dev(c.w_qkv), dev(c.w_o), dev(c.g_mlp), dev(c.w_gate_up),
+                                           dev(c.w_down), c.num_q_heads, c.num_kv_heads, c.head_dim, c.eps)
+
+
+def test_prefill_layer_parity_and_appended_rows():
+    B, start, T = 3, 19, 45
+    c = gen.layer_case(701, batch=B, context=start + 1, capacity=start + T + 8, **SMALL)
+    x = np.random.default_rng(3).standard_normal((B, T, c.hidden)).astype(np.float32)
+    cache = cache_of(c.cache)
+    st = np.full(B, start, np.int32)
+    xt = dev(x)
+    dfx.prefill_layer(xt, weights_of(c), cache, dev(st), start + T + 8)
+    torch.cuda.synchronize()
+    want, kp, vp, _ = prefill_layer(x, c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.eps,
+                                    c.cache.k_pool, c.cache.v_pool, c.cache.block_table, st, c.num_q_heads,
+                                    c.num_kv_heads, c.head_dim)
+    layer_close(xt.cpu().numpy(), want)
+    gk, gv = host_bits(cache.k), host_bits(cache.v)
+    # the pool changed exactly at the chunk's slots, and agrees with the oracle's appended rows
+    changed = np.any(gk != c.cache.k_pool, axis=(1, 3))
+    assert np.array_equal(changed, np.any(kp != c.cache.k_pool, axis=(1, 3)))
+    for got, ref in ((gk, kp), (gv, vp)):
+        # slots the chunk wrote: equal bits but for rare rounding decisions one bf16 step apart
+        # (the GPU and the oracle round fp32 and fp64 projections of slightly different rows)
+        rows = changed[:, None, :, None] & np.ones_like(got, bool)
+        same = got[rows] == ref[rows]
+        assert same.mean() > 0.995
+        g = gen.bf16_bits_to_f32(got[rows][~same]).astype(np.float64)
+        r = gen.bf16_bits_to_f32(ref[rows][~same]).astype(np.float64)
+        _, e = np.frexp(np.maximum(np.abs(g), np.abs(r)))
+        assert np.all(np.abs(g - r) <= np.ldexp(1.0, e - 8))
+
+
+def test_chunked_prefill_is_bit_identical_to_one_chunk():
+    B, start, T, T1 = 2, 6, 40, 17
+    c = gen.layer_case(702, batch=B, context=start + 1, capacity=start + T + 8, **SMALL)
+    x = np.random.default_rng(4).standard_normal((B, T, c.hidden)).astype(np.float32)
+    w = weights_of(c)
+    mc = start + T + 8
+    one = cache_of(c.cache)
+    xa = dev(x)
+    dfx.prefill_layer(xa, w, one, dev(np.full(B, start, np.int32)), mc)
+    two = cache_of(c.cache)
+    xb1, xb2 = dev(x[:, :T1].copy()), dev(x[:, T1:].copy())
+    dfx.prefill_layer(xb1, w, two, dev(np.full(B, start, np.int32)), mc)
+    dfx.prefill_layer(xb2, w, two, dev(np.full(B, start + T1, np.int32)), mc)
+    torch.cuda.synchronize()
+    assert np.array_equal(torch.cat([xb1, xb2], 1).cpu().numpy(), xa.cpu().numpy())
+    assert np.array_equal(host_bits(one.k), host_bits(two.k)) and np.array_equal(host_bits(one.v), host_bits(two.v))
+
+
+def test_prefill_then_aux_start_matches_oracle():
+    """A prompt of n tokens: the primary prefills n - 1 of them, then the decode step with both
+    flows at the last position; against the oracle's composition of the same two steps."""
+    B, n, L = 2, 24, 2
+    vocab = 50
+    layers = [gen.layer_case(710 + l, batch=B, context=1, capacity=n + 8, **SMALL) for l in range(L)]
+    rng = np.random.default_rng(5)
+    e1 = gen.f32_to_bf16_bits(rng.standard_normal((vocab, SMALL["hidden"])).astype(np.float32))
+    e2 = gen.f32_to_bf16_bits(rng.standard_normal((vocab, SMALL["hidden"])).astype(np.float32))
+    tokens = rng.integers(0, vocab, (B, n)).astype(np.int32)
+    caches = [cache_of(Lc.cache) for Lc in layers]
+    ws = [dfx.LayerWeights.from_row_major(dev(Lc.g_attn), dev(Lc.w_qkv), dev(Lc.w_o), dev(Lc.g_mlp),
+                                          dev(Lc.w_gate_up), dev(Lc.w_down), Lc.num_q_heads, Lc.num_kv_heads,
+                                          Lc.head_dim, Lc.eps, dev(Lc.a), dev(Lc.b), dev(Lc.c)) for Lc in layers]
+    zero = dev(np.zeros(B, np.int32))
+    xp = dfx.prefill_step(dev(tokens[:, : n - 1].copy()), dev(e1), ws, caches, zero, n + 8)
+    ctx = dev(np.full(B, n, np.int32))
+    x_last = dfx.dual_flow_decode_step(dev(tokens[:, n - 1].copy()), dev(e1), dev(e2), ws, caches, ctx, n + 8)
+    torch.cuda.synchronize()
+    # oracle: the same composition
+    want_p, pools = prefill_step(tokens[:, : n - 1], e1, layers, np.zeros(B))
+    layer_close(xp.cpu().numpy(), want_p)
+    for Lc, (kp, vp) in zip(layers, pools):
+        Lc.cache.k_pool, Lc.cache.v_pool = kp, vp
+    want, _ = dual_flow_step(tokens[:, n - 1], e1, e2, layers, np.full(B, n - 1))
+    layer_close(x_last.cpu().numpy(), want)
