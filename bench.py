@@ -1,7 +1,7 @@
 """Benchmark of the dual-flow decode step on one MI355X.
 
 python bench.py [--steps K] [--warmup W]
-                [--workload layer|attn-b16|attn-ragged|attn-long|attn-fp32|step|head|moe]
+                [--workload layer|attn-b16|attn-ragged|attn-long|attn-fp32|step|head|moe|prefill]
 
 A step of the default workload is one full dual-flow decode layer (both flows, batch
 32, context 8192, hidden 4096, 32/8 heads x 128, SwiGLU 14336, paged bf16 cache of
@@ -18,7 +18,8 @@ CPU oracle timed on the host cores (a reported baseline, not a target).
 `step` times a whole decode step of a layer stack (token ids -> embeddings -> layers ->
 shared output head -> next token), eagerly and as a HIP-graph replay; `head` the output
 head alone (final norm, shared vocabulary projection, mixture, greedy token); `moe` the
-mixture-of-experts MLP block with router replay.
+mixture-of-experts MLP block with router replay; `prefill` one layer of primary-only prefill
+over a prompt chunk and its causal attention alone.
 """
 import argparse
 import hashlib
@@ -40,7 +41,10 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="layer",
-                   choices=["layer", "attn-b16", "attn-ragged", "attn-long", "attn-fp32", "step", "head", "moe"])
+                   choices=["layer", "attn-b16", "attn-ragged", "attn-long", "attn-fp32", "step", "head", "moe",
+                            "prefill"])
+    p.add_argument("--prompt", type=int, default=2048, help="prompt chunk of the 'prefill' workload")
+    p.add_argument("--prefill-batch", type=int, default=2, help="sequences of the 'prefill' workload")
     p.add_argument("--layers", type=int, default=8, help="layers of the 'step' workload")
     p.add_argument("--vocab", type=int, default=128256,
                    help="vocabulary of the 'step' and 'head' workloads (0: the step ends at the last layer)")
@@ -146,6 +150,8 @@ def main():
         return bench_head(args)
     if args.workload == "moe":
         return bench_moe(args)
+    if args.workload == "prefill":
+        return bench_prefill(args)
     if args.copy_calibration:
         n = args.copy_calibration - args.copy_calibration % 16
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -483,6 +489,68 @@ def bench_moe(args):
             "aux_fanout_4": {"ms": round(res[(2, 4)][0], 4), "experts_used": res[(2, 4)][2]},
             "primary_only": {"ms": round(res[(1, 2)][0], 4), "experts_used": res[(1, 2)][2]},
             "dual_over_single": round(ms / res[(1, 2)][0], 3)}
+    print(json.dumps(line))
+
+
+def bench_prefill(args):
+    """Primary-only prefill of a prompt chunk through one layer of the one-layer workload's shape
+    (hidden 4096, 32/8 heads x 128, SwiGLU 14336, paged bf16 cache of 16-token blocks), and its
+    causal attention alone; synthetic GPU-drawn weights and queries. Algorithmic flops: 2 per
+    weight per row for the projections, 4 * head_dim per (query head, query, attended key) for
+    attention (the hi/lo split the kernel uses for accuracy is not counted)."""
+    import torch
+
+    import dual_flow_shared_amd as dfx
+    torch.cuda.set_device(0)
+    gen_ = torch.Generator(device="cuda").manual_seed(55)
+    B, T, H, Hq, Hkv, D, I, bs = args.prefill_batch, args.prompt, 4096, 32, 8, 128, 14336, 16
+
+    def randn(*shape, std=0.02):
+        return (torch.randn(*shape, generator=gen_, device="cuda") * std).to(torch.bfloat16)
+
+    gains = lambda n: torch.rand(n, generator=gen_, device="cuda") * 0.2 + 0.9
+    w = dfx.LayerWeights.from_row_major(gains(H), randn((Hq + 2 * Hkv) * D, H), randn(H, Hq * D), gains(H),
+                                        randn(2 * I, H), randn(H, I), Hq, Hkv, D, 1e-5)
+    nblk = B * (T // bs + 1)
+    table = torch.randperm(nblk, generator=gen_, device="cuda").to(torch.int32).view(B, -1)
+    cache = dfx.KVCache(randn(nblk, Hkv, bs, D, std=1.0), randn(nblk, Hkv, bs, D, std=1.0), table)
+    cap = table.shape[1] * bs
+    start = torch.zeros(B, dtype=torch.int32, device="cuda")
+    x0 = torch.randn(B, T, H, generator=gen_, device="cuda")
+    x = x0.clone()
+    ws = dfx.Workspace()
+    stream = torch.cuda.current_stream()
+
+    def layer():
+        x.copy_(x0)
+        dfx.prefill_layer(x, w, cache, start, cap, workspace=ws)
+
+    q = torch.randn(B, T, Hq, D, generator=gen_, device="cuda")
+    attn = lambda: dfx.prefill_attn(q, cache, start, cap)
+    for _ in range(args.warmup):
+        layer()
+        attn()
+    torch.cuda.synchronize()
+    ms = timed(layer, args.steps, stream)
+    attn_ms = timed(attn, args.steps, stream)
+    rows = B * T
+    wparams = (Hq + 2 * Hkv) * D * H + H * Hq * D + 2 * I * H + H * I
+    attn_flops = 4.0 * D * Hq * B * T * (T + 1) / 2
+    flops = 2.0 * rows * wparams + attn_flops
+    tf = flops / (ms * 1e-3) / 1e12
+    atf = attn_flops / (attn_ms * 1e-3) / 1e12
+    line = {"metric": "dual-flow prefill (primary only) tokens/s, one layer", "value": round(rows * 1000.0 / ms, 1),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"primary-only prefill: {B} sequences x {T}-token prompt chunk from position 0, "
+                                   f"one layer, hidden {H}, {Hq}/{Hkv} heads x {D}, SwiGLU {I}, paged bf16 cache",
+                       "batch": B, "prompt": T, "hidden": H},
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                         "frac": round(tf / 2500.0, 4), "traffic": None,
+                         "kernel": "whole prefill layer (8 launches); algorithmic flops of projections + causal attention",
+                         "flops_per_launch": flops},
+            "cpu_baseline": None,
+            "attention": {"ms": round(attn_ms, 4), "tflops": round(atf, 1), "frac_of_bf16_peak": round(atf / 2500.0, 4)}}
     print(json.dumps(line))
 
 

@@ -51,12 +51,18 @@ __device__ __forceinline__ void store_result(const AttnArgs &p, int split, int b
   }
 }
 
+#ifndef DFX_ATTN_WAVES
+#define DFX_ATTN_WAVES 4
+#endif
+constexpr int kAttnWaves = DFX_ATTN_WAVES;  // waves per work-group, interleaved over the tiles
+
 template <int D, bool QBF16, bool PAGED>
-__global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs p) {
+__global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) {
   constexpr int KS = D / 32;  // k-steps of the score contraction
   constexpr int VEC = D / 16; // head-dim elements one lane loads per V row; also O^T blocks
-  __shared__ float s_o[4][16][D];
-  __shared__ float s_m[4][16], s_l[4][16];
+  constexpr int W = kAttnWaves, NT = 64 * kAttnWaves;
+  __shared__ float s_o[W][16][D];
+  __shared__ float s_m[W][16], s_l[W][16];
   __shared__ int32_t s_tbl[kMaxChunkBlocks];
 
   const int g = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
@@ -114,14 +120,14 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs p) {
   const int first_blk = PAGED ? (start >> p.block_shift) : 0;
   if constexpr (PAGED) {
     const int nblk = end > start ? ((end - 1) >> p.block_shift) - first_blk + 1 : 0;
-    for (int i = threadIdx.x; i < nblk; i += 256) {
+    for (int i = threadIdx.x; i < nblk; i += NT) {
       const uint32_t e = (uint32_t)p.table[(int64_t)b * p.max_blocks + first_blk + i];
       s_tbl[i] = (uint64_t)e < (uint64_t)p.num_blocks ? (int32_t)e : (int32_t)(p.num_blocks - 1);
     }
   }
   __syncthreads();
 
-  // Tiles of a wave are 128 tokens apart (the four waves interleave). The next tile's K
+  // Tiles of a wave are 32 W tokens apart (the W waves interleave). The next tile's K
   // loads are issued as soon as this tile's scores have consumed the K registers, and
   // its V loads as soon as P.V has consumed the V registers. The steady-state loop has
   // no conditional loads, so the compiler can wait for exactly the loads it needs.
@@ -134,8 +140,8 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs p) {
     load_k<D>(kp, hb, lx, n, j, tr);
     load_v<D>(vp, hb, lx, n, j, tr);
     f32x4 sacc[2];
-    for (; t0 + 128 < end; t0 += 128) {
-      half_bases<PAGED>(p, s_tbl, first_blk, b, g, t0 + 128, end, hb, lx);
+    for (; t0 + 32 * W < end; t0 += 32 * W) {
+      half_bases<PAGED>(p, s_tbl, first_blk, b, g, t0 + 32 * W, end, hb, lx);
       tile_scores<D>(tr, qh, ql, sacc);
       load_k<D>(kp, hb, lx, n, j, tr);
       tile_softmax_pv<D>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
@@ -145,7 +151,7 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs p) {
     tile_softmax_pv<D>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
   }
 
-  // ---- combine the four waves (fixed order), then store output or split partial
+  // ---- combine the W waves (fixed order), then store output or split partial
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (j == 0) {
@@ -157,13 +163,15 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_o[wave][n][VEC * (4 * j + i) + mb] = oacc[mb][i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < R * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < R * D; idx += NT) {
     const int r = idx / D, d = idx % D;
-    float M = fmaxf(fmaxf(s_m[0][r], s_m[1][r]), fmaxf(s_m[2][r], s_m[3][r]));
+    float M = s_m[0][r];
+#pragma unroll
+    for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w][r]);
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float c = exp2f(s_m[w][r] - M);
         L += c * s_l[w][r];
         O += c * s_o[w][r][d];
@@ -177,7 +185,7 @@ hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s) {
   // The hardware hands work-group i to XCD i % 8. With the KV head fastest, XCD k serves
   // head k of every sequence (an equal share whatever the context lengths), and each XCD
   // dispatches all first splits (the longest pieces of ragged batches) before the later ones.
-  const dim3 grid(a.num_kv_heads, a.batch, a.num_splits), block(256);
+  const dim3 grid(a.num_kv_heads, a.batch, a.num_splits), block(64 * kAttnWaves);
   const bool paged = a.block_shift >= 0;
 #define DFX_ATTN_LAUNCH(D, QB, PG) attn_mfma_kernel<D, QB, PG><<<grid, block, 0, s>>>(a)
   if (a.head_dim == 128) {
