@@ -89,10 +89,21 @@ constexpr int kXSlot = 4 * 64;  // u32x4 per slot
 template <bool XF32, bool XPACKED, bool WPACKED>
 __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
   __shared__ u32x4 xs[2][kXSlot];
-  const int tile = blockIdx.x, ks = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
   const int F = p.n_flows, K = p.K, N = p.N;
+  const int ks = blockIdx.y;
+  int tile = blockIdx.x, gslice = blockIdx.z;
+  if (!p.expert_rows && p.group_split > 1) {
+    // one-dimensional grid, XCD-grouped: work-group i runs on XCD i % 8, and every group slice
+    // of a feature tile goes to the same XCD back to back, so the tile's weights stay in that
+    // XCD's L2 while the row groups pass over them
+    const int tiles = p.swiglu ? (N / 2 + 63) / 64 : (N + 127) / 128;
+    const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+    tile = xcd + 8 * (idx / p.group_split);
+    gslice = idx % p.group_split;
+    if (tile >= tiles) return;
+  }
   const int rpg = 64 / F;  // rows of each flow in one group
   int rows = p.rows;
   const void *px = p.x;
@@ -112,7 +123,7 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
   int g_begin = 0, g_end = groups;
   if (!p.expert_rows && p.group_split > 1) {
     const int per = (groups + p.group_split - 1) / p.group_split;
-    g_begin = blockIdx.z * per;
+    g_begin = gslice * per;
     g_end = min(groups, g_begin + per);
   }
   const int nks = K / 32, ng = N / 16;
@@ -286,8 +297,10 @@ __global__ void __launch_bounds__(256) grouped_linear_reduce_kernel(GemmArgs p) 
 }
 
 hipError_t launch_grouped_linear(const GemmArgs &g, hipStream_t s) {
-  const dim3 grid(g.swiglu ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128, g.ksplit,
-                  g.expert_rows ? g.experts : (g.group_split > 1 ? g.group_split : 1)),
+  const int tiles = g.swiglu ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;
+  const bool gsplit = !g.expert_rows && g.group_split > 1;  // one split, XCD-grouped 1-D grid
+  const dim3 grid(gsplit ? 8 * ((tiles + 7) / 8) * g.group_split : tiles, gsplit ? 1 : g.ksplit,
+                  g.expert_rows ? g.experts : 1),
       block(256);
 #define DFX_GL(XF, XP, WP) grouped_linear_kernel<XF, XP, WP><<<grid, block, 0, s>>>(g)
   if (g.x_packed) {
