@@ -932,10 +932,15 @@ dfx_status prefill_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int3
   return DFX_OK;
 }
 
-// One projection of the prefill rows (one flow, one split, every 64-row group its own
-// work-group slice): fp32 out (optionally plus residual, in place), or SwiGLU bf16 rows.
+// One projection of the prefill rows (one flow): the LDS-staged dense kernel when there is more
+// than one row group and K is a multiple of 128, else the grouped linear with every 64-row group
+// its own work-group slice. fp32 out (optionally plus residual, in place), or SwiGLU bf16 rows.
 dfx_status prefill_linear(int32_t rows, int32_t K, int32_t N, const uint16_t *x_packed, const uint16_t *w,
                           void *y, const float *residual, int swiglu, hipStream_t s) {
+  if (rows > 64 && prefill_gemm_fits(K, N, swiglu)) {
+    PrefillGemmArgs a{rows, K, N, x_packed, w, y, residual};
+    return hip_status(launch_prefill_gemm(a, swiglu, s), "prefill projection launch");
+  }
   GemmArgs g{};
   g.n_flows = 1; g.rows = rows; g.K = K; g.N = N; g.x_packed = 1; g.x = x_packed; g.w = w; g.w_packed = 1;
   g.y = y; g.residual = residual; g.ksplit = 1; g.kper = K / 32; g.swiglu = swiglu;

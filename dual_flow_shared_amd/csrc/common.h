@@ -246,6 +246,17 @@ struct PrefillGlueArgs {
   const int32_t *start;    // [B] position of each sequence's first new token
 };
 hipError_t launch_prefill_append(const PrefillGlueArgs &a, hipStream_t s);
+
+// Dense projection of many rows (prefill, one flow); packed operands as the grouped linear's.
+struct PrefillGemmArgs {
+  int32_t M, K, N;          // rows, in features, out features (gate/up mode: N = 2 I)
+  const uint16_t *x;        // packed rows [ceil(M / 64)][K / 32][4][64][8]
+  const uint16_t *w;        // packed [K / 32][N / 16][64][8]
+  void *y;                  // fp32 [M][N], or gate/up mode: bf16 packed rows with K = N / 2
+  const float *residual;    // [M][N] or NULL (may alias y)
+};
+bool prefill_gemm_fits(int32_t K, int32_t N, bool swiglu);
+hipError_t launch_prefill_gemm(const PrefillGemmArgs &a, bool swiglu, hipStream_t s);
 // packed_flows > 0: y in the fragment order of xpack_offset for that many flows (rows =
 // flows x batch); 0: row-major.
 hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,

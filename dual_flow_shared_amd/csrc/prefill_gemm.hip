@@ -1,0 +1,165 @@
+// Shared-weight projections of a prompt chunk (prefill, one flow): Y = bf16(X) W^T over many
+// rows, a dense contraction on the matrix cores.
+//
+// Operands are the grouped linear's packed layouts: W [K/32][N/16][64 lanes][8] (the A
+// fragment of a 16x16x32 bf16 MFMA for 16 output features and one 32-wide k-step, 1 KiB
+// contiguous) and X [M/64][K/32][4][64 lanes][8] (the B fragment of 16 rows likewise).
+// A work-group owns 256 output features x 128 rows as 2 x 2 waves of 128 features x 64 rows.
+// Per k-step it stages the 24 fragments it needs (16 of W, 8 of X; 24 KiB) in LDS, each loaded
+// once from global memory kDensePipe k-steps ahead through registers; every wave then reads its
+// 12 fragments from LDS and issues 32 MFMAs. LDS holds two k-steps (a barrier per k-step).
+//
+// Work-group i runs on XCD i % 8; all row tiles of one feature tile go to one XCD back to back,
+// so the tile's weights are fetched from HBM about once and re-read from that XCD's L2.
+//
+// Epilogues: fp32 rows [M][N] (plus a residual that may alias them), or, in gate/up mode, the
+// work-group's 256 features are 128 gate features and their 128 up features (the gate rows of
+// W come first) and it writes bf16 silu(gate) * up rows in the packed X layout of the next
+// projection (K = N / 2).
+#include "common.h"
+
+namespace dfx {
+
+constexpr int kDensePipe = 4;  // k-steps of fragments in flight per thread (registers)
+constexpr int kDenseFrags = 24;  // fragments per k-step: 16 of W, 8 of X
+
+template <bool SWIGLU>
+__global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillGemmArgs p) {
+  __shared__ u32x4 lds[2][kDenseFrags][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, j = lane >> 4;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int M = p.M, K = p.K, N = p.N;
+  const int nks = K / 32, ng = N / 16, ngh = ng / 2, groups = (M + 63) / 64;
+  const int RT = (groups + 1) / 2;
+  const int CT = SWIGLU ? (N / 2 + 127) / 128 : (N + 255) / 256;
+  const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+  const int ct = xcd + 8 * (idx / RT), rt = idx % RT;
+  if (ct >= CT) return;  // uniform for the work-group, before any barrier
+
+  // global feature group of the work-group's feature group fg (0..15)
+  auto wgroup = [&](int fg) {
+    if (SWIGLU) {
+      const int g = min(ct * 8 + (fg & 7), ngh - 1);
+      return fg < 8 ? g : g + ngh;
+    }
+    return min(ct * 16 + fg, ng - 1);
+  };
+  // this thread stages fragments f = wave + 4 r (r < 6), lane `lane` of each
+  const uint16_t *src[6];
+  int64_t sstep[6];
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const int f = wave + 4 * r;
+    if (f < 16) {
+      src[r] = p.w + ((int64_t)wgroup(f) * 64 + lane) * 8;
+      sstep[r] = (int64_t)ng * 512;
+    } else {
+      const int grp = min(2 * rt + (f - 16) / 4, groups - 1), nb = (f - 16) % 4;
+      src[r] = p.x + (((int64_t)grp * nks * 4 + nb) * 64 + lane) * 8;
+      sstep[r] = 4 * 512;
+    }
+  }
+  u32x4 stage[kDensePipe][6];
+  auto gload = [&](int s, u32x4 *d) {
+    const int sc = min(s, nks - 1);  // past the last k-step: re-read it (never used)
+#pragma unroll
+    for (int r = 0; r < 6; ++r) d[r] = *(const u32x4 *)(src[r] + sc * sstep[r]);
+  };
+  auto lstore = [&](int slot, const u32x4 *d) {
+#pragma unroll
+    for (int r = 0; r < 6; ++r) lds[slot][wave + 4 * r][lane] = d[r];
+  };
+  // this wave's fragments in LDS: W groups (gate/up mode: 4 gate and their 4 up groups)
+  int wfrag[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) wfrag[c] = SWIGLU ? (c < 4 ? 4 * wc + c : 8 + 4 * wc + c - 4) : 8 * wc + c;
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int u = 0; u < kDensePipe; ++u) gload(u, stage[u]);
+  lstore(0, stage[0]);
+  gload(kDensePipe, stage[0]);
+  __syncthreads();
+  // k-step s = base + u: LDS slot s & 1 holds it; stage[(u + 1) % kDensePipe] holds s + 1
+  for (int base = 0; base < nks; base += kDensePipe) {
+#pragma unroll
+    for (int u = 0; u < kDensePipe; ++u) {
+      const int s = base + u, slot = u & 1;  // kDensePipe is even
+      u32x4 wf[8], xf[4];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) wf[c] = lds[slot][wfrag[c]][lane];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) xf[nb] = lds[slot][16 + 4 * wr + nb][lane];
+      lstore(slot ^ 1, stage[(u + 1) % kDensePipe]);
+      gload(s + 1 + kDensePipe, stage[(u + 1) % kDensePipe]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[c][nb] = mfma16x16x32(as_bf16x8(wf[c]), as_bf16x8(xf[nb]), acc[c][nb]);
+      __syncthreads();
+    }
+  }
+
+  // C layout: lane holds row 16 nb + n of its group and features 16 cg + 4 j .. + 3
+  const int grp = 2 * rt + wr;
+  if (grp >= groups) return;
+  if constexpr (SWIGLU) {
+    const int I = N / 2;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int g = ct * 8 + 4 * wc + c;
+      if (g >= ngh) continue;
+      const int col = 16 * g + 4 * j;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int row = 64 * grp + 16 * nb + n;
+        if (row >= M) continue;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = silu(acc[c][nb][i]) * acc[c + 4][nb][i];
+        *(u32x2 *)((uint16_t *)p.y + xpack_offset(1, 0, row, col, I)) =
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int g = ct * 16 + 8 * wc + c;
+      if (g >= ng) continue;
+      const int col = 16 * g + 4 * j;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int row = 64 * grp + 16 * nb + n;
+        if (row >= M) continue;
+        const int64_t o = (int64_t)row * N + col;
+        f32x4 v = acc[c][nb];
+        if (p.residual) v += *(const f32x4 *)(p.residual + o);
+        *(f32x4 *)((float *)p.y + o) = v;
+      }
+    }
+  }
+}
+
+bool prefill_gemm_fits(int32_t K, int32_t N, bool swiglu) {
+  return K % (32 * kDensePipe) == 0 && N % (swiglu ? 32 : 16) == 0;
+}
+
+hipError_t launch_prefill_gemm(const PrefillGemmArgs &a, bool swiglu, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  const int groups = (a.M + 63) / 64, RT = (groups + 1) / 2;
+  const int CT = swiglu ? (a.N / 2 + 127) / 128 : (a.N + 255) / 256;
+  const int64_t per_xcd = (int64_t)((CT + 7) / 8) * RT;  // work-groups of the busiest XCD
+  const dim3 grid((unsigned)(8 * per_xcd)), block(256);
+  if (swiglu) prefill_gemm_kernel<true><<<grid, block, 0, s>>>(a);
+  else prefill_gemm_kernel<false><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace dfx
