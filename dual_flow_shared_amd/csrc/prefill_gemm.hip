@@ -4,18 +4,19 @@
 // Operands are the grouped linear's packed layouts: W [K/32][N/16][64 lanes][8] (the A
 // fragment of a 16x16x32 bf16 MFMA for 16 output features and one 32-wide k-step, 1 KiB
 // contiguous) and X [M/64][K/32][4][64 lanes][8] (the B fragment of 16 rows likewise).
-// A work-group owns 256 output features x 128 rows as 2 x 2 waves of 128 features x 64 rows.
-// Per k-step it stages the 24 fragments it needs (16 of W, 8 of X; 24 KiB) in LDS, each loaded
-// once from global memory kDensePipe k-steps ahead through registers; every wave then reads its
-// 12 fragments from LDS and issues 32 MFMAs. LDS holds two k-steps (a barrier per k-step).
+// A work-group owns 256 output features x 128 rows as 2 x 4 waves of 64 features x 64 rows
+// (two waves per SIMD, so one can issue MFMAs while the other waits). Per k-step it stages the 24
+// fragments it needs (16 of W, 8 of X; 24 KiB) in LDS, each loaded once from global memory
+// kDensePipe k-steps ahead through registers; every wave then reads its 8 fragments from LDS and
+// issues 16 MFMAs. LDS holds two k-steps (a barrier per k-step).
 //
 // Work-group i runs on XCD i % 8; all row tiles of one feature tile go to one XCD back to back,
 // so the tile's weights are fetched from HBM about once and re-read from that XCD's L2.
 //
 // Epilogues: fp32 rows [M][N] (plus a residual that may alias them), or, in gate/up mode, the
 // work-group's 256 features are 128 gate features and their 128 up features (the gate rows of
-// W come first) and it writes bf16 silu(gate) * up rows in the packed X layout of the next
-// projection (K = N / 2).
+// W come first; a wave holds 32 gate features and their up features) and it writes bf16
+// silu(gate) * up rows in the packed X layout of the next projection (K = N / 2).
 #include "common.h"
 
 namespace dfx {
@@ -23,12 +24,15 @@ namespace dfx {
 constexpr int kDensePipe = 4;  // k-steps of fragments in flight per thread (registers)
 constexpr int kDenseFrags = 24;  // fragments per k-step: 16 of W, 8 of X
 
+constexpr int kDenseWaves = 8;  // 2 row waves x 4 feature waves
+constexpr int kDenseStage = kDenseFrags * 64 / (64 * kDenseWaves);  // fragments a thread stages
+
 template <bool SWIGLU>
-__global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillGemmArgs p) {
+__global__ void __launch_bounds__(64 * kDenseWaves) prefill_gemm_kernel(PrefillGemmArgs p) {
   __shared__ u32x4 lds[2][kDenseFrags][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> 2, wc = wave & 3;  // row group of the tile, feature quarter
   const int M = p.M, K = p.K, N = p.N;
   const int nks = K / 32, ng = N / 16, ngh = ng / 2, groups = (M + 63) / 64;
   const int RT = (groups + 1) / 2;
@@ -45,12 +49,12 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillGemmArgs p) {
     }
     return min(ct * 16 + fg, ng - 1);
   };
-  // this thread stages fragments f = wave + 4 r (r < 6), lane `lane` of each
-  const uint16_t *src[6];
-  int64_t sstep[6];
+  // this thread stages fragments f = wave + kDenseWaves r, lane `lane` of each
+  const uint16_t *src[kDenseStage];
+  int64_t sstep[kDenseStage];
 #pragma unroll
-  for (int r = 0; r < 6; ++r) {
-    const int f = wave + 4 * r;
+  for (int r = 0; r < kDenseStage; ++r) {
+    const int f = wave + kDenseWaves * r;
     if (f < 16) {
       src[r] = p.w + ((int64_t)wgroup(f) * 64 + lane) * 8;
       sstep[r] = (int64_t)ng * 512;
@@ -60,24 +64,24 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillGemmArgs p) {
       sstep[r] = 4 * 512;
     }
   }
-  u32x4 stage[kDensePipe][6];
+  u32x4 stage[kDensePipe][kDenseStage];
   auto gload = [&](int s, u32x4 *d) {
     const int sc = min(s, nks - 1);  // past the last k-step: re-read it (never used)
 #pragma unroll
-    for (int r = 0; r < 6; ++r) d[r] = *(const u32x4 *)(src[r] + sc * sstep[r]);
+    for (int r = 0; r < kDenseStage; ++r) d[r] = *(const u32x4 *)(src[r] + sc * sstep[r]);
   };
   auto lstore = [&](int slot, const u32x4 *d) {
 #pragma unroll
-    for (int r = 0; r < 6; ++r) lds[slot][wave + 4 * r][lane] = d[r];
+    for (int r = 0; r < kDenseStage; ++r) lds[slot][wave + kDenseWaves * r][lane] = d[r];
   };
-  // this wave's fragments in LDS: W groups (gate/up mode: 4 gate and their 4 up groups)
-  int wfrag[8];
+  // this wave's weight fragments in LDS (gate/up mode: 2 gate groups and their 2 up groups)
+  int wfrag[4];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) wfrag[c] = SWIGLU ? (c < 4 ? 4 * wc + c : 8 + 4 * wc + c - 4) : 8 * wc + c;
+  for (int c = 0; c < 4; ++c) wfrag[c] = SWIGLU ? (c < 2 ? 2 * wc + c : 8 + 2 * wc + c - 2) : 4 * wc + c;
 
-  f32x4 acc[8][4];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
+  for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -91,15 +95,15 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillGemmArgs p) {
 #pragma unroll
     for (int u = 0; u < kDensePipe; ++u) {
       const int s = base + u, slot = u & 1;  // kDensePipe is even
-      u32x4 wf[8], xf[4];
+      u32x4 wf[4], xf[4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) wf[c] = lds[slot][wfrag[c]][lane];
+      for (int c = 0; c < 4; ++c) wf[c] = lds[slot][wfrag[c]][lane];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) xf[nb] = lds[slot][16 + 4 * wr + nb][lane];
       lstore(slot ^ 1, stage[(u + 1) % kDensePipe]);
       gload(s + 1 + kDensePipe, stage[(u + 1) % kDensePipe]);
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
           acc[c][nb] = mfma16x16x32(as_bf16x8(wf[c]), as_bf16x8(xf[nb]), acc[c][nb]);
@@ -113,8 +117,8 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillGemmArgs p) {
   if constexpr (SWIGLU) {
     const int I = N / 2;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int g = ct * 8 + 4 * wc + c;
+    for (int c = 0; c < 2; ++c) {
+      const int g = ct * 8 + 2 * wc + c;
       if (g >= ngh) continue;
       const int col = 16 * g + 4 * j;
 #pragma unroll
@@ -123,15 +127,15 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillGemmArgs p) {
         if (row >= M) continue;
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = silu(acc[c][nb][i]) * acc[c + 4][nb][i];
+        for (int i = 0; i < 4; ++i) v[i] = silu(acc[c][nb][i]) * acc[c + 2][nb][i];
         *(u32x2 *)((uint16_t *)p.y + xpack_offset(1, 0, row, col, I)) =
             u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int g = ct * 16 + 8 * wc + c;
+    for (int c = 0; c < 4; ++c) {
+      const int g = ct * 16 + 4 * wc + c;
       if (g >= ng) continue;
       const int col = 16 * g + 4 * j;
 #pragma unroll
@@ -156,7 +160,7 @@ hipError_t launch_prefill_gemm(const PrefillGemmArgs &a, bool swiglu, hipStream_
   const int groups = (a.M + 63) / 64, RT = (groups + 1) / 2;
   const int CT = swiglu ? (a.N / 2 + 127) / 128 : (a.N + 255) / 256;
   const int64_t per_xcd = (int64_t)((CT + 7) / 8) * RT;  // work-groups of the busiest XCD
-  const dim3 grid((unsigned)(8 * per_xcd)), block(256);
+  const dim3 grid((unsigned)(8 * per_xcd)), block(64 * kDenseWaves);
   if (swiglu) prefill_gemm_kernel<true><<<grid, block, 0, s>>>(a);
   else prefill_gemm_kernel<false><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
