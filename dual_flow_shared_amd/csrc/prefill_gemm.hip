@@ -21,7 +21,7 @@
 
 namespace dfx {
 
-constexpr int kDensePipe = 4;  // k-steps of fragments in flight per thread (registers)
+constexpr int kDensePipe = 2;  // k-steps of fragments in flight per thread (registers)
 constexpr int kDenseFrags = 24;  // fragments per k-step: 16 of W, 8 of X
 
 constexpr int kDenseWaves = 8;  // 2 row waves x 4 feature waves
