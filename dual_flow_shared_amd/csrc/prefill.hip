@@ -161,11 +161,144 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(AttnArgs p) {
   if (j == 0 && p.lse) p.lse[r * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
+// The same attention with the four waves' K/V tiles shared through LDS (head_dim 128, the
+// four heads of a work-group in one KV group). A tile's register image -- what load_k and
+// load_v leave in each lane: 8 K fragments and 8 V rows of 16 bytes -- is 16 components of 64
+// lanes; wave w loads components 4w .. 4w + 3 of the next tile from memory while all waves
+// multiply the current one from LDS, so each K/V byte is fetched once per work-group.
+__device__ __forceinline__ u32x4 tile_component(const uint16_t *kp, const uint16_t *vp, const int64_t *hb,
+                                                const int *lx, int n, int j, int c) {
+  constexpr int D = 128;
+  if (c < 8) {  // K fragment: 16-token half c / 4, head-dim chunk 4 (c % 4) + j of row n
+    const int mb = c >> 2, s = c & 3;
+    return kv_load<u32x4>(kp + hb[mb] + (int64_t)min(n, lx[mb]) * D + 8 * (4 * s + j));
+  }
+  const int v = c - 8, h = v >> 2, x = 4 * j + (v & 3);  // V row tau(j, v), elements 8n .. 8n + 7
+  return kv_load<u32x4>(vp + hb[h] + (int64_t)min(x, lx[h]) * D + 8 * n);
+}
+
+template <bool PAGED>
+__global__ void __launch_bounds__(256) prefill_attn_shared_kernel(AttnArgs p) {
+  constexpr int D = 128, KS = D / 32, VEC = D / 16;
+  __shared__ int32_t s_tbl[kMaxChunkBlocks];
+  __shared__ u32x4 s_img[2][16][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, j = lane >> 4;
+  const int h = blockIdx.x * 4 + wave, b = blockIdx.y;
+  const int tile = gridDim.z - 1 - blockIdx.z;  // the longest tiles are dispatched first
+  const int T = p.prefill_T, t0 = 16 * tile;
+  const int g = h / p.group;  // the same for the four waves (group % 4 == 0)
+  const int cap = p.max_context;
+  const int start = min(max(p.ctx[b], 0), cap);
+  const int rows = min(16, T - t0);
+  const int kend = max(min(start + t0 + rows, cap), 1);
+  const int my_end = n < rows ? min(start + t0 + n + 1, kend) : 1;
+
+  u32x4 qh[KS], ql[KS];
+  {
+    const bool valid = n < rows;
+    const int64_t qoff = ((int64_t)b * T + t0 + (valid ? n : 0)) * p.q_bstride + (int64_t)h * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float q[8];
+      load8<false>(p.q1, qoff + 8 * (4 * s + j), q);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t h0, l0, h1, l1;
+        split_bf16(valid ? q[2 * w] : 0.f, h0, l0);
+        split_bf16(valid ? q[2 * w + 1] : 0.f, h1, l1);
+        qh[s][w] = h0 | (h1 << 16);
+        ql[s][w] = l0 | (l1 << 16);
+      }
+    }
+  }
+  const uint16_t *kp = (const uint16_t *)p.k;
+  const uint16_t *vp = (const uint16_t *)p.v;
+  f32x4 oacc[VEC];
+#pragma unroll
+  for (int mb = 0; mb < VEC; ++mb) oacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int chunk_tok = PAGED ? (kMaxChunkBlocks << p.block_shift) : kend;
+  for (int cs = 0; cs < kend; cs += chunk_tok) {
+    const int ce = min(cs + chunk_tok, kend);
+    const int first_blk = PAGED ? (cs >> p.block_shift) : 0;
+    __syncthreads();  // the previous chunk's ids and images are no longer read
+    if constexpr (PAGED) {
+      const int nblk = ((ce - 1) >> p.block_shift) - first_blk + 1;
+      for (int i = threadIdx.x; i < nblk; i += 256) {
+        const uint32_t e = (uint32_t)p.table[(int64_t)b * p.max_blocks + first_blk + i];
+        s_tbl[i] = (uint64_t)e < (uint64_t)p.num_blocks ? (int32_t)e : (int32_t)(p.num_blocks - 1);
+      }
+      __syncthreads();
+    }
+    int64_t hb[2];
+    int lx[2];
+    u32x4 st[4];
+    half_bases<PAGED>(p, s_tbl, first_blk, b, g, cs, ce, hb, lx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st[i] = tile_component(kp, vp, hb, lx, n, j, 4 * wave + i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_img[0][4 * wave + i][lane] = st[i];
+    __syncthreads();
+    int slot = 0;
+    for (int t = cs; t < ce; t += 32) {
+      // the next tile's components (the current tile again after the last: never read)
+      const int tn = t + 32 < ce ? t + 32 : t;
+      half_bases<PAGED>(p, s_tbl, first_blk, b, g, tn, ce, hb, lx);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[i] = tile_component(kp, vp, hb, lx, n, j, 4 * wave + i);
+      TileRegs<D> tr;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) tr.kf[c >> 2][c & 3] = s_img[slot][c][lane];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const u32x4 y = s_img[slot][8 + v][lane];
+        tr.vr[v][0] = y[0]; tr.vr[v][1] = y[1]; tr.vr[v][2] = y[2]; tr.vr[v][3] = y[3];
+      }
+      f32x4 sacc[2];
+      tile_scores<D>(tr, qh, ql, sacc);
+      tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, m_run, l_run, oacc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_img[slot ^ 1][4 * wave + i][lane] = st[i];
+      __syncthreads();
+      slot ^= 1;
+    }
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (n >= rows) return;
+  const float inv = 1.0f / l_tot;
+  const int64_t r = (int64_t)b * T + t0 + n;
+  const int Hq = p.num_q_heads;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float o[VEC];
+#pragma unroll
+    for (int mb = 0; mb < VEC; ++mb) o[mb] = oacc[mb][i] * inv;
+    const int d0 = VEC * (4 * j + i);
+    if (p.o_packed) {
+      uint16_t *dst = (uint16_t *)p.o1 + xpack_offset(1, 0, (int)r, h * D + d0, Hq * D);
+      *(u32x4 *)dst = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                            pack_bf16x2(o[6], o[7])};
+    } else {
+      float *dst = p.o1 + (r * Hq + h) * D + d0;
+      *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
+      *(f32x4 *)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    }
+  }
+  if (j == 0 && p.lse) p.lse[r * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
+}
+
 hipError_t launch_prefill_attn(const AttnArgs &a, hipStream_t s) {
   if (a.batch == 0 || a.prefill_T == 0) return hipSuccess;
   const dim3 grid(a.num_q_heads / 4, a.batch, (a.prefill_T + 15) / 16), block(256);
   const bool paged = a.block_shift >= 0;
-  if (a.head_dim == 128) {
+  if (a.head_dim == 128 && a.group % 4 == 0) {
+    if (paged) prefill_attn_shared_kernel<true><<<grid, block, 0, s>>>(a);
+    else prefill_attn_shared_kernel<false><<<grid, block, 0, s>>>(a);
+  } else if (a.head_dim == 128) {
     if (paged) prefill_attn_kernel<128, true><<<grid, block, 0, s>>>(a);
     else prefill_attn_kernel<128, false><<<grid, block, 0, s>>>(a);
   } else {

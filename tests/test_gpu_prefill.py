@@ -30,6 +30,7 @@ def layer_close(y, want):
     (True, 128, 32, 8, 16, [5, 0]),
     (False, 64, 4, 4, 50, [3, 7]),         # contiguous cache, head_dim 64, no grouping
     (True, 128, 8, 1, 1, [40, 0]),         # one new position (a decode-shaped chunk)
+    (True, 128, 8, 4, 33, [2, 17]),        # two heads per KV head: the per-wave K/V kernel
 ])
 def test_prefill_attention(paged, D, Hq, Hkv, T, starts):
     B = len(starts)
