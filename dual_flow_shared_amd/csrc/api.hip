@@ -843,10 +843,9 @@ dfx_status dfx_dual_flow_moe_mlp(const dfx_moe_weights *w, int32_t batch, int32_
   uint16_t *inter = (uint16_t *)c;                c += p.inter;
   float *tiles = (float *)c;
   a.tiles = tiles; a.couple_c = F == 2 ? w->couple_c : nullptr; a.x = x;
-  dfx_status r = hip_status(launch_rmsnorm(F * B, H, x, w->norm_gain, w->rms_eps, (uint16_t *)a.h, s, 0),
-                            "rmsnorm launch");
+  a.gain = w->norm_gain; a.eps = w->rms_eps;
+  dfx_status r = hip_status(launch_moe(kMoeRoute, a, s), "norm + route launch");
   if (r) return r;
-  if ((r = hip_status(launch_moe(kMoeRoute, a, s), "route launch"))) return r;
   if ((r = hip_status(launch_moe(kMoeLists, a, s), "expert lists launch"))) return r;
   if ((r = hip_status(launch_moe(kMoeGather, a, s), "gather launch"))) return r;
   const size_t rows64 = (size_t)p.max_groups * 64;

@@ -233,6 +233,8 @@ struct MoeArgs {
   const float *tiles;        // [E][ksplit][max_groups][64][H]
   const float *couple_c;     // [H] or NULL
   float *x;                  // [F][B][H] residual rows, updated in place
+  const float *gain;         // [H] norm gain
+  float eps;
 };
 hipError_t launch_moe(int which, const MoeArgs &a, hipStream_t s);
 

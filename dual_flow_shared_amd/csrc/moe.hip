@@ -9,8 +9,8 @@
 // over them; b couples each expert's intermediate where the primary also ran the expert, c the
 // block output.
 //
-// Launches after the norm: route (per sequence: router logits of both flows, ranking,
-// weights) -> lists (per expert: the sequences that use it, in ascending order) -> gather
+// Launches: norm + route (per sequence: both flows' normed rows, their router logits, the
+// ranking, weights) -> lists (per expert: the sequences that use it, in ascending order) -> gather
 // (each expert's rows in the grouped linear's fragment order; a flow that did not select the
 // expert gets a zero row, so its intermediate is exactly zero) -> gate/up and down as the
 // grouped linear in expert mode (an expert's weights are read once for every row of both
@@ -20,16 +20,35 @@
 
 namespace dfx {
 
-// One work-group of 4 waves per sequence: wave w computes the router dot products
-// d = w, w + 4, ... of the F * E (flow, expert) pairs (lane slices of 8, fixed order, wave
-// butterfly); then wave 0 ranks the primary's logits by kmax rounds of a wave arg max and
-// lane 0 forms each flow's weights. NaN logits rank last.
-__global__ void __launch_bounds__(256) moe_route_kernel(MoeArgs a) {
+// One work-group of 16 waves per sequence: first both flows' rows are normalized (the shared
+// norm helpers, so the rounding is the RMSNorm kernel's) into h; then wave w computes the
+// router dot products d = w, w + 16, ... of the F * E (flow, expert) pairs (lane slices of 8,
+// fixed order, wave butterfly); then wave 0 ranks the primary's logits by kmax rounds of a
+// wave arg max and lane 0 forms each flow's weights. NaN logits rank last.
+__global__ void __launch_bounds__(1024) moe_route_kernel(MoeArgs a) {
+  __shared__ float red[2][16];
   __shared__ float lg[2][kMoeMaxExperts];
   __shared__ int32_t sel[kMoeMaxK];
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int F = a.F, E = a.E, H = a.H;
-  for (int d = wave; d < F * E; d += 4) {
+  for (int f = 0; f < F; ++f) {
+    const int64_t row = (int64_t)f * a.B + b;
+    const float *xr = a.x + row * H;
+    f32x4 v[kNormSlices], gg[kNormSlices];
+#pragma unroll
+    for (int u = 0; u < kNormSlices; ++u) {
+      const int i = threadIdx.x + 1024 * u;
+      v[u] = gg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (4 * i < H) {
+        v[u] = *(const f32x4 *)(xr + 4 * i);
+        gg[u] = *(const f32x4 *)(a.gain + 4 * i);
+      }
+    }
+    const float r = norm_scale(v, H, a.eps, red[f]);
+    norm_store(v, gg, r, H, (uint16_t *)a.h, 0, f, b, row);
+  }
+  __syncthreads();  // this work-group's normed rows are written
+  for (int d = wave; d < F * E; d += 16) {
     const int f = d / E, e = d % E;
     const uint16_t *hr = a.h + ((int64_t)f * a.B + b) * H;
     const uint16_t *wr = a.w_router + (int64_t)e * H;
@@ -46,7 +65,7 @@ __global__ void __launch_bounds__(256) moe_route_kernel(MoeArgs a) {
     if (lane == 0) lg[f][e] = acc;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < F * E; i += 256)
+  for (int i = threadIdx.x; i < F * E; i += 1024)
     a.logits[((int64_t)(i / E) * a.B + b) * E + i % E] = lg[i / E][i % E];
   if (wave != 0) return;
   const int kmax = F == 2 ? max(a.k1, a.k2) : a.k1;
@@ -198,7 +217,7 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(MoeArgs a) {
 hipError_t launch_moe(int which, const MoeArgs &a, hipStream_t s) {
   switch (which) {
     case kMoeRoute:
-      moe_route_kernel<<<a.B, 256, 0, s>>>(a);
+      moe_route_kernel<<<a.B, 1024, 0, s>>>(a);
       break;
     case kMoeLists:
       moe_lists_kernel<<<1, 1024, (size_t)a.E * ((a.B + 31) / 32) * sizeof(uint32_t), s>>>(a);
