@@ -100,6 +100,21 @@ def timed(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
+def timed_each(fn, reps, stream):
+    """Per-call durations (ms) of reps back-to-back calls, an event pair around each."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    with torch.cuda.stream(stream):
+        fn()
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
 def source_sha(name):
     path = os.path.join(ROOT, "dual_flow_shared_amd", "csrc", name)
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
@@ -262,6 +277,9 @@ def main():
 
     attn_ms = timed(attn_call, args.kernel_reps, stream)
     single_ms = timed(lambda: attn_call(None, None), args.kernel_reps, stream)
+    each = np.array(timed_each(attn_call, args.kernel_reps, stream))
+    extra["attn_ms_each"] = {"median": round(float(np.median(each)), 4), "p10": round(float(np.percentile(each, 10)), 4),
+                             "p90": round(float(np.percentile(each, 90)), 4), "calls": int(each.size)}
     abytes = attn_bytes(shape, ctx_np, F, 4 if args.workload == "layer" else shape["kv_el"])
     achieved = abytes / (attn_ms * 1e-3) / 1e9
     splits, _ = dfx.decode_attn_plan(kv, B, shape["Hq"], F, mc, args.splits)
