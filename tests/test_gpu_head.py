@@ -170,3 +170,12 @@ def test_head_full_size_sampled():
                                      tok, np.arange(8), np.arange(128256 - 8, 128256)]))
     check_logits(c, h, logits, cols)
     check_mixture(logits, tok, alpha, pm)
+
+
+def test_head_smallest_vocabulary():
+    """vocab 16: one 16-wide projection tile, one partial mixture chunk."""
+    c = gen.head_case(915, 2, 3, 64, 16, w_std=0.5)
+    tok, alpha, pm, h, logits, _ = run(c, 2)
+    check_logits(c, h, logits)
+    check_mixture(logits, tok, alpha, pm)
+    assert np.allclose(pm.sum(-1), 1.0, atol=1e-5)

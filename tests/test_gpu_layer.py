@@ -240,3 +240,13 @@ def test_full_size_layer_sampled():
     assert np.all(np.isfinite(y))
     changed = np.argwhere(np.any(kp != c.cache.k_pool, axis=-1))
     assert len(changed) == c.batch * c.num_kv_heads
+
+
+@pytest.mark.parametrize("flows", [2, 1])
+def test_layer_single_sequence(flows):
+    # one sequence: a 64-row group holding one row per flow, context 1 (the appended token only)
+    c = gen.layer_case(806, batch=1, context=1, hidden=256, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                       intermediate=512, w_std=0.05)
+    y, kp, _ = check_layer_chain(c, flows=flows)
+    layer_close(y, run_oracle(c, flows=flows)[0])
+    assert np.sum(np.any(kp != c.cache.k_pool, axis=-1)) == c.num_kv_heads

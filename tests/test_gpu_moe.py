@@ -217,3 +217,10 @@ def test_moe_full_size_sampled():
     c = gen.moe_case(975, 32, hidden=4096, num_experts=8, intermediate=14336, router_std=0.02)
     cols = np.random.default_rng(2).choice(4096, 96, replace=False)
     check_chain(c, 2, 2, 2, rows=[0, 13, 31], cols=cols)
+
+
+def test_moe_largest_fanouts():
+    """64 experts, the primary on 8 and the auxiliary on 16 (the largest fan-out), 6 sequences."""
+    c = gen.moe_case(976, 6, hidden=128, num_experts=64, intermediate=64, router_std=0.3, w_std=0.05)
+    g = check_chain(c, 2, 8, 16)
+    assert np.all(g["ids"][1, :, :16] >= 0) and np.all(g["ids"][0, :, 8:] == -1)
