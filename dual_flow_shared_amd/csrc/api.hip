@@ -876,6 +876,7 @@ dfx_status check_prefill(const dfx_kv_cache *kv, int32_t B, int32_t T, int32_t m
   if (st) return st;
   if (B < 0 || B > 65535 || T < 0) return fail(DFX_EINVAL, "batch %d chunk %d", B, T);
   if ((int64_t)B * T > (int64_t)1 << 22) return fail(DFX_EUNSUPPORTED, "batch * chunk above 2^22 rows");
+  if (T > 65535 * 16) return fail(DFX_EUNSUPPORTED, "chunk %d above %d positions (16 per grid row)", T, 65535 * 16);
   if (kv->dtype != DFX_BF16) return fail(DFX_EUNSUPPORTED, "prefill needs a bf16 cache");
   if (kv->block_table && kv->block_size < 16)
     return fail(DFX_EUNSUPPORTED, "prefill needs paged blocks of >= 16 tokens (got %d)", kv->block_size);

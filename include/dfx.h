@@ -457,8 +457,9 @@ dfx_status dfx_dual_flow_moe_mlp(const dfx_moe_weights *w, int32_t batch, int32_
  * then dfx_dual_flow_decode_step at position n-1 with both flows. A chunk holds `chunk` new
  * positions of every sequence; start_pos[b] (device int32 [batch]) is the position of
  * sequence b's first new token, and start_pos[b] + chunk <= max_context <= the cache's capacity.
- * The cache must be bf16, paged blocks >= 16 tokens; num_q_heads a multiple of 4. Positions
- * and block ids are clamped on the device like the decode calls'.
+ * The cache must be bf16, paged blocks >= 16 tokens; num_q_heads a multiple of 4; batch * chunk
+ * at most 2^22 rows and chunk at most 1048560 positions. Positions and block ids are clamped on
+ * the device like the decode calls'.
  *
  * dfx_prefill_attn: causal attention of the new positions, whose keys and values are already
  * in the cache: query t of sequence b attends to positions [0, start_pos[b] + t].

@@ -296,6 +296,8 @@ def test_prefill_rejects():
     assert lib.dfx_prefill_attn(ctypes.byref(k), FAKE, 2, 16, 64, 32, FAKE + 4, 0, FAKE, None, None) == 1
     assert lib.dfx_prefill_attn(ctypes.byref(k), FAKE, 2, 16, 64, 30, FAKE, 0, FAKE, None, None) == 2    # heads
     assert lib.dfx_prefill_attn(ctypes.byref(k), FAKE, 1 << 16, 16, 64, 32, FAKE, 0, FAKE, None, None) == 1
+    kbig = kv(mb=1 << 17, nb=1 << 17)
+    assert lib.dfx_prefill_attn(ctypes.byref(kbig), FAKE, 1, 65535 * 16 + 1, 1 << 21, 32, FAKE, 0, FAKE, None, None) == 2
     W = _abi.LayerWeightsStruct * 1
     K = _abi.KVCacheStruct * 1
     ws, ks = W(), K()
