@@ -275,6 +275,11 @@ dfx_status run_attn(const AttnCall &c, hipStream_t s) {
   a.scale_log2 = scale * kLog2e;
   a.o1 = c.o1; a.o2 = c.o2; a.lse = c.lse; a.o_bf16 = c.o_bf16 != 0; a.o_packed = c.o_bf16 == 2;
   a.num_splits = splits; a.chunk = chunk;
+  // K tiles through LDS as whole rows at >= 2 (sequence, KV head) pairs per CU, where the
+  // whole-row loads stream faster (measured: B64 ragged 1k-16k paged, 412 -> 388 us); with
+  // fewer pairs the direct A-operand loads are as fast or slightly faster (B32 x 8192 paged
+  // 165 vs 167 us, B16 x 4096 contiguous 49.6 vs 50.5 us, B8 x 131072 the same).
+  a.k_rows = c.batch * kv->num_kv_heads >= 2 * kTargetAttnGroups;
   if (splits > 1) {
     const size_t rows = (size_t)splits * F * c.batch * c.hq;
     a.part_o = (float *)c.ws;

@@ -54,9 +54,50 @@ __device__ __forceinline__ void store_result(const AttnArgs &p, int split, int b
 #ifndef DFX_ATTN_WAVES
 #define DFX_ATTN_WAVES 4
 #endif
+
+// K through LDS (AttnArgs::k_rows): a wave loads its tile's K rows with whole-row accesses (one
+// load instruction covers 64 x 16 contiguous bytes, D / 8 lanes per row), writes them to a padded
+// row-major LDS area of its own, and reads them back in the MFMA A-operand order (row n, head-dim
+// chunk 4 s + j). The direct path reads the A operand straight from memory, 16 rows x 64 bytes per
+// instruction. Which one streams faster depends on the launch; the planner picks.
+template <int D>
+struct KRows {
+  static constexpr int CPR = D / 8;         // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;      // rows per load instruction
+  static constexpr int NI = 2 * 16 / RPI;   // load instructions per 32-token tile
+};
+
+template <int D>
+__device__ __forceinline__ void load_k_rows(const uint16_t *kp, const int64_t *hb, const int *lastx, int lane,
+                                            u32x4 *kr) {
+  using R = KRows<D>;
+#pragma unroll
+  for (int i = 0; i < R::NI; ++i) {
+    const int mb = i / (R::NI / 2), tok = (i % (R::NI / 2)) * R::RPI + lane / R::CPR;
+    kr[i] = kv_load<u32x4>(kp + hb[mb] + (int64_t)min(tok, lastx[mb]) * D + 8 * (lane % R::CPR));
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_k_rows(u32x4 (*sk)[KRows<D>::CPR + 1], int lane, const u32x4 *kr) {
+  using R = KRows<D>;
+#pragma unroll
+  for (int i = 0; i < R::NI; ++i) {
+    const int mb = i / (R::NI / 2), tok = (i % (R::NI / 2)) * R::RPI + lane / R::CPR;
+    sk[16 * mb + tok][lane % R::CPR] = kr[i];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void read_k_frags(u32x4 (*sk)[KRows<D>::CPR + 1], int n, int j, TileRegs<D> &r) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) r.kf[mb][s] = sk[16 * mb + n][4 * s + j];
+}
 constexpr int kAttnWaves = DFX_ATTN_WAVES;  // waves per work-group, interleaved over the tiles
 
-template <int D, bool QBF16, bool PAGED>
+template <int D, bool QBF16, bool PAGED, bool KROWS>
 __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) {
   constexpr int KS = D / 32;  // k-steps of the score contraction
   constexpr int VEC = D / 16; // head-dim elements one lane loads per V row; also O^T blocks
@@ -64,6 +105,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) 
   __shared__ float s_o[W][16][D];
   __shared__ float s_m[W][16], s_l[W][16];
   __shared__ int32_t s_tbl[kMaxChunkBlocks];
+  __shared__ u32x4 s_k[KROWS ? W : 1][32][KRows<D>::CPR + 1];  // each wave's K rows of its tile
 
   const int g = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -137,15 +179,32 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) 
     int64_t hb[2];
     int lx[2];
     half_bases<PAGED>(p, s_tbl, first_blk, b, g, t0, end, hb, lx);
-    load_k<D>(kp, hb, lx, n, j, tr);
-    load_v<D>(vp, hb, lx, n, j, tr);
     f32x4 sacc[2];
-    for (; t0 + 32 * W < end; t0 += 32 * W) {
-      half_bases<PAGED>(p, s_tbl, first_blk, b, g, t0 + 32 * W, end, hb, lx);
-      tile_scores<D>(tr, qh, ql, sacc);
-      load_k<D>(kp, hb, lx, n, j, tr);
-      tile_softmax_pv<D>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
+    if constexpr (KROWS) {
+      u32x4 kr[KRows<D>::NI];
+      load_k_rows<D>(kp, hb, lx, lane, kr);
       load_v<D>(vp, hb, lx, n, j, tr);
+      store_k_rows<D>(s_k[wave], lane, kr);
+      for (; t0 + 32 * W < end; t0 += 32 * W) {
+        half_bases<PAGED>(p, s_tbl, first_blk, b, g, t0 + 32 * W, end, hb, lx);
+        read_k_frags<D>(s_k[wave], n, j, tr);
+        tile_scores<D>(tr, qh, ql, sacc);
+        load_k_rows<D>(kp, hb, lx, lane, kr);
+        tile_softmax_pv<D>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
+        load_v<D>(vp, hb, lx, n, j, tr);
+        store_k_rows<D>(s_k[wave], lane, kr);  // after this wave's reads of the current rows
+      }
+      read_k_frags<D>(s_k[wave], n, j, tr);
+    } else {
+      load_k<D>(kp, hb, lx, n, j, tr);
+      load_v<D>(vp, hb, lx, n, j, tr);
+      for (; t0 + 32 * W < end; t0 += 32 * W) {
+        half_bases<PAGED>(p, s_tbl, first_blk, b, g, t0 + 32 * W, end, hb, lx);
+        tile_scores<D>(tr, qh, ql, sacc);
+        load_k<D>(kp, hb, lx, n, j, tr);
+        tile_softmax_pv<D>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
+        load_v<D>(vp, hb, lx, n, j, tr);
+      }
     }
     tile_scores<D>(tr, qh, ql, sacc);
     tile_softmax_pv<D>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
@@ -187,7 +246,11 @@ hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s) {
   // dispatches all first splits (the longest pieces of ragged batches) before the later ones.
   const dim3 grid(a.num_kv_heads, a.batch, a.num_splits), block(64 * kAttnWaves);
   const bool paged = a.block_shift >= 0;
-#define DFX_ATTN_LAUNCH(D, QB, PG) attn_mfma_kernel<D, QB, PG><<<grid, block, 0, s>>>(a)
+#define DFX_ATTN_LAUNCH(D, QB, PG)                                           \
+  do {                                                                       \
+    if (a.k_rows) attn_mfma_kernel<D, QB, PG, true><<<grid, block, 0, s>>>(a); \
+    else attn_mfma_kernel<D, QB, PG, false><<<grid, block, 0, s>>>(a);         \
+  } while (0)
   if (a.head_dim == 128) {
     if (a.q_bf16) { if (paged) DFX_ATTN_LAUNCH(128, true, true); else DFX_ATTN_LAUNCH(128, true, false); }
     else { if (paged) DFX_ATTN_LAUNCH(128, false, true); else DFX_ATTN_LAUNCH(128, false, false); }

@@ -137,6 +137,7 @@ struct AttnArgs {
   int32_t o_packed;  // bf16 rows in the grouped linear's fragment order, both flows in o1
   float *part_o, *part_lse;  // [S][F][B][Hq][D], [S][F][B][Hq] (log2 domain)
   int32_t num_splits, chunk;
+  int32_t k_rows;  // matrix-core decode: stage K tiles through LDS as whole rows
   // prefill (primary only): T query positions per sequence, ctx[b] = position of the first;
   // q1 rows are (b, t) with row stride q_bstride
   int32_t prefill_T;

@@ -70,6 +70,21 @@ def test_small_shapes(shape, per_head):
     assert o2 is None and max_err(o1, w1) < TOL[dt]
 
 
+@pytest.mark.parametrize("D,paged,q_dtype", [(128, True, "bf16"), (64, True, "bf16"), (128, False, "bf16"),
+                                            (64, False, "f32")])
+def test_large_batch_whole_row_k_tiles(D, paged, q_dtype):
+    """At 512 or more (sequence, KV head) pairs the kernel stages K tiles through LDS as whole
+    rows: ragged lengths with empty, one-token and tail-tile sequences, both layouts."""
+    B, Hkv = 128, 4
+    ctx = np.random.default_rng(D + paged).integers(1, 300, B).astype(np.int32)
+    ctx[:4] = [0, 1, 31, 33]
+    case = gen.attention_case(620 + D + paged, B, 8, Hkv, D, ctx, dtype="bf16", paged=paged)
+    if q_dtype == "f32":  # fp32 queries (the same values) against the bf16 cache
+        case.q1, case.q2 = gen.bf16_bits_to_f32(case.q1), gen.bf16_bits_to_f32(case.q2)
+    check(case, run_attn(case), oracle(case))
+    check(case, run_attn(case, num_splits=3), oracle(case))
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 32])
 def test_split_counts(splits):
     case = gen.attention_case(601, 3, 32, 8, 128, [4096, 1500, 3001], dtype="bf16", paged=True)
