@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--splits", type=int, default=0, help="attention context splits (0 = plan)")
     p.add_argument("--kernel-reps", type=int, default=20)
+    p.add_argument("--no-split-sweep", action="store_true",
+                   help="skip timing dual and single flow at each split count (own-best-split ratio)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run the plain copy kernel on BYTES (5 launches): the reference "
                         "for scaling hardware traffic counters")
@@ -280,6 +282,24 @@ def main():
     each = np.array(timed_each(attn_call, args.kernel_reps, stream))
     extra["attn_ms_each"] = {"median": round(float(np.median(each)), 4), "p10": round(float(np.percentile(each, 10)), 4),
                              "p90": round(float(np.percentile(each, 90)), 4), "calls": int(each.size)}
+    if not args.no_split_sweep:
+        # dual and single flow, each at its own best split count (the ratio above uses the plan's)
+        max_s = max(1, -(-mc // 128))
+        # the split counts the planner actually runs for each request (long contexts cap the chunk)
+        cands = sorted({dfx.decode_attn_plan(kv, B, shape["Hq"], F, mc, c)[0]
+                        for c in (0, 1, 2, 3, 4, 6, 8, 12, 16, 32) if c <= max_s})
+        best = {}
+        for name, fn in (("dual", lambda s_: dfx.decode_attn(q1, q2, a, cache=caches[next(turn)], context_lens=ctx_t,
+                                                             max_context=mc, num_splits=s_, want_lse=False,
+                                                             workspace=aws)),
+                         ("single", lambda s_: dfx.decode_attn(q1, None, None, cache=caches[next(turn)],
+                                                               context_lens=ctx_t, max_context=mc, num_splits=s_,
+                                                               want_lse=False, workspace=aws))):
+            t = {c: timed(lambda: fn(c), args.kernel_reps, stream) for c in cands}
+            c = min(t, key=t.get)
+            best[name] = {"splits": c, "ms": round(t[c], 4)}
+        best["ratio"] = round(best["dual"]["ms"] / best["single"]["ms"], 3)
+        extra["attn_best_split"] = best
     abytes = attn_bytes(shape, ctx_np, F, 4 if args.workload == "layer" else shape["kv_el"])
     achieved = abytes / (attn_ms * 1e-3) / 1e9
     splits, _ = dfx.decode_attn_plan(kv, B, shape["Hq"], F, mc, args.splits)

@@ -35,6 +35,11 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kChunkQuantum = 128;  // tokens: 4 waves x 32-token tiles
 constexpr int kMinChunk = 1024;   // tokens: shorter splits cost more in merge than they gain
+// The vector-ALU kernel walks its split one 32-token tile after another, a memory round trip
+// each, so it takes splits of a tile or more: at batch 1 x 512 fp32 tokens, 1 split 136 us,
+// 4 splits 41 us.
+constexpr int kValuQuantum = 32;
+constexpr int kValuMinChunk = 32;
 constexpr int kMaxChunk = 8192;   // tokens: longer splits leave CUs idle when lengths differ
                                   // (doubled for small batches, see attn_plan)
 constexpr int kMaxChunkLargeBatch = 3072;  // tokens, at >= 2 (sequence, KV head) pairs per CU
@@ -80,14 +85,24 @@ int64_t capacity(const dfx_kv_cache *kv) {
 // most kMaxChunkBlocks - 1 whole blocks (the kernel holds the split's block ids in LDS).
 constexpr int kMaxChunkBlocks = 1024;
 
-void attn_plan(int batch, int hkv, int max_ctx, int requested, int block_size, int *splits,
-               int *chunk) {
-  const int max_s = max_ctx > 0 ? (max_ctx + kChunkQuantum - 1) / kChunkQuantum : 1;
-  // Splits start at multiples of kChunkQuantum, so with blocks of at most that many tokens
-  // a split covers whole blocks and may span all kMaxChunkBlocks of them.
-  const int64_t cap = block_size <= 0 ? (int64_t)1 << 30
-      : block_size <= kChunkQuantum ? (int64_t)kMaxChunkBlocks * block_size
-      : ((int64_t)(kMaxChunkBlocks - 1) * block_size) / kChunkQuantum * kChunkQuantum;
+// The matrix-core kernel serves bf16 caches with at most 16 query rows per KV head and paged
+// blocks of >= 16 tokens (a 16-token half tile then lies in one block); the rest runs on the
+// vector-ALU kernel.
+bool attn_mfma_path(const dfx_kv_cache *kv, int n_flows, int group) {
+  return kv->dtype == DFX_BF16 && n_flows * group <= 16 && (!kv->block_table || kv->block_size >= 16);
+}
+
+void attn_plan(int batch, int hkv, int max_ctx, int requested, int block_size, bool mfma,
+               int *splits, int *chunk) {
+  const int quantum = mfma ? kChunkQuantum : kValuQuantum;
+  const int min_chunk = mfma ? kMinChunk : kValuMinChunk;
+  const int max_s = max_ctx > 0 ? (max_ctx + quantum - 1) / quantum : 1;
+  // Splits start at multiples of the quantum. The matrix-core kernel stages a split's block
+  // ids in LDS: with blocks of at most a quantum a split covers whole blocks and may span
+  // all kMaxChunkBlocks of them. The vector-ALU kernel reads the table directly.
+  const int64_t cap = block_size <= 0 || !mfma ? (int64_t)1 << 30
+      : block_size <= quantum ? (int64_t)kMaxChunkBlocks * block_size
+      : ((int64_t)(kMaxChunkBlocks - 1) * block_size) / quantum * quantum;
   int s;
   if (requested > 0) {
     s = requested < max_s ? requested : max_s;
@@ -104,13 +119,13 @@ void attn_plan(int batch, int hkv, int max_ctx, int requested, int block_size, i
                           : pairs >= kTargetAttnGroups ? kMaxChunk : 2 * kMaxChunk;
     const int by_max = (max_ctx + max_chunk - 1) / max_chunk;
     if (s < by_max) s = by_max;
-    const int by_min = max_ctx > kMinChunk ? (max_ctx + kMinChunk - 1) / kMinChunk : 1;
+    const int by_min = max_ctx > min_chunk ? (max_ctx + min_chunk - 1) / min_chunk : 1;
     if (s > by_min) s = by_min;
     if (s > max_s) s = max_s;
     if (s < 1) s = 1;
   }
-  int64_t c = max_ctx > 0 ? (max_ctx + s - 1) / s : kChunkQuantum;
-  c = (c + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
+  int64_t c = max_ctx > 0 ? (max_ctx + s - 1) / s : quantum;
+  c = (c + quantum - 1) / quantum * quantum;
   if (c > cap) c = cap;
   *chunk = (int)c;
   *splits = max_ctx > 0 ? (int)((max_ctx + c - 1) / c) : 1;
@@ -257,7 +272,8 @@ dfx_status run_attn(const AttnCall &c, hipStream_t s) {
   const dfx_kv_cache *kv = c.kv;
   const int F = c.q2 ? 2 : 1, G = c.hq / kv->num_kv_heads;
   int splits, chunk;
-  attn_plan(c.batch, kv->num_kv_heads, c.max_context, c.splits, paged_bs(kv), &splits, &chunk);
+  const bool mfma = attn_mfma_path(kv, F, G);
+  attn_plan(c.batch, kv->num_kv_heads, c.max_context, c.splits, paged_bs(kv), mfma, &splits, &chunk);
   const size_t need = attn_ws_bytes(splits, F, c.batch, c.hq, kv->head_dim);
   if (need && (!c.ws || c.ws_bytes < need))
     return fail(DFX_EWORKSPACE, "decode_attn needs %zu workspace bytes for %d splits, got %zu", need, splits, c.ws_bytes);
@@ -285,9 +301,6 @@ dfx_status run_attn(const AttnCall &c, hipStream_t s) {
     a.part_o = (float *)c.ws;
     a.part_lse = (float *)((char *)c.ws + round_up(rows * kv->head_dim * sizeof(float), 256));
   }
-  // matrix-core path: bf16 cache, at most 16 query rows per KV head, paged blocks of
-  // >= 16 tokens (a 16-token half tile then lies in one block)
-  const bool mfma = a.kv_bf16 && F * G <= 16 && (!kv->block_table || kv->block_size >= 16);
   hipError_t e = mfma ? launch_attn_mfma(a, s) : launch_attn_valu(a, s);
   if (e != hipSuccess) return hip_status(e, "decode_attn launch");
   if (splits > 1) return hip_status(launch_attn_merge(a, s), "decode_attn merge launch");
@@ -315,7 +328,9 @@ dfx_status dfx_decode_attn_plan(const dfx_kv_cache *kv, int32_t batch, int32_t n
     return fail(DFX_EINVAL, "bad plan arguments");
   if (max_context > capacity(kv)) return fail(DFX_EINVAL, "max_context above cache capacity");
   int s, c;
-  attn_plan(batch, kv->num_kv_heads, max_context, num_splits, paged_bs(kv), &s, &c);
+  const int G = num_q_heads % kv->num_kv_heads == 0 ? num_q_heads / kv->num_kv_heads : 32;
+  attn_plan(batch, kv->num_kv_heads, max_context, num_splits, paged_bs(kv), attn_mfma_path(kv, n_flows, G),
+            &s, &c);
   if (splits_out) *splits_out = s;
   if (workspace_bytes) *workspace_bytes = attn_ws_bytes(s, n_flows, batch, num_q_heads, kv->head_dim);
   return DFX_OK;
@@ -464,7 +479,8 @@ dfx_status layer_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_
   p.h2 = a256(prow * H * 2);               // normed rows entering W_gate_up
   p.inter = a256(prow * I * 2);            // SwiGLU rows entering W_down
   int chunk;
-  attn_plan(B, kv->num_kv_heads, max_context, 0, paged_bs(kv), &p.splits, &chunk);
+  attn_plan(B, kv->num_kv_heads, max_context, 0, paged_bs(kv), attn_mfma_path(kv, F, Hq / kv->num_kv_heads),
+            &p.splits, &chunk);
   p.attn_ws = a256(attn_ws_bytes(p.splits, F, B, Hq, D));
   // the projections followed by a finish kernel write their fp32 tiles
   // [ksplit][groups][64][N]; they run in stream order, so one region serves them all

@@ -68,16 +68,37 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs p) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 
+  // The next tile's K/V elements are loaded into registers while the current tile is
+  // multiplied. Thread tid holds elements tid + 256 i of the [kT][D] tile; tokens past the
+  // split re-read its last token and are zeroed when stored.
+  constexpr int kPer = kT * kMaxD / 256;
+  float kn[kPer], vn[kPer];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < kT * D) {
+        const int t = idx / D, d = idx % D;
+        const int64_t row = kv_row_v(p, b, g, min(t0 + t, end - 1));
+        kn[i] = ld<KVBF16>(p.k, row + d);
+        vn[i] = ld<KVBF16>(p.v, row + d);
+      }
+    }
+  };
+  if (start < end) load_tile(start);
   for (int t0 = start; t0 < end; t0 += kT) {
     __syncthreads();
-    for (int idx = tid; idx < kT * D; idx += 256) {
-      const int t = idx / D, d = idx % D;
-      const int tok = t0 + t;
-      const int64_t row = kv_row_v(p, b, g, min(tok, ctx - 1));
-      const bool ok = tok < end;
-      k_s[t][d] = ok ? ld<KVBF16>(p.k, row + d) : 0.f;
-      v_s[t][d] = ok ? ld<KVBF16>(p.v, row + d) : 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < kT * D) {
+        const int t = idx / D, d = idx % D;
+        const bool ok = t0 + t < end;
+        k_s[t][d] = ok ? kn[i] : 0.f;
+        v_s[t][d] = ok ? vn[i] : 0.f;
+      }
     }
+    if (t0 + kT < end) load_tile(t0 + kT);
     __syncthreads();
     for (int idx = tid; idx < R * kT; idx += 256) {
       const int r = idx / kT, t = idx % kT;

@@ -103,7 +103,19 @@ def test_plan_is_host_arithmetic():
     assert s.value == 8          # raised to respect the 1024-block split limit
     assert lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 20, ctypes.byref(s), ctypes.byref(n)) == 0
     assert s.value == 20
-    # the plan does not depend on the number of flows (primary results stay bit-identical)
+    # fp32 caches run on the vector-ALU kernel, which walks a split one 32-token tile at a
+    # time: batch 1 x 512 tokens, 8 KV heads -> splits of one tile
+    kf = kv(dtype=0, D=64, table=None, bs=512, nb=1)
+    assert lib.dfx_decode_attn_plan(ctypes.byref(kf), 1, 8, 2, 512, 0, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value == 16 and n.value >= 16 * 2 * 8 * 65 * 4
+    assert lib.dfx_decode_attn_plan(ctypes.byref(kf), 1, 8, 2, 512, 3, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value == 3          # chunks of 192 tokens (a multiple of the 32-token tile)
+    # so do bf16 caches with more than 16 query rows per KV head (2 flows x 16 heads)
+    assert lib.dfx_decode_attn_plan(ctypes.byref(kb := kv(heads=4, nb=4096, mb=256)), 2, 64, 2, 4096, 0,
+                                    ctypes.byref(s), ctypes.byref(n)) == 0
+    assert s.value == 32         # 8 pairs -> 32 splits of 128 tokens
+    # the plan does not depend on the number of flows while both counts use the same kernel
+    # (primary results stay bit-identical)
     s1 = ctypes.c_int32()
     lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 1, 131072, 0, ctypes.byref(s1), ctypes.byref(n))
     lib.dfx_decode_attn_plan(ctypes.byref(k), 8, 64, 2, 131072, 0, ctypes.byref(s), ctypes.byref(n))
