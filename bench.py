@@ -16,8 +16,9 @@ timed with HIP events on the stream it runs on, its algorithmic HBM bytes, and t
 CPU oracle timed on the host cores (a reported baseline, not a target).
 
 `step` times a whole decode step of a layer stack (token ids -> embeddings -> layers ->
-shared output head -> next token), eagerly and as a HIP-graph replay; `head` the output
-head alone (final norm, shared vocabulary projection, mixture, greedy token); `moe` the
+shared output head -> next token), eagerly and as a HIP-graph replay (value: the faster);
+`head` the output head alone (final norm, shared vocabulary projection, mixture, greedy
+token); `moe` the
 mixture-of-experts MLP block with router replay; `prefill` one layer of primary-only prefill
 over a prompt chunk and its causal attention alone.
 """
@@ -404,14 +405,16 @@ def bench_step(args):
     w_bytes = 2 * (Hq + 2 * Hkv) * D * H + 2 * H * Hq * D + 2 * 2 * I * H + 2 * H * I
     kv_bytes = 2 * B * ctx_len * Hkv * D * 2
     step_bytes = nl * (w_bytes + kv_bytes) + 2 * B * H * 2 + (2 * vocab * H if with_head else 0)
+    # value: the faster of the two ways of launching the same step (both are timed and reported)
     ms = min(eager_ms, graph_ms)
-    line = {"metric": "dual-flow multi-layer decode steps/s at batch x ctx", "value": round(1000.0 / graph_ms, 2),
-            "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(graph_ms, 4),
+    mode = "eager launches" if eager_ms <= graph_ms else "HIP-graph replay"
+    line = {"metric": "dual-flow multi-layer decode steps/s at batch x ctx", "value": round(1000.0 / ms, 2),
+            "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"dual-flow decode step: {nl} layers, batch {B} x context {ctx_len}, hidden {H}, "
                                    f"{Hq}/{Hkv} heads x {D}, SwiGLU {I}, vocab {vocab}, both flows"
                                    + (", shared output head + mixture + greedy token" if with_head else "")
-                                   + ", HIP-graph replay",
+                                   + f", {mode}",
                        "layers": nl, "batch": B, "context": ctx_len, "hidden": H, "flows": 2,
                        "vocab": vocab, "output_head": with_head},
             "roofline": {"bound": "hbm", "achieved": round(step_bytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
@@ -420,7 +423,7 @@ def bench_step(args):
                          "kernel": "whole step (weights + KV of every layer, and the output matrix, read once)",
                          "bytes_per_launch": int(step_bytes)},
             "cpu_baseline": None, "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
-            "tokens_per_s": round(B * 1000.0 / graph_ms, 1), "ms_per_layer": round(graph_ms / nl, 4)}
+            "tokens_per_s": round(B * 1000.0 / ms, 1), "ms_per_layer": round(ms / nl, 4)}
     print(json.dumps(line))
 
 
