@@ -18,9 +18,8 @@ CPU oracle timed on the host cores (a reported baseline, not a target).
 `step` times a whole decode step of a layer stack (token ids -> embeddings -> layers ->
 shared output head -> next token), eagerly and as a HIP-graph replay (value: the faster);
 `head` the output head alone (final norm, shared vocabulary projection, mixture, greedy
-token); `moe` the
-mixture-of-experts MLP block with router replay; `prefill` one layer of primary-only prefill
-over a prompt chunk and its causal attention alone.
+token); `moe` the mixture-of-experts MLP block with router replay; `prefill` one layer of
+primary-only prefill over a prompt chunk and its causal attention alone.
 """
 import argparse
 import hashlib
