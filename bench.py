@@ -102,6 +102,24 @@ def timed(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
+def best_split_ratio(dfx, kv, B, Hq, F, mc, q1, q2, a, caches, turn, ctx_t, aws, reps, stream):
+    """Dual and single flow, each timed at every split count the planner runs for a range of
+    requests and reported at its own best (the plan's ratio is reported beside it)."""
+    max_s = max(1, -(-mc // 32))
+    cands = sorted({dfx.decode_attn_plan(kv, B, Hq, F, mc, r)[0]
+                    for r in (0, 1, 2, 3, 4, 6, 8, 12, 16, 32) if r <= max_s})
+    best = {}
+    for name, (qq, aa) in (("dual", (q2, a)), ("single", (None, None))):
+        def call(n, qq=qq, aa=aa):
+            dfx.decode_attn(q1, qq, aa, cache=caches[next(turn)], context_lens=ctx_t, max_context=mc,
+                            num_splits=n, want_lse=False, workspace=aws)
+        t = {n: timed(lambda n=n: call(n), reps, stream) for n in cands}
+        n_best = min(t, key=t.get)
+        best[name] = {"splits": n_best, "ms": round(t[n_best], 4)}
+    best["ratio"] = round(best["dual"]["ms"] / best["single"]["ms"], 3)
+    return best
+
+
 def timed_each(fn, reps, stream):
     """Per-call durations (ms) of reps back-to-back calls, an event pair around each."""
     import torch
@@ -283,23 +301,8 @@ def main():
     extra["attn_ms_each"] = {"median": round(float(np.median(each)), 4), "p10": round(float(np.percentile(each, 10)), 4),
                              "p90": round(float(np.percentile(each, 90)), 4), "calls": int(each.size)}
     if not args.no_split_sweep:
-        # dual and single flow, each at its own best split count (the ratio above uses the plan's)
-        max_s = max(1, -(-mc // 128))
-        # the split counts the planner actually runs for each request (long contexts cap the chunk)
-        cands = sorted({dfx.decode_attn_plan(kv, B, shape["Hq"], F, mc, c)[0]
-                        for c in (0, 1, 2, 3, 4, 6, 8, 12, 16, 32) if c <= max_s})
-        best = {}
-        for name, fn in (("dual", lambda s_: dfx.decode_attn(q1, q2, a, cache=caches[next(turn)], context_lens=ctx_t,
-                                                             max_context=mc, num_splits=s_, want_lse=False,
-                                                             workspace=aws)),
-                         ("single", lambda s_: dfx.decode_attn(q1, None, None, cache=caches[next(turn)],
-                                                               context_lens=ctx_t, max_context=mc, num_splits=s_,
-                                                               want_lse=False, workspace=aws))):
-            t = {c: timed(lambda: fn(c), args.kernel_reps, stream) for c in cands}
-            c = min(t, key=t.get)
-            best[name] = {"splits": c, "ms": round(t[c], 4)}
-        best["ratio"] = round(best["dual"]["ms"] / best["single"]["ms"], 3)
-        extra["attn_best_split"] = best
+        extra["attn_best_split"] = best_split_ratio(dfx, kv, B, shape["Hq"], F, mc, q1, q2, a, caches, turn, ctx_t,
+                                                    aws, args.kernel_reps, stream)
     abytes = attn_bytes(shape, ctx_np, F, 4 if args.workload == "layer" else shape["kv_el"])
     achieved = abytes / (attn_ms * 1e-3) / 1e9
     splits, _ = dfx.decode_attn_plan(kv, B, shape["Hq"], F, mc, args.splits)
