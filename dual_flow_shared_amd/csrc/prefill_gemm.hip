@@ -22,32 +22,38 @@
 namespace dfx {
 
 constexpr int kDensePipe = 2;  // k-steps of fragments in flight per thread (registers)
-constexpr int kDenseFrags = 24;  // fragments per k-step: 16 of W, 8 of X
+// feature waves (64 features each) per work-group; 2 (128 x 128 per work-group, 4 waves) ran
+// the prefill layer in 2.59 ms against 2.10
+constexpr int kFeatWaves = 4;
+constexpr int kWFrags = 4 * kFeatWaves;    // W fragments per k-step (16 features each)
+constexpr int kDenseFrags = kWFrags + 8;   // plus 8 X fragments (2 row groups of 64)
 
-constexpr int kDenseWaves = 8;  // 2 row waves x 4 feature waves
+constexpr int kDenseWaves = 2 * kFeatWaves;  // 2 row waves x kFeatWaves feature waves
 constexpr int kDenseStage = kDenseFrags * 64 / (64 * kDenseWaves);  // fragments a thread stages
+static_assert(kDenseFrags % kDenseWaves == 0, "staging");
 
 template <bool SWIGLU>
 __global__ void __launch_bounds__(64 * kDenseWaves) prefill_gemm_kernel(PrefillGemmArgs p) {
   __shared__ u32x4 lds[2][kDenseFrags][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
-  const int wr = wave >> 2, wc = wave & 3;  // row group of the tile, feature quarter
+  const int wr = wave / kFeatWaves, wc = wave % kFeatWaves;  // row group of the tile, feature wave
   const int M = p.M, K = p.K, N = p.N;
   const int nks = K / 32, ng = N / 16, ngh = ng / 2, groups = (M + 63) / 64;
   const int RT = (groups + 1) / 2;
-  const int CT = SWIGLU ? (N / 2 + 127) / 128 : (N + 255) / 256;
+  const int CT = SWIGLU ? (N / 2 + 32 * kFeatWaves - 1) / (32 * kFeatWaves)
+                        : (N + 64 * kFeatWaves - 1) / (64 * kFeatWaves);
   const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
   const int ct = xcd + 8 * (idx / RT), rt = idx % RT;
   if (ct >= CT) return;  // uniform for the work-group, before any barrier
 
-  // global feature group of the work-group's feature group fg (0..15)
+  // global feature group of the work-group's feature group fg (0 .. kWFrags - 1)
   auto wgroup = [&](int fg) {
     if (SWIGLU) {
-      const int g = min(ct * 8 + (fg & 7), ngh - 1);
-      return fg < 8 ? g : g + ngh;
+      const int g = min(ct * (kWFrags / 2) + fg % (kWFrags / 2), ngh - 1);
+      return fg < kWFrags / 2 ? g : g + ngh;
     }
-    return min(ct * 16 + fg, ng - 1);
+    return min(ct * kWFrags + fg, ng - 1);
   };
   // this thread stages fragments f = wave + kDenseWaves r, lane `lane` of each
   const uint16_t *src[kDenseStage];
@@ -55,11 +61,11 @@ __global__ void __launch_bounds__(64 * kDenseWaves) prefill_gemm_kernel(PrefillG
 #pragma unroll
   for (int r = 0; r < kDenseStage; ++r) {
     const int f = wave + kDenseWaves * r;
-    if (f < 16) {
+    if (f < kWFrags) {
       src[r] = p.w + ((int64_t)wgroup(f) * 64 + lane) * 8;
       sstep[r] = (int64_t)ng * 512;
     } else {
-      const int grp = min(2 * rt + (f - 16) / 4, groups - 1), nb = (f - 16) % 4;
+      const int grp = min(2 * rt + (f - kWFrags) / 4, groups - 1), nb = (f - kWFrags) % 4;
       src[r] = p.x + (((int64_t)grp * nks * 4 + nb) * 64 + lane) * 8;
       sstep[r] = 4 * 512;
     }
@@ -77,7 +83,8 @@ __global__ void __launch_bounds__(64 * kDenseWaves) prefill_gemm_kernel(PrefillG
   // this wave's weight fragments in LDS (gate/up mode: 2 gate groups and their 2 up groups)
   int wfrag[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) wfrag[c] = SWIGLU ? (c < 2 ? 2 * wc + c : 8 + 2 * wc + c - 2) : 4 * wc + c;
+  for (int c = 0; c < 4; ++c)
+    wfrag[c] = SWIGLU ? (c < 2 ? 2 * wc + c : kWFrags / 2 + 2 * wc + c - 2) : 4 * wc + c;
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -99,7 +106,7 @@ __global__ void __launch_bounds__(64 * kDenseWaves) prefill_gemm_kernel(PrefillG
 #pragma unroll
       for (int c = 0; c < 4; ++c) wf[c] = lds[slot][wfrag[c]][lane];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) xf[nb] = lds[slot][16 + 4 * wr + nb][lane];
+      for (int nb = 0; nb < 4; ++nb) xf[nb] = lds[slot][kWFrags + 4 * wr + nb][lane];
       lstore(slot ^ 1, stage[(u + 1) % kDensePipe]);
       gload(s + 1 + kDensePipe, stage[(u + 1) % kDensePipe]);
 #pragma unroll
@@ -118,7 +125,7 @@ __global__ void __launch_bounds__(64 * kDenseWaves) prefill_gemm_kernel(PrefillG
     const int I = N / 2;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int g = ct * 8 + 2 * wc + c;
+      const int g = ct * (kWFrags / 2) + 2 * wc + c;
       if (g >= ngh) continue;
       const int col = 16 * g + 4 * j;
 #pragma unroll
@@ -135,7 +142,7 @@ __global__ void __launch_bounds__(64 * kDenseWaves) prefill_gemm_kernel(PrefillG
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int g = ct * 16 + 4 * wc + c;
+      const int g = ct * kWFrags + 4 * wc + c;
       if (g >= ng) continue;
       const int col = 16 * g + 4 * j;
 #pragma unroll
@@ -158,7 +165,8 @@ bool prefill_gemm_fits(int32_t K, int32_t N, bool swiglu) {
 hipError_t launch_prefill_gemm(const PrefillGemmArgs &a, bool swiglu, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   const int groups = (a.M + 63) / 64, RT = (groups + 1) / 2;
-  const int CT = swiglu ? (a.N / 2 + 127) / 128 : (a.N + 255) / 256;
+  const int CT = swiglu ? (a.N / 2 + 32 * kFeatWaves - 1) / (32 * kFeatWaves)
+                        : (a.N + 64 * kFeatWaves - 1) / (64 * kFeatWaves);
   const int64_t per_xcd = (int64_t)((CT + 7) / 8) * RT;  // work-groups of the busiest XCD
   const dim3 grid((unsigned)(8 * per_xcd)), block(64 * kDenseWaves);
   if (swiglu) prefill_gemm_kernel<true><<<grid, block, 0, s>>>(a);
