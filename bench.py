@@ -569,13 +569,18 @@ def bench_prefill(args):
         dfx.prefill_layer(x, w, cache, start, cap, workspace=ws)
 
     q = torch.randn(B, T, Hq, D, generator=gen_, device="cuda")
+    q2 = torch.randn(B, T, Hq, D, generator=gen_, device="cuda")
+    av = torch.rand(D, generator=gen_, device="cuda") * 2 - 1
     attn = lambda: dfx.prefill_attn(q, cache, start, cap)
+    dual = lambda: dfx.prefill_dual_attn(q, q2, av, cache, start, cap)   # both flows (training-time forward)
     for _ in range(args.warmup):
         layer()
         attn()
+        dual()
     torch.cuda.synchronize()
     ms = timed(layer, args.steps, stream)
     attn_ms = timed(attn, args.steps, stream)
+    dual_ms = timed(dual, args.steps, stream)
     rows = B * T
     wparams = (Hq + 2 * Hkv) * D * H + H * Hq * D + 2 * I * H + H * I
     attn_flops = 4.0 * D * Hq * B * T * (T + 1) / 2
@@ -593,7 +598,9 @@ def bench_prefill(args):
                          "kernel": "whole prefill layer (8 launches); algorithmic flops of projections + causal attention",
                          "flops_per_launch": flops},
             "cpu_baseline": None,
-            "attention": {"ms": round(attn_ms, 4), "tflops": round(atf, 1), "frac_of_bf16_peak": round(atf / 2500.0, 4)}}
+            "attention": {"ms": round(attn_ms, 4), "tflops": round(atf, 1), "frac_of_bf16_peak": round(atf / 2500.0, 4)},
+            "dual_attention": {"ms": round(dual_ms, 4), "tflops": round(2 * attn_flops / (dual_ms * 1e-3) / 1e12, 1),
+                               "dual_over_single": round(dual_ms / attn_ms, 3)}}
     print(json.dumps(line))
 
 

@@ -471,6 +471,29 @@ def prefill_attn(q: torch.Tensor, cache: KVCache, start_pos: torch.Tensor, max_c
     return (o, lse) if want_lse else o
 
 
+def prefill_dual_attn(q1: torch.Tensor, q2_raw: torch.Tensor, a: Optional[torch.Tensor], cache: KVCache,
+                      start_pos: torch.Tensor, max_context: int, want_lse: bool = False, stream=None):
+    """Causal attention of a chunk with both flows at every position (the training-time
+    forward): q1, q2_raw fp32 [B][T][Hq][D], a fp32 [D] or [Hq][D] or None (Q2 = q2_raw + a * Q1)
+    -> o1, o2 fp32 [B][T][Hq][D] (and lse [2][B][T][Hq])."""
+    q1, q2_raw = _contig(q1, "q1"), _contig(q2_raw, "q2_raw")
+    if q1.dim() != 4 or q1.dtype != torch.float32 or q2_raw.shape != q1.shape or q2_raw.dtype != torch.float32:
+        raise ValueError("q1 and q2_raw must be fp32 [batch][chunk][heads][head_dim] of one shape")
+    B, T, Hq, D = q1.shape
+    stride = 0
+    if a is not None:
+        a = _contig(a, "a")
+        if a.dtype != torch.float32 or a.numel() not in (D, Hq * D):
+            raise ValueError("a must be fp32 [head_dim] or [heads][head_dim]")
+        stride = 0 if a.numel() == D else D
+    o1, o2 = torch.empty_like(q1), torch.empty_like(q1)
+    lse = torch.empty(2, B, T, Hq, dtype=torch.float32, device=q1.device) if want_lse else None
+    c = cache.struct()
+    check(lib().dfx_prefill_dual_attn(ctypes.byref(c), _ptr(start_pos), B, T, max_context, Hq, _ptr(q1), _ptr(q2_raw),
+                                      _ptr(a), stride, 0, _ptr(o1), _ptr(o2), _ptr(lse), _stream(stream)))
+    return (o1, o2, lse) if want_lse else (o1, o2)
+
+
 def prefill_layer(x: torch.Tensor, weights: LayerWeights, cache: KVCache, start_pos: torch.Tensor,
                   max_context: int, workspace: Optional[Workspace] = None, stream=None) -> torch.Tensor:
     """One layer of the primary over a prompt chunk, in place on x [B][T][hidden] fp32."""

@@ -80,6 +80,7 @@ SIGNATURES = {
     "dfx_dual_flow_moe_mlp_taps": (I32, [MWP, I32, I32, ctypes.POINTER(MoeTapsStruct)]),
     "dfx_dual_flow_moe_mlp": (I32, [MWP, I32, I32, P, P, SZ, P]),
     "dfx_prefill_attn": (I32, [KVP, P, I32, I32, I32, I32, P, I64, P, P, P]),
+    "dfx_prefill_dual_attn": (I32, [KVP, P, I32, I32, I32, I32, P, P, P, I32, I64, P, P, P, P]),
     "dfx_prefill_layer_workspace_size": (I32, [LWP, KVP, I32, I32, I32, PSZ]),
     "dfx_prefill_layer": (I32, [LWP, KVP, P, I32, I32, I32, P, P, SZ, P]),
     "dfx_prefill_step_workspace_size": (I32, [LWP, KVP, I32, I32, I32, I32, PSZ]),

@@ -1012,6 +1012,33 @@ dfx_status dfx_prefill_attn(const dfx_kv_cache *kv, const int32_t *start_pos, in
   DFX_END
 }
 
+dfx_status dfx_prefill_dual_attn(const dfx_kv_cache *kv, const int32_t *start_pos, int32_t batch, int32_t chunk,
+                                 int32_t max_context, int32_t num_q_heads, const float *q1, const float *q2_raw,
+                                 const float *a, int32_t a_head_stride, int64_t q_row_stride, float *o1, float *o2,
+                                 float *lse, void *stream) {
+  DFX_BEGIN
+  dfx_status st = check_prefill(kv, batch, chunk, max_context, num_q_heads);
+  if (st) return st;
+  const int64_t row = (int64_t)num_q_heads * kv->head_dim;
+  if (q_row_stride == 0) q_row_stride = row;
+  if (q_row_stride < row || q_row_stride % 4) return fail(DFX_EINVAL, "q_row_stride %lld", (long long)q_row_stride);
+  if (a_head_stride != 0 && a_head_stride != kv->head_dim)
+    return fail(DFX_EINVAL, "a_head_stride %d (0 or head_dim)", a_head_stride);
+  if (batch == 0 || chunk == 0) return DFX_OK;
+  if (!start_pos || !q1 || !q2_raw || !o1 || !o2) return fail(DFX_EINVAL, "start_pos / q1 / q2_raw / o1 / o2 is NULL");
+  if (!aligned16(q1) || !aligned16(q2_raw) || !aligned16(o1) || !aligned16(o2) || ((uintptr_t)lse & 3) ||
+      ((uintptr_t)a & 3))
+    return fail(DFX_EINVAL, "misaligned pointer");
+  AttnArgs at = prefill_attn_args(kv, start_pos, batch, chunk, max_context, num_q_heads, q1, q_row_stride, o1, 0, lse);
+  at.n_flows = 2;
+  at.q2 = q2_raw;
+  at.a = a;
+  at.a_hstride = a_head_stride;
+  at.o2 = o2;
+  return hip_status(launch_prefill_attn(at, (hipStream_t)stream), "prefill dual attention launch");
+  DFX_END
+}
+
 dfx_status dfx_prefill_layer_workspace_size(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_t batch,
                                             int32_t chunk, int32_t max_context, size_t *bytes) {
   DFX_BEGIN

@@ -11,6 +11,11 @@
 // MFMA tile code (attn_tiles.h); each lane masks its own row at the row's position. The waves
 // of a group of heads read the same K/V lines at about the same time, so the cache is fetched
 // from HBM about once per work-group and re-read from the CU's caches by the other waves.
+//
+// The same kernels with both flows at every position are the training-time forward of the
+// attention (the summary's cost section: training runs both flows over the whole sequence):
+// a work-group then holds 2 query heads x 2 flows, the auxiliary's query coupled to the
+// primary's (Q2 = q2_raw + a (.) Q1), both attending to the primary's keys and values.
 #include "attn_tiles.h"
 
 namespace dfx {
@@ -54,13 +59,94 @@ hipError_t launch_prefill_append(const PrefillGlueArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, bool PAGED>
+// Per-flow state of a wave's 16 query rows: the queries split into bf16 hi + lo, O^T
+// accumulators and the online-softmax statistics of the lane's row.
+template <int D>
+struct FlowAcc {
+  u32x4 qh[D / 32], ql[D / 32];
+  f32x4 oacc[D / 16];
+  float m_run, l_run;
+};
+
+// Query row n of the wave (position t0 + n of head h) for flow f. The auxiliary's query is
+// q2_raw + a (.) q1 in fp32 (the decode kernels' formula); rows past the chunk are zero.
+template <int D>
+__device__ __forceinline__ void prefill_query(const AttnArgs &p, int f, int b, int t0, int n, int j, int rows,
+                                              int h, FlowAcc<D> &fa) {
+  constexpr int KS = D / 32;
+  const bool valid = n < rows;
+  const int64_t qoff = ((int64_t)b * p.prefill_T + t0 + (valid ? n : 0)) * p.q_bstride + (int64_t)h * D;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int d0 = 8 * (4 * s + j);
+    float q[8];
+    load8<false>(p.q1, qoff + d0, q);
+    if (f == 1) {
+      float q2[8];
+      load8<false>(p.q2, qoff + d0, q2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        q[i] = p.a ? fmaf(p.a[(int64_t)h * p.a_hstride + d0 + i], q[i], q2[i]) : q2[i];
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t h0, l0, h1, l1;
+      split_bf16(valid ? q[2 * w] : 0.f, h0, l0);
+      split_bf16(valid ? q[2 * w + 1] : 0.f, h1, l1);
+      fa.qh[s][w] = h0 | (h1 << 16);
+      fa.ql[s][w] = l0 | (l1 << 16);
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) fa.oacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  fa.m_run = -INFINITY;
+  fa.l_run = 0.f;
+}
+
+// Row n's result for flow f: its sum over the four lanes that hold it, then 32 consecutive
+// head-dim values per lane -- fp32 rows of o1 / o2, or (one flow) bf16 rows of W_o's input in
+// the grouped linear's fragment order -- and the natural-log sum, [F][batch * chunk][Hq].
+template <int D>
+__device__ __forceinline__ void prefill_store(const AttnArgs &p, int f, int b, int t0, int n, int j, int rows,
+                                              int h, const FlowAcc<D> &fa) {
+  constexpr int VEC = D / 16;
+  float l_tot = fa.l_run + __shfl_xor(fa.l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (n >= rows) return;
+  const float inv = 1.0f / l_tot;
+  const int64_t r = (int64_t)b * p.prefill_T + t0 + n;
+  const int Hq = p.num_q_heads;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float o[VEC];
+#pragma unroll
+    for (int mb = 0; mb < VEC; ++mb) o[mb] = fa.oacc[mb][i] * inv;
+    const int d0 = VEC * (4 * j + i);
+    if (p.o_packed) {
+      uint16_t *dst = (uint16_t *)p.o1 + xpack_offset(1, 0, (int)r, h * D + d0, Hq * D);
+      if constexpr (VEC == 8)
+        *(u32x4 *)dst = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                              pack_bf16x2(o[6], o[7])};
+      else
+        *(u32x2 *)dst = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    } else {
+      float *dst = (f == 0 ? p.o1 : p.o2) + (r * Hq + h) * D + d0;
+#pragma unroll
+      for (int v = 0; v < VEC; v += 4) *(f32x4 *)(dst + v) = f32x4{o[v], o[v + 1], o[v + 2], o[v + 3]};
+    }
+  }
+  if (j == 0 && p.lse)
+    p.lse[((int64_t)f * p.batch * p.prefill_T + r) * Hq + h] = (fa.m_run + __log2f(l_tot)) * kLn2;
+}
+
+// F flows: wave w takes flow w % F of query head (4 / F) x + w / F, so with both flows the two
+// waves of a head read the same K/V lines at the same time.
+template <int D, bool PAGED, int F>
 __global__ void __launch_bounds__(256) prefill_attn_kernel(AttnArgs p) {
-  constexpr int KS = D / 32, VEC = D / 16;
   __shared__ int32_t s_tbl[kMaxChunkBlocks];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
-  const int h = blockIdx.x * 4 + wave, b = blockIdx.y;
+  const int h = blockIdx.x * (4 / F) + wave / F, f = wave % F, b = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;  // the longest tiles are dispatched first
   const int T = p.prefill_T, t0 = 16 * tile;
   const int g = h / p.group;
@@ -71,32 +157,11 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(AttnArgs p) {
   const int kend = max(min(start + t0 + rows, cap), 1);
   const int my_end = n < rows ? min(start + t0 + n + 1, kend) : 1;
 
-  // query row n of this wave: position t0 + n of head h, split into bf16 hi + lo
-  u32x4 qh[KS], ql[KS];
-  {
-    const bool valid = n < rows;
-    const int64_t qoff = ((int64_t)b * T + t0 + (valid ? n : 0)) * p.q_bstride + (int64_t)h * D;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      float q[8];
-      load8<false>(p.q1, qoff + 8 * (4 * s + j), q);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t h0, l0, h1, l1;
-        split_bf16(valid ? q[2 * w] : 0.f, h0, l0);
-        split_bf16(valid ? q[2 * w + 1] : 0.f, h1, l1);
-        qh[s][w] = h0 | (h1 << 16);
-        ql[s][w] = l0 | (l1 << 16);
-      }
-    }
-  }
+  FlowAcc<D> fa;
+  prefill_query<D>(p, f, b, t0, n, j, rows, h, fa);
 
   const uint16_t *kp = (const uint16_t *)p.k;
   const uint16_t *vp = (const uint16_t *)p.v;
-  f32x4 oacc[VEC];
-#pragma unroll
-  for (int mb = 0; mb < VEC; ++mb) oacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
 
   // keys in chunks of at most kMaxChunkBlocks staged block ids
   const int chunk_tok = PAGED ? (kMaxChunkBlocks << p.block_shift) : kend;
@@ -122,43 +187,16 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(AttnArgs p) {
     load_v<D>(vp, hb, lx, n, j, tr);
     for (; t + 32 < ce; t += 32) {
       half_bases<PAGED>(p, s_tbl, first_blk, b, g, t + 32, ce, hb, lx);
-      tile_scores<D>(tr, qh, ql, sacc);
+      tile_scores<D>(tr, fa.qh, fa.ql, sacc);
       load_k<D>(kp, hb, lx, n, j, tr);
-      tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, m_run, l_run, oacc);
+      tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
       load_v<D>(vp, hb, lx, n, j, tr);
     }
-    tile_scores<D>(tr, qh, ql, sacc);
-    tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, m_run, l_run, oacc);
+    tile_scores<D>(tr, fa.qh, fa.ql, sacc);
+    tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
   }
 
-  // row n's sum over the four lanes that hold it, then 32 consecutive head-dim values per lane
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (n >= rows) return;
-  const float inv = 1.0f / l_tot;
-  const int64_t r = (int64_t)b * T + t0 + n;
-  const int Hq = p.num_q_heads;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float o[VEC];
-#pragma unroll
-    for (int mb = 0; mb < VEC; ++mb) o[mb] = oacc[mb][i] * inv;
-    const int d0 = VEC * (4 * j + i);
-    if (p.o_packed) {
-      // bf16 rows of W_o's input in the grouped linear's fragment order (one flow)
-      uint16_t *dst = (uint16_t *)p.o1 + xpack_offset(1, 0, (int)r, h * D + d0, Hq * D);
-      if constexpr (VEC == 8)
-        *(u32x4 *)dst = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                              pack_bf16x2(o[6], o[7])};
-      else
-        *(u32x2 *)dst = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-    } else {
-      float *dst = p.o1 + (r * Hq + h) * D + d0;
-#pragma unroll
-      for (int v = 0; v < VEC; v += 4) *(f32x4 *)(dst + v) = f32x4{o[v], o[v + 1], o[v + 2], o[v + 3]};
-    }
-  }
-  if (j == 0 && p.lse) p.lse[r * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
+  prefill_store<D>(p, f, b, t0, n, j, rows, h, fa);
 }
 
 // The same attention with the four waves' K/V tiles shared through LDS (head_dim 128, the
@@ -177,14 +215,15 @@ __device__ __forceinline__ u32x4 tile_component(const uint16_t *kp, const uint16
   return kv_load<u32x4>(vp + hb[h] + (int64_t)min(x, lx[h]) * D + 8 * n);
 }
 
-template <bool PAGED>
+template <bool PAGED, int F>
 __global__ void __launch_bounds__(256) prefill_attn_shared_kernel(AttnArgs p) {
-  constexpr int D = 128, KS = D / 32, VEC = D / 16;
+  constexpr int D = 128;
   __shared__ int32_t s_tbl[kMaxChunkBlocks];
   __shared__ u32x4 s_img[2][16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
-  const int h = blockIdx.x * 4 + wave, b = blockIdx.y;
+  // wave w: flow w % F of query head (4 / F) x + w / F
+  const int h = blockIdx.x * (4 / F) + wave / F, f = wave % F, b = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;  // the longest tiles are dispatched first
   const int T = p.prefill_T, t0 = 16 * tile;
   const int g = h / p.group;  // the same for the four waves (group % 4 == 0)
@@ -194,30 +233,10 @@ __global__ void __launch_bounds__(256) prefill_attn_shared_kernel(AttnArgs p) {
   const int kend = max(min(start + t0 + rows, cap), 1);
   const int my_end = n < rows ? min(start + t0 + n + 1, kend) : 1;
 
-  u32x4 qh[KS], ql[KS];
-  {
-    const bool valid = n < rows;
-    const int64_t qoff = ((int64_t)b * T + t0 + (valid ? n : 0)) * p.q_bstride + (int64_t)h * D;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      float q[8];
-      load8<false>(p.q1, qoff + 8 * (4 * s + j), q);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t h0, l0, h1, l1;
-        split_bf16(valid ? q[2 * w] : 0.f, h0, l0);
-        split_bf16(valid ? q[2 * w + 1] : 0.f, h1, l1);
-        qh[s][w] = h0 | (h1 << 16);
-        ql[s][w] = l0 | (l1 << 16);
-      }
-    }
-  }
+  FlowAcc<D> fa;
+  prefill_query<D>(p, f, b, t0, n, j, rows, h, fa);
   const uint16_t *kp = (const uint16_t *)p.k;
   const uint16_t *vp = (const uint16_t *)p.v;
-  f32x4 oacc[VEC];
-#pragma unroll
-  for (int mb = 0; mb < VEC; ++mb) oacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
 
   const int chunk_tok = PAGED ? (kMaxChunkBlocks << p.block_shift) : kend;
   for (int cs = 0; cs < kend; cs += chunk_tok) {
@@ -257,8 +276,8 @@ __global__ void __launch_bounds__(256) prefill_attn_shared_kernel(AttnArgs p) {
         tr.vr[v][0] = y[0]; tr.vr[v][1] = y[1]; tr.vr[v][2] = y[2]; tr.vr[v][3] = y[3];
       }
       f32x4 sacc[2];
-      tile_scores<D>(tr, qh, ql, sacc);
-      tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, m_run, l_run, oacc);
+      tile_scores<D>(tr, fa.qh, fa.ql, sacc);
+      tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_img[slot ^ 1][4 * wave + i][lane] = st[i];
       __syncthreads();
@@ -266,45 +285,29 @@ __global__ void __launch_bounds__(256) prefill_attn_shared_kernel(AttnArgs p) {
     }
   }
 
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (n >= rows) return;
-  const float inv = 1.0f / l_tot;
-  const int64_t r = (int64_t)b * T + t0 + n;
-  const int Hq = p.num_q_heads;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float o[VEC];
-#pragma unroll
-    for (int mb = 0; mb < VEC; ++mb) o[mb] = oacc[mb][i] * inv;
-    const int d0 = VEC * (4 * j + i);
-    if (p.o_packed) {
-      uint16_t *dst = (uint16_t *)p.o1 + xpack_offset(1, 0, (int)r, h * D + d0, Hq * D);
-      *(u32x4 *)dst = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                            pack_bf16x2(o[6], o[7])};
-    } else {
-      float *dst = p.o1 + (r * Hq + h) * D + d0;
-      *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
-      *(f32x4 *)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
-    }
+  prefill_store<D>(p, f, b, t0, n, j, rows, h, fa);
+}
+
+template <int F>
+void launch_prefill_attn_flows(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  const bool paged = a.block_shift >= 0;
+  if (a.head_dim == 128 && a.group % 4 == 0) {
+    if (paged) prefill_attn_shared_kernel<true, F><<<grid, block, 0, s>>>(a);
+    else prefill_attn_shared_kernel<false, F><<<grid, block, 0, s>>>(a);
+  } else if (a.head_dim == 128) {
+    if (paged) prefill_attn_kernel<128, true, F><<<grid, block, 0, s>>>(a);
+    else prefill_attn_kernel<128, false, F><<<grid, block, 0, s>>>(a);
+  } else {
+    if (paged) prefill_attn_kernel<64, true, F><<<grid, block, 0, s>>>(a);
+    else prefill_attn_kernel<64, false, F><<<grid, block, 0, s>>>(a);
   }
-  if (j == 0 && p.lse) p.lse[r * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
 hipError_t launch_prefill_attn(const AttnArgs &a, hipStream_t s) {
   if (a.batch == 0 || a.prefill_T == 0) return hipSuccess;
-  const dim3 grid(a.num_q_heads / 4, a.batch, (a.prefill_T + 15) / 16), block(256);
-  const bool paged = a.block_shift >= 0;
-  if (a.head_dim == 128 && a.group % 4 == 0) {
-    if (paged) prefill_attn_shared_kernel<true><<<grid, block, 0, s>>>(a);
-    else prefill_attn_shared_kernel<false><<<grid, block, 0, s>>>(a);
-  } else if (a.head_dim == 128) {
-    if (paged) prefill_attn_kernel<128, true><<<grid, block, 0, s>>>(a);
-    else prefill_attn_kernel<128, false><<<grid, block, 0, s>>>(a);
-  } else {
-    if (paged) prefill_attn_kernel<64, true><<<grid, block, 0, s>>>(a);
-    else prefill_attn_kernel<64, false><<<grid, block, 0, s>>>(a);
-  }
+  const dim3 grid(a.num_q_heads * a.n_flows / 4, a.batch, (a.prefill_T + 15) / 16), block(256);
+  if (a.n_flows == 2) launch_prefill_attn_flows<2>(a, grid, block, s);
+  else launch_prefill_attn_flows<1>(a, grid, block, s);
   return hipGetLastError();
 }
 

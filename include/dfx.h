@@ -474,6 +474,27 @@ dfx_status dfx_prefill_attn(const dfx_kv_cache *kv, const int32_t *start_pos, in
                             float *o, float *lse, void *stream);
 
 /*
+ * dfx_prefill_dual_attn: the same causal attention with both flows at every new position, the
+ * training-time forward of the attention (Sintesi Tecnica: Dual-Flow Transformers, "Costi di
+ * Inferenza vs. Addestramento": training runs both flows over the whole sequence; "Meccanismi
+ * Chiave": the auxiliary's query is coupled to the primary's and attends to the primary's keys
+ * and values). Query t of sequence b, flow f, attends to positions [0, start_pos[b] + t] of the
+ * cache, which holds the primary's keys and values; each K/V tile is loaded once for both
+ * flows.
+ *   q1, q2_raw     device fp32 rows laid out as dfx_prefill_attn's q (same q_row_stride); the
+ *                  auxiliary's query is Q2 = q2_raw + a (.) Q1 (fp32 fma).
+ *   a              device fp32 [head_dim] (a_head_stride 0) or [num_q_heads][head_dim]
+ *                  (a_head_stride head_dim), 4-byte aligned; NULL: Q2 = q2_raw.
+ *   o1, o2         device fp32 [batch][chunk][num_q_heads][head_dim], outputs.
+ *   lse            device fp32 [2][batch][chunk][num_q_heads] natural-log sums, or NULL.
+ * The limits and errors of dfx_prefill_attn. No workspace; the cache is only read.
+ */
+dfx_status dfx_prefill_dual_attn(const dfx_kv_cache *kv, const int32_t *start_pos, int32_t batch, int32_t chunk,
+                                 int32_t max_context, int32_t num_q_heads, const float *q1, const float *q2_raw,
+                                 const float *a, int32_t a_head_stride, int64_t q_row_stride, float *o1, float *o2,
+                                 float *lse, void *stream);
+
+/*
  * dfx_prefill_layer: one layer for the new positions of the primary, in place on x (device
  * fp32 [batch][chunk][hidden]): the decode layer's steps with one flow and every position a
  * row -- norm, shared Q/K/V projection, the chunk's keys and values appended at start_pos[b] + t

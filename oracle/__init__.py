@@ -34,6 +34,8 @@ Functions and their pins (tests/test_oracle_*.py):
   prefill.prefill_attention  -- torch causal SDPA (GQA, cached prefix); prefill_layer = the
        / prefill_layer /       pinned decode layer token by token; chunking invariance; the
        prefill_step            aux started at the last prompt position = aux at every position
+  prefill.prefill_dual_      -- torch causal SDPA per flow with Q2 materialised (per-head a);
+       attention               primary rows = prefill_attention's; Q2 = Q1 -> O2 = O1
 The placement of the b and c coupling vectors is a reading of the pages (they
 name the levels, not the formula); it is pinned only by the identities above:
 "parity unpinned" beyond this reading. So is the mixture weight alpha_t = (1 + c_t) / 2

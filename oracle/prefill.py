@@ -10,7 +10,9 @@ a decode step with both flows at position n-1 (which appends that token's key an
 
 prefill_attention: query t of sequence b attends to positions [0, start_b + t], which is the
 decode attention of that one query with context start_b + t + 1 (composition of the pinned
-decode attention). prefill_layer: the decode layer's steps for the primary, applied to the T
+decode attention). prefill_dual_attention: the same with both flows' queries at every
+position, the forward of the attention at training time, when both flows run over the whole
+sequence. prefill_layer: the decode layer's steps for the primary, applied to the T
 rows of every sequence at once, with the same bf16 rounding points (normed rows, appended
 keys and values, attention rows, normed rows, MLP intermediate).
 """
@@ -35,6 +37,27 @@ def prefill_attention(q, k_pool, v_pool, block_table, start_pos, batches=None, d
                                     batches=batches, dtype=dtype)
         o[:, t], lse[:, t] = o1, l[0]
     return o, lse
+
+
+def prefill_dual_attention(q1, q2_raw, a, a_head_stride, k_pool, v_pool, block_table, start_pos, batches=None,
+                           dtype=np.float64):
+    """Both flows at every new position: the training-time forward of the attention (the
+    summary's cost section: training runs both flows over the whole sequence). Query t of
+    either flow attends to positions [0, start_b + t] of the primary's cache, which is the
+    pinned decode attention of that position's two queries (Q2 = q2_raw + a (.) Q1) with
+    context start_b + t + 1. q1, q2_raw: [B][T][Hq][D]; a: [D] (stride 0) or [Hq][D] (stride D)
+    or None. Returns o1, o2 [B][T][Hq][D] and lse [2][B][T][Hq] (natural log)."""
+    q1, q2_raw = np.asarray(q1), np.asarray(q2_raw)
+    B, T, Hq, D = q1.shape
+    start = np.asarray(start_pos, np.int64)
+    o1 = np.full((B, T, Hq, D), np.nan)
+    o2 = np.full((B, T, Hq, D), np.nan)
+    lse = np.full((2, B, T, Hq), np.nan)
+    for t in range(T):
+        r1, r2, l = decode_attention(q1[:, t], q2_raw[:, t], a, a_head_stride, k_pool, v_pool, block_table,
+                                     start + t + 1, batches=batches, dtype=dtype)
+        o1[:, t], o2[:, t], lse[:, :, t] = r1, r2, l
+    return o1, o2, lse
 
 
 def prefill_layer(x, g_attn, g_mlp, w_qkv, w_o, w_gate_up, w_down, eps, k_pool, v_pool, block_table,

@@ -21,7 +21,7 @@ def declared():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = _abi.lib()
     names = declared()
-    assert len(names) == 29
+    assert len(names) == 30
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, n
@@ -310,6 +310,17 @@ def test_prefill_rejects():
     assert lib.dfx_prefill_attn(ctypes.byref(k), FAKE, 1 << 16, 16, 64, 32, FAKE, 0, FAKE, None, None) == 1
     kbig = kv(mb=1 << 17, nb=1 << 17)
     assert lib.dfx_prefill_attn(ctypes.byref(kbig), FAKE, 1, 65535 * 16 + 1, 1 << 21, 32, FAKE, 0, FAKE, None, None) == 2
+    # both flows: the same limits, plus the auxiliary's query, output and coupling stride
+    dual = lambda kk, **o: lib.dfx_prefill_dual_attn(
+        ctypes.byref(kk), FAKE, o.get("B", 2), 16, 64, o.get("hq", 32), FAKE, o.get("q2", FAKE), o.get("a", FAKE),
+        o.get("ast", 0), 0, FAKE, o.get("o2", FAKE), None, None)
+    assert dual(k32) == 2
+    assert dual(k, hq=30) == 2
+    assert dual(k, q2=None) == 1 and "q2_raw" in lib.dfx_last_error().decode()
+    assert dual(k, o2=None) == 1
+    assert dual(k, ast=64) == 1 and "a_head_stride" in lib.dfx_last_error().decode()
+    assert dual(k, a=FAKE + 2) == 1
+    assert dual(k, B=0, q2=None) == 0          # nothing to do: no pointer is read
     W = _abi.LayerWeightsStruct * 1
     K = _abi.KVCacheStruct * 1
     ws, ks = W(), K()

@@ -1,5 +1,6 @@
-"""GPU parity of the primary-only prefill (dfx_prefill_attn, dfx_prefill_layer, dfx_prefill_step)
-and of the auxiliary flow's start at the last prompt position.
+"""GPU parity of the primary-only prefill (dfx_prefill_attn, dfx_prefill_layer, dfx_prefill_step),
+of the auxiliary flow's start at the last prompt position, and of the causal attention with
+both flows at every position (dfx_prefill_dual_attn, the training-time forward).
 
 Tolerances: the causal attention outputs against the oracle at max-abs 2e-3 (bf16 cache) and,
 tighter, 5e-5 (Q and P are split into two bf16 terms, so the kernel carries about 16 more bits
@@ -14,7 +15,7 @@ import torch
 import dfx_inputs as gen
 import dual_flow_shared_amd as dfx
 from gpu_util import cache_of, dev, host_bits
-from oracle.prefill import prefill_attention, prefill_layer, prefill_step
+from oracle.prefill import prefill_attention, prefill_dual_attention, prefill_layer, prefill_step
 from oracle.step import dual_flow_step
 
 pytestmark = pytest.mark.gpu
@@ -46,6 +47,41 @@ def test_prefill_attention(paged, D, Hq, Hkv, T, starts):
     err = np.abs(o.cpu().numpy() - want).max()
     assert err < 2e-3 and err < 5e-5, err
     assert np.abs(lse.cpu().numpy() - wl).max() < 1e-4
+
+
+@pytest.mark.parametrize("paged,D,Hq,Hkv,T,starts,per_head", [
+    (True, 128, 8, 2, 37, [0, 21], False),   # K/V tiles shared through LDS, ragged tail tile
+    (False, 128, 32, 8, 16, [5, 0], True),   # the same, contiguous cache, per-head a
+    (True, 64, 4, 4, 50, [3, 7], False),     # per-wave kernel, head_dim 64
+    (True, 128, 8, 4, 33, [2, 17], True),    # per-wave kernel, head_dim 128
+    (True, 128, 8, 1, 1, [40, 0], False),    # one position
+])
+def test_prefill_dual_attention(paged, D, Hq, Hkv, T, starts, per_head):
+    """Both flows at every position against the oracle; the primary's rows bit-identical to
+    the primary-only call's; Q2 = Q1 gives the auxiliary exactly the primary's rows."""
+    B = len(starts)
+    st = np.array(starts, np.int32)
+    ctx = st + T
+    c = gen.attention_case(650 + T, B, Hq, Hkv, D, ctx, "bf16", paged=paged, block_size=16,
+                           capacity=int(ctx.max()) + 16)
+    rng = np.random.default_rng(T + D)
+    q1 = rng.standard_normal((B, T, Hq, D)).astype(np.float32)
+    q2 = rng.standard_normal((B, T, Hq, D)).astype(np.float32)
+    a = rng.uniform(-1, 1, (Hq, D) if per_head else D).astype(np.float32)
+    cache = cache_of(c)
+    mc = int(ctx.max()) + 16
+    q1t, stt = dev(q1), dev(st)
+    o1, o2, lse = dfx.prefill_dual_attn(q1t, dev(q2), dev(a), cache, stt, mc, want_lse=True)
+    p1 = dfx.prefill_attn(q1t, cache, stt, mc)
+    s1, s2 = dfx.prefill_dual_attn(q1t, q1t, None, cache, stt, mc)
+    torch.cuda.synchronize()
+    w1, w2, wl = prefill_dual_attention(q1, q2, a, D if per_head else 0, c.k_pool, c.v_pool, c.block_table, st)
+    for got, want in ((o1, w1), (o2, w2)):
+        err = np.abs(got.cpu().numpy() - want).max()
+        assert err < 2e-3 and err < 5e-5, err
+    assert np.abs(lse.cpu().numpy() - wl).max() < 1e-4
+    assert torch.equal(o1, p1)
+    assert torch.equal(s1, s2) and torch.equal(s1, p1)
 
 
 SMALL = dict(hidden=256, num_q_heads=8, num_kv_heads=2, head_dim=128, intermediate=512, w_std=0.05)

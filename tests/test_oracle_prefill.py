@@ -12,7 +12,7 @@ import torch
 import dfx_inputs as gen
 from oracle.layer import dual_flow_layer
 from oracle.numerics import widen
-from oracle.prefill import prefill_attention, prefill_layer, prefill_step
+from oracle.prefill import prefill_attention, prefill_dual_attention, prefill_layer, prefill_step
 from oracle.step import dual_flow_step
 
 SMALL = dict(hidden=64, num_q_heads=4, num_kv_heads=2, head_dim=32, intermediate=64, w_std=0.1)
@@ -33,6 +33,43 @@ def test_prefill_attention_matches_torch_causal_sdpa():
         want = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask).numpy()
         assert np.allclose(o[b].transpose(1, 0, 2), want, rtol=0, atol=1e-12)
     assert np.all(np.isfinite(lse))
+
+
+def test_dual_prefill_attention_matches_two_causal_sdpa():
+    """Both flows at every position against torch's causal SDPA per flow, the auxiliary's query
+    materialised as q2_raw + a * q1 (per-head a), over the primary's keys and values."""
+    B, T, Hq, Hkv, D, P = 2, 7, 4, 2, 32, 3
+    c = gen.attention_case(33, B, Hq, Hkv, D, np.full(B, P + T, np.int32), "f32", paged=True, block_size=4)
+    rng = np.random.default_rng(5)
+    q1, q2 = rng.standard_normal((B, T, Hq, D)), rng.standard_normal((B, T, Hq, D))
+    a = rng.uniform(-1, 1, (Hq, D))
+    o1, o2, lse = prefill_dual_attention(q1, q2, a, D, c.k_pool, c.v_pool, c.block_table, np.full(B, P))
+    mask = torch.arange(P + T)[None, :] <= (P + torch.arange(T))[:, None]
+    for b in range(B):
+        blocks = c.block_table[b, : -(-(P + T) // 4)]
+        K = torch.from_numpy(widen(c.k_pool[blocks]).transpose(1, 0, 2, 3).reshape(Hkv, -1, D)[:, : P + T])
+        V = torch.from_numpy(widen(c.v_pool[blocks]).transpose(1, 0, 2, 3).reshape(Hkv, -1, D)[:, : P + T])
+        K, V = K.repeat_interleave(Hq // Hkv, 0), V.repeat_interleave(Hq // Hkv, 0)
+        for q, o in ((q1[b], o1[b]), (q2[b] + a[None] * q1[b], o2[b])):
+            Q = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))          # [Hq][T][D]
+            want = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask).numpy()
+            assert np.allclose(o.transpose(1, 0, 2), want, rtol=0, atol=1e-12)
+    assert np.all(np.isfinite(lse))
+
+
+def test_dual_prefill_attention_flow_properties():
+    """Adding the auxiliary leaves the primary's rows exactly as the primary-only attention's;
+    Q2 = Q1 (q2_raw = q1, a = 0) gives the auxiliary exactly the primary's rows."""
+    B, T, Hq, Hkv, D, P = 2, 5, 4, 1, 32, 6
+    c = gen.attention_case(34, B, Hq, Hkv, D, np.full(B, P + T, np.int32), "f32", paged=True, block_size=4)
+    rng = np.random.default_rng(6)
+    q1, q2 = rng.standard_normal((B, T, Hq, D)), rng.standard_normal((B, T, Hq, D))
+    st = np.full(B, P)
+    o1, _, lse = prefill_dual_attention(q1, q2, rng.uniform(-1, 1, D), 0, c.k_pool, c.v_pool, c.block_table, st)
+    p1, pl = prefill_attention(q1, c.k_pool, c.v_pool, c.block_table, st)
+    assert np.array_equal(o1, p1) and np.array_equal(lse[0], pl)
+    s1, s2, sl = prefill_dual_attention(q1, q1, np.zeros(D), 0, c.k_pool, c.v_pool, c.block_table, st)
+    assert np.array_equal(s1, s2) and np.array_equal(sl[0], sl[1])
 
 
 def prefill_case(seed, B=2, start=3, T=6):
