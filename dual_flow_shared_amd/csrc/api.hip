@@ -33,6 +33,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+constexpr int kMaxGridRows = 65535;  // the y and z extents of a launch grid
 constexpr int kChunkQuantum = 128;  // tokens: 4 waves x 32-token tiles
 constexpr int kMinChunk = 1024;   // tokens: shorter splits cost more in merge than they gain
 // The vector-ALU kernel walks its split one 32-token tile after another, a memory round trip
@@ -246,6 +247,7 @@ dfx_status validate_attn(const AttnCall &c) {
   if (c.q_dtype != DFX_F32 && c.q_dtype != DFX_BF16) return fail(DFX_EINVAL, "q_dtype %d", c.q_dtype);
   if (c.max_context < 0 || c.max_context > capacity(kv))
     return fail(DFX_EINVAL, "max_context %d outside [0, capacity %lld]", c.max_context, (long long)capacity(kv));
+  if (c.batch > kMaxGridRows) return fail(DFX_EUNSUPPORTED, "batch %d above %d", c.batch, kMaxGridRows);
   if (c.batch > 0 && !c.ctx) return fail(DFX_EINVAL, "context_lens is NULL");
   if (c.batch > 0 && kv->block_table == nullptr && kv->num_blocks < c.batch)
     return fail(DFX_EINVAL, "contiguous cache smaller than batch");
@@ -274,6 +276,7 @@ dfx_status run_attn(const AttnCall &c, hipStream_t s) {
   int splits, chunk;
   const bool mfma = attn_mfma_path(kv, F, G);
   attn_plan(c.batch, kv->num_kv_heads, c.max_context, c.splits, paged_bs(kv), mfma, &splits, &chunk);
+  if (splits > kMaxGridRows) return fail(DFX_EUNSUPPORTED, "%d context splits above %d", splits, kMaxGridRows);
   const size_t need = attn_ws_bytes(splits, F, c.batch, c.hq, kv->head_dim);
   if (need && (!c.ws || c.ws_bytes < need))
     return fail(DFX_EWORKSPACE, "decode_attn needs %zu workspace bytes for %d splits, got %zu", need, splits, c.ws_bytes);
@@ -457,6 +460,7 @@ dfx_status layer_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_
   dfx_status st = check_kv(kv, batch < 0 ? 0 : batch);
   if (st) return st;
   if (batch < 0 || (n_flows != 1 && n_flows != 2)) return fail(DFX_EINVAL, "batch %d n_flows %d", batch, n_flows);
+  if (batch > kMaxGridRows) return fail(DFX_EUNSUPPORTED, "batch %d above %d", batch, kMaxGridRows);
   if (kv->dtype != DFX_BF16) return fail(DFX_EUNSUPPORTED, "layer needs a bf16 cache");
   if (w->head_dim != kv->head_dim || w->num_kv_heads != kv->num_kv_heads)
     return fail(DFX_EINVAL, "weights and cache disagree on head_dim / num_kv_heads");
@@ -481,6 +485,7 @@ dfx_status layer_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_
   int chunk;
   attn_plan(B, kv->num_kv_heads, max_context, 0, paged_bs(kv), attn_mfma_path(kv, F, Hq / kv->num_kv_heads),
             &p.splits, &chunk);
+  if (p.splits > kMaxGridRows) return fail(DFX_EUNSUPPORTED, "%d context splits above %d", p.splits, kMaxGridRows);
   p.attn_ws = a256(attn_ws_bytes(p.splits, F, B, Hq, D));
   // the projections followed by a finish kernel write their fp32 tiles
   // [ksplit][groups][64][N]; they run in stream order, so one region serves them all

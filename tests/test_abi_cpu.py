@@ -72,6 +72,19 @@ def test_attention_rejects(kvover, over, status, needle):
     assert st == status and needle in msg, (st, msg)
 
 
+def test_grid_extent_limits():
+    """Batches and split counts beyond a launch grid's y / z extent (65535) are refused on
+    the host, before any launch."""
+    lib = _abi.lib()
+    st, msg = attn(kv(nb=1 << 17, mb=8), batch=65536)
+    assert st == 2 and "batch" in msg
+    # 65536 requested splits of a contiguous 2^22-token cache (the vector-ALU kernel's
+    # 32-token quantum allows them): refused
+    kc = kv(dtype=0, table=None, bs=1 << 22, nb=1, heads=1, D=64)
+    st, msg = attn(kc, batch=1, maxc=1 << 22, hq=1, q2=None, o2=None, a=None, splits=65536, qdt=0)
+    assert st == 2 and "splits" in msg, msg
+
+
 def test_plan_is_host_arithmetic():
     lib = _abi.lib()
     s, n = ctypes.c_int32(), ctypes.c_size_t()
