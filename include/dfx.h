@@ -130,6 +130,7 @@ dfx_status dfx_decode_attn_plan(const dfx_kv_cache *kv, int32_t batch, int32_t n
  *               more splits than requested; dfx_decode_attn_plan reports the count.
  *  workspace    device scratch of >= the dfx_decode_attn_plan size (may be NULL
  *               when that size is 0); owned by the caller, not kept after the call.
+ *  Limits: batch and the plan's split count at most 65535 each (DFX_EUNSUPPORTED).
  * The pool is only read. Results for one (b, h, f) do not depend on the other
  * flow, heads or sequences: o1 is bit-identical with and without q2_raw.
  */
@@ -280,6 +281,7 @@ dfx_status dfx_dual_flow_decode_layer_workspace_size(const dfx_layer_weights *w,
  * the shared projection and discarded. workspace: >= the size above, no initial
  * contents needed; after the call it holds the step's intermediates
  * (dfx_dual_flow_decode_layer_taps). Calls sharing a workspace must not overlap.
+ * batch at most 65535 (DFX_EUNSUPPORTED), as for dfx_decode_attn.
  */
 dfx_status dfx_dual_flow_decode_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv,
                                       const int32_t *context_lens, int32_t batch,
