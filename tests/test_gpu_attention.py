@@ -209,6 +209,21 @@ def test_ragged_paged_full_size_sampled():
     assert np.all(np.isfinite(got[0])) and np.all(np.isfinite(got[1]))
 
 
+def test_largest_batch_sampled():
+    """65535 sequences (the grid's largest y extent) of 0-19 tokens: sampled sequences against
+    the oracle, with the planner's single split and with two splits and the merge."""
+    B = 65535
+    ctx = np.random.default_rng(17).integers(0, 20, B).astype(np.int32)
+    ctx[[0, 1]] = [0, 19]
+    case = gen.attention_case(905, B, 8, 1, 64, ctx, dtype="bf16", paged=True)
+    rows = [0, 1, 2, 32767, B - 1]
+    want = oracle(case, batches=rows)
+    for splits in (0, 2):
+        got = run_attn(case, num_splits=splits)
+        check(case, got, want, rows=rows)
+        assert np.all(np.isfinite(got[0])) and np.all(np.isfinite(got[1]))
+
+
 def test_long_context_reduced_twin():
     case = gen.attention_case(404, 8, 64, 8, 128, np.full(8, 8192, np.int32), dtype="bf16",
                               paged=True, num_blocks=8 * 512 + 9)
