@@ -102,6 +102,19 @@ def timed(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
+def stream_read(dfx, stream, nbytes=4 << 30, reps=10):
+    """Achievable HBM read bandwidth next to the 8 TB/s published figure: the library's read
+    helper (contiguous non-temporal 1 KiB loads) over a 4 GiB buffer, HIP events."""
+    import torch
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    dfx.fill_bytes(buf, 0x01010101)
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: dfx.read_bytes(buf, sink), reps, stream)
+    del buf
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"bytes": nbytes, "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def best_split_ratio(dfx, kv, B, Hq, F, mc, q1, q2, a, caches, turn, ctx_t, aws, reps, stream):
     """Dual and single flow, each timed at every split count the planner runs for a range of
     requests and reported at its own best (the plan's ratio is reported beside it)."""
@@ -311,6 +324,7 @@ def main():
                   "step_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
                   "step_bytes": int(step_bytes), "wall_s": round(wall, 3)})
 
+    extra["stream_read"] = stream_read(dfx, stream)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic_from_profiles("attn_mfma.hip", args.workload),

@@ -118,14 +118,34 @@ __global__ void __launch_bounds__(256) fill_kernel(u32x4 *dst, int64_t n, uint32
 }
 
 // Reads every 16-byte word once (a measurement of achievable read bandwidth); the XOR of
-// what each thread read goes to sink[thread] so the loads cannot be dropped.
+// what each thread read goes to sink[thread] so the loads cannot be dropped. The source is
+// cut into 4 KiB tiles; each wave streams a contiguous run of them, two tiles (8 loads of 16
+// bytes per lane, each instruction covering 1 KiB) in flight, non-temporal -- the fastest read
+// pattern measured on this GPU. Words past the last whole tile are read grid-stride.
 __global__ void __launch_bounds__(256) read_kernel(const u32x4 *src, int64_t n, uint32_t *sink) {
-  uint32_t acc = 0;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const u32x4 v = src[i];
-    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * 4, w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t tiles = n / 256, per = (tiles + waves - 1) / waves;
+  const int64_t t_end = min(min(w * per, tiles) + per, tiles);
+  int64_t t = min(w * per, tiles);
+  u32x4 acc = u32x4{0u, 0u, 0u, 0u};
+  for (; t + 1 < t_end; t += 2) {
+    u32x4 v[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) v[s] = __builtin_nontemporal_load(src + t * 256 + 64 * s + lane);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc ^= v[s];
   }
-  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+  if (t < t_end) {
+    u32x4 v[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v[s] = __builtin_nontemporal_load(src + t * 256 + 64 * s + lane);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc ^= v[s];
+  }
+  for (int64_t i = tiles * 256 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    acc ^= src[i];
+  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
 hipError_t launch_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s) {
