@@ -133,19 +133,30 @@ def best_split_ratio(dfx, kv, B, Hq, F, mc, q1, q2, a, caches, turn, ctx_t, aws,
     return best
 
 
-def timed_each(fn, reps, stream):
-    """Per-call durations (ms) of reps back-to-back calls, an event pair around each."""
+def timed_each(fn, reps, stream, flush=None):
+    """Per-call durations (ms) of reps calls, an event pair around each; flush(), if given,
+    runs between the calls outside the event pairs."""
     import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     with torch.cuda.stream(stream):
         fn()
         torch.cuda.synchronize()
         for a, b in ev:
+            if flush is not None:
+                flush()
             a.record(stream)
             fn()
             b.record(stream)
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in ev]
+
+
+def hbm_flush(dfx, nbytes=512 << 20):
+    """A callable that writes nbytes (the library's fill) so that the next call finds none of
+    its inputs in the last-level cache."""
+    import torch
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    return lambda: dfx.fill_bytes(buf, 0)
 
 
 def source_sha(name):
@@ -310,9 +321,11 @@ def main():
 
     attn_ms = timed(attn_call, args.kernel_reps, stream)
     single_ms = timed(lambda: attn_call(None, None), args.kernel_reps, stream)
-    each = np.array(timed_each(attn_call, args.kernel_reps, stream))
+    # per call, with 512 MB written between the calls (outside the event pairs)
+    each = np.array(timed_each(attn_call, args.kernel_reps, stream, flush=hbm_flush(dfx)))
     extra["attn_ms_each"] = {"median": round(float(np.median(each)), 4), "p10": round(float(np.percentile(each, 10)), 4),
-                             "p90": round(float(np.percentile(each, 90)), 4), "calls": int(each.size)}
+                             "p90": round(float(np.percentile(each, 90)), 4), "calls": int(each.size),
+                             "flush_bytes_between": 512 << 20}
     if not args.no_split_sweep:
         extra["attn_best_split"] = best_split_ratio(dfx, kv, B, shape["Hq"], F, mc, q1, q2, a, caches, turn, ctx_t,
                                                     aws, args.kernel_reps, stream)
