@@ -200,6 +200,38 @@ def test_one_token_returns_v_and_constant_v():
     assert max_err(o1, np.ones_like(o1)) < 1e-5 and max_err(o2, np.ones_like(o2)) < 1e-5
 
 
+@pytest.mark.parametrize("gain", [40.0, 150.0])
+@pytest.mark.parametrize("splits", [1, 3, 8])
+def test_peaked_softmax_and_far_apart_split_maxima(gain, splits):
+    """Queries scaled so that scores spread over tens to hundreds of units: the softmax is
+    nearly one-hot, most terms underflow, and the splits' maxima differ by far more than
+    exp's range -- the online rescale and the merge must lose nothing. Outputs within the
+    bf16 bar. lse, now of magnitude up to ~5 * gain, within the error that the kernel's query
+    representation allows: an fp32 query (the auxiliary's, q2_raw + a * q1) is carried as two
+    bf16 terms, about 2^-17 relative per element, so a score is off by at most
+    2^-16 * scale * sum_d |Q_d K_d| and the lse (a smooth maximum of the scores) by the
+    largest such bound over the keys."""
+    case = gen.attention_case(640, 2, 8, 2, 128, [1000, 777], dtype="bf16", paged=True)
+    for name in ("q1", "q2"):
+        q = gen.bf16_bits_to_f32(getattr(case, name)) * np.float32(gain)
+        setattr(case, name, gen.f32_to_bf16_bits(q))
+    o1, o2, lse = run_attn(case, num_splits=splits)
+    w1, w2, wl = oracle(case)
+    assert max_err(o1, w1) < 2e-3 and max_err(o2, w2) < 2e-3, (max_err(o1, w1), max_err(o2, w2))
+    D, G, bs = case.head_dim, case.num_q_heads // case.num_kv_heads, case.block_size
+    q1 = gen.bf16_bits_to_f32(case.q1).astype(np.float64)
+    qs = (q1, gen.bf16_bits_to_f32(case.q2).astype(np.float64) + case.a.astype(np.float64) * q1)
+    bound = np.empty_like(wl)
+    for b, n in enumerate(case.context_lens):
+        blocks = case.block_table[b, : -(-n // bs)]
+        for h in range(case.num_q_heads):
+            k = gen.bf16_bits_to_f32(case.k_pool[blocks, h // G]).reshape(-1, D)[:n].astype(np.float64)
+            for f in range(2):
+                bound[f, b, h] = 2.0 ** -16 / np.sqrt(D) * (np.abs(k) @ np.abs(qs[f][b, h])).max()
+    err = np.abs(lse - wl)
+    assert np.all(err <= 1e-4 + bound), float((err / (1e-4 + bound)).max())
+
+
 def test_ragged_paged_full_size_sampled():
     case = gen.config_attention(3)
     rows = [0, 17, 63]
