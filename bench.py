@@ -386,10 +386,14 @@ def bench_step(args):
 
     layers, caches = [], []
     nblk = B * ctx_len // bs
-    for _ in range(nl):
-        w = dfx.LayerWeights.from_row_major(gains(H), randn((Hq + 2 * Hkv) * D, H, std=0.02), randn(H, Hq * D, std=0.02),
-                                            gains(H), randn(2 * I, H, std=0.02), randn(H, I, std=0.02), Hq, Hkv, D, 1e-5,
-                                            unif(D), unif(I), unif(H))
+    rm0 = None  # layer 0's row-major matrices and vectors (the CPU baseline's sample)
+    for l in range(nl):
+        rm = dict(g_attn=gains(H), w_qkv=randn((Hq + 2 * Hkv) * D, H, std=0.02), w_o=randn(H, Hq * D, std=0.02),
+                  g_mlp=gains(H), w_gate_up=randn(2 * I, H, std=0.02), w_down=randn(H, I, std=0.02),
+                  a=unif(D), b=unif(I), c=unif(H))
+        w = dfx.LayerWeights.from_row_major(rm["g_attn"], rm["w_qkv"], rm["w_o"], rm["g_mlp"], rm["w_gate_up"],
+                                            rm["w_down"], Hq, Hkv, D, 1e-5, rm["a"], rm["b"], rm["c"])
+        rm0 = rm if l == 0 else rm0
         table = torch.randperm(nblk, generator=gen_, device="cuda").to(torch.int32).view(B, ctx_len // bs)
         caches.append(dfx.KVCache(randn(nblk, Hkv, bs, D), randn(nblk, Hkv, bs, D), table))
         layers.append(w)
@@ -402,7 +406,8 @@ def bench_step(args):
     ws.get(dfx.step_workspace_size(layers, caches, B, 2, ctx_len))
     hws = dfx.Workspace()
     if with_head:
-        w_out = dfx.pack_weight(randn(vocab, H, std=0.02))
+        w_out_rm = randn(vocab, H, std=0.02)
+        w_out = dfx.pack_weight(w_out_rm)
         g_out = gains(H)
         hws.get(dfx.output_head_workspace_size(2, B, H, vocab))
 
@@ -431,6 +436,26 @@ def bench_step(args):
         graph.replay()
     torch.cuda.synchronize()
     graph_ms = timed(graph.replay, args.steps, stream)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle.head import output_head
+        from oracle.layer import dual_flow_layer
+        wts = {k: (v.cpu().numpy() if v.dtype == torch.float32 else host_bits(v)) for k, v in rm0.items()}
+        kpool, vpool, tbl = host_bits(caches[0].k), host_bits(caches[0].v), caches[0].block_table.cpu().numpy()
+        xs = np.random.default_rng(0).standard_normal((2, B, H)).astype(np.float32)
+        before = np.full(B, ctx_len - 1)
+        sec_l, n_l, tot_l = oracle_seconds(lambda: dual_flow_layer(
+            xs, wts["g_attn"], wts["g_mlp"], wts["w_qkv"], wts["w_o"], wts["w_gate_up"], wts["w_down"], wts["a"],
+            wts["b"], wts["c"], 1e-5, kpool, vpool, tbl, before, Hq, Hkv, D), budget=1.0)
+        sec_h, n_h = 0.0, 0
+        if with_head:
+            wo, go = host_bits(w_out_rm), g_out.cpu().numpy()
+            sec_h, n_h, _ = oracle_seconds(lambda: output_head(xs, go, 1e-5, wo), budget=1.0)
+        cpu = baseline_line(1.0 / (nl * sec_l + sec_h), "steps/s",
+                            f"layer 0 of the {nl} identical-shape layers timed whole ({n_l} run(s), {sec_l:.1f} s) and "
+                            f"counted {nl} times" + (f", plus the output head ({n_h} run(s), {sec_h:.1f} s)"
+                                                    if with_head else ""))
     w_bytes = 2 * (Hq + 2 * Hkv) * D * H + 2 * H * Hq * D + 2 * 2 * I * H + 2 * H * I
     kv_bytes = 2 * B * ctx_len * Hkv * D * 2
     step_bytes = nl * (w_bytes + kv_bytes) + 2 * B * H * 2 + (2 * vocab * H if with_head else 0)
@@ -451,7 +476,7 @@ def bench_step(args):
                          "traffic": None,
                          "kernel": "whole step (weights + KV of every layer, and the output matrix, read once)",
                          "bytes_per_launch": int(step_bytes)},
-            "cpu_baseline": None, "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
+            "cpu_baseline": cpu, "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
             "tokens_per_s": round(B * 1000.0 / ms, 1), "ms_per_layer": round(ms / nl, 4)}
     print(json.dumps(line))
 
@@ -469,7 +494,8 @@ def bench_head(args):
     B, F, H, V = 32, 2, 4096, args.vocab
     x = torch.randn(F, B, H, generator=g, device="cuda")
     gain = torch.rand(H, generator=g, device="cuda") * 0.2 + 0.9
-    w = dfx.pack_weight((torch.randn(V, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16))
+    w_rm = (torch.randn(V, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    w = dfx.pack_weight(w_rm)
     ws = dfx.Workspace()
     ws.get(dfx.output_head_workspace_size(F, B, H, V))
     stream = torch.cuda.current_stream()
@@ -483,6 +509,13 @@ def bench_head(args):
     ms = timed(call, args.steps, stream)
     alg = 2 * V * H + F * B * H * 4 + 4 * H + B * 8     # W_out, rows, gain, token + alpha
     gbps = alg / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle.head import output_head
+        xs, gs, wb = x.cpu().numpy(), gain.cpu().numpy(), host_bits(w_rm)
+        sec, n, tot = oracle_seconds(lambda: output_head(xs, gs, 1e-5, wb))
+        cpu = baseline_line(B / sec, "tokens/s", f"the whole head call (batch {B}, both flows, vocab {V}), "
+                                                 f"median of {n} runs, {tot:.1f} s in total")
     line = {"metric": "dual-flow output head (shared vocab projection + mixture) tokens/s", "value": round(B * 1000.0 / ms, 1),
             "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -493,7 +526,7 @@ def bench_head(args):
                          "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                          "kernel": "whole head call (5 launches); algorithmic bytes = W_out + rows + gain + outputs",
                          "bytes_per_launch": int(alg)},
-            "cpu_baseline": None}
+            "cpu_baseline": cpu}
     print(json.dumps(line))
 
 
@@ -515,8 +548,10 @@ def bench_moe(args):
 
     gain = torch.rand(H, generator=g, device="cuda") * 0.2 + 0.9
     wr = randn(E, H)
-    gu = torch.stack([dfx.pack_weight(randn(2 * I, H)) for _ in range(E)])
-    dn = torch.stack([dfx.pack_weight(randn(H, I)) for _ in range(E)])
+    gu_rm = [randn(2 * I, H) for _ in range(E)]
+    dn_rm = [randn(H, I) for _ in range(E)]
+    gu = torch.stack([dfx.pack_weight(t) for t in gu_rm])
+    dn = torch.stack([dfx.pack_weight(t) for t in dn_rm])
     bvec = torch.rand(I, generator=g, device="cuda") * 2 - 1
     cvec = torch.rand(H, generator=g, device="cuda") * 2 - 1
     x0 = torch.randn(2, B, H, generator=g, device="cuda")
@@ -544,6 +579,16 @@ def bench_moe(args):
         res[(F, k2)] = (ms, alg, used)
     ms, alg, used = res[(2, 2)]
     gbps = alg / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle.moe import moe_mlp
+        import numpy as np
+        args_np = (x0.cpu().numpy(), gain.cpu().numpy(), 1e-5, host_bits(wr),
+                   np.stack([host_bits(t) for t in gu_rm]), np.stack([host_bits(t) for t in dn_rm]), 2, 2,
+                   bvec.cpu().numpy(), cvec.cpu().numpy())
+        sec, n, tot = oracle_seconds(lambda: moe_mlp(*args_np))
+        cpu = baseline_line(B / sec, "tokens/s", f"the whole block (batch {B}, both flows, fan-outs 2 / 2), "
+                                                 f"median of {n} runs, {tot:.1f} s in total")
     line = {"metric": "dual-flow MoE block (router replay) tokens/s", "value": round(B * 1000.0 / ms, 1),
             "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -555,7 +600,7 @@ def bench_moe(args):
                          "kernel": "whole block call (7 launches, timed with the residual reset copy); algorithmic "
                                    "bytes = router + used experts' matrices once + rows",
                          "bytes_per_launch": int(alg), "experts_used": used},
-            "cpu_baseline": None,
+            "cpu_baseline": cpu,
             "aux_fanout_4": {"ms": round(res[(2, 4)][0], 4), "experts_used": res[(2, 4)][2]},
             "primary_only": {"ms": round(res[(1, 2)][0], 4), "experts_used": res[(1, 2)][2]},
             "dual_over_single": round(ms / res[(1, 2)][0], 3)}
@@ -579,8 +624,10 @@ def bench_prefill(args):
         return (torch.randn(*shape, generator=gen_, device="cuda") * std).to(torch.bfloat16)
 
     gains = lambda n: torch.rand(n, generator=gen_, device="cuda") * 0.2 + 0.9
-    w = dfx.LayerWeights.from_row_major(gains(H), randn((Hq + 2 * Hkv) * D, H), randn(H, Hq * D), gains(H),
-                                        randn(2 * I, H), randn(H, I), Hq, Hkv, D, 1e-5)
+    rm = dict(g_attn=gains(H), w_qkv=randn((Hq + 2 * Hkv) * D, H), w_o=randn(H, Hq * D), g_mlp=gains(H),
+              w_gate_up=randn(2 * I, H), w_down=randn(H, I))
+    w = dfx.LayerWeights.from_row_major(rm["g_attn"], rm["w_qkv"], rm["w_o"], rm["g_mlp"], rm["w_gate_up"],
+                                        rm["w_down"], Hq, Hkv, D, 1e-5)
     nblk = B * (T // bs + 1)
     table = torch.randperm(nblk, generator=gen_, device="cuda").to(torch.int32).view(B, -1)
     cache = dfx.KVCache(randn(nblk, Hkv, bs, D, std=1.0), randn(nblk, Hkv, bs, D, std=1.0), table)
@@ -614,6 +661,17 @@ def bench_prefill(args):
     flops = 2.0 * rows * wparams + attn_flops
     tf = flops / (ms * 1e-3) / 1e12
     atf = attn_flops / (attn_ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle.prefill import prefill_layer
+        xs, kpool, vpool, tbl = x0.cpu().numpy(), host_bits(cache.k), host_bits(cache.v), table.cpu().numpy()
+        wts = {k: (v.cpu().numpy() if v.dtype == torch.float32 else host_bits(v)) for k, v in rm.items()}
+        sec, n, tot = oracle_seconds(lambda: prefill_layer(xs, wts["g_attn"], wts["g_mlp"], wts["w_qkv"], wts["w_o"],
+                                                           wts["w_gate_up"], wts["w_down"], 1e-5, kpool, vpool, tbl,
+                                                           np.zeros(B, np.int64), Hq, Hkv, D), budget=1.0)
+        cpu = baseline_line(rows / sec, "tokens/s", f"the whole layer over the {B} x {T}-token chunk, "
+                                                    f"{n} run(s), {tot:.1f} s in total")
     line = {"metric": "dual-flow prefill (primary only) tokens/s, one layer", "value": round(rows * 1000.0 / ms, 1),
             "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -624,7 +682,7 @@ def bench_prefill(args):
                          "frac": round(tf / 2500.0, 4), "traffic": None,
                          "kernel": "whole prefill layer (8 launches); algorithmic flops of projections + causal attention",
                          "flops_per_launch": flops},
-            "cpu_baseline": None,
+            "cpu_baseline": cpu,
             "attention": {"ms": round(attn_ms, 4), "tflops": round(atf, 1), "frac_of_bf16_peak": round(atf / 2500.0, 4)},
             "dual_attention": {"ms": round(dual_ms, 4), "tflops": round(2 * attn_flops / (dual_ms * 1e-3) / 1e12, 1),
                                "dual_over_single": round(dual_ms / attn_ms, 3)}}
@@ -669,6 +727,30 @@ def cpu_baseline(workload, env):
                   f"passes over the batch, {t:.1f} s), scaled by the share of context tokens")
     return {"value": round(1.0 / full, 4), "unit": "steps/s", "cores": cpu_threads(), "kind": "oracle",
             "sample": sample, "cpu_model": cpu_model()}
+
+
+def oracle_seconds(fn, budget=10.0, max_runs=50):
+    """Median wall seconds of an oracle call, repeated until about `budget` seconds have
+    passed (at least once); also the number of runs and their total."""
+    import numpy as np
+    times = []
+    while not times or (sum(times) < budget and len(times) < max_runs):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), len(times), float(sum(times))
+
+
+def host_bits(t):
+    """A bf16 device tensor's bit patterns as a host uint16 array."""
+    import numpy as np
+    import torch
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def baseline_line(value, unit, sample):
+    return {"value": round(value, 4), "unit": unit, "cores": cpu_threads(), "kind": "oracle", "sample": sample,
+            "cpu_model": cpu_model()}
 
 
 def cpu_model():
