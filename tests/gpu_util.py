@@ -24,9 +24,9 @@ def cache_of(case):
                        None if case.block_table is None else dev(case.block_table))
 
 
-def run_attn(case, cache=None, q2=True, a=True, num_splits=0, max_context=None, q1=None, q2v=None):
+def run_attn(case, cache=None, q2=True, a=True, num_splits=0, max_context=None, q1=None, q2v=None, ctx=None):
     cache = cache_of(case) if cache is None else cache
-    ctx = dev(case.context_lens)
+    ctx = dev(case.context_lens if ctx is None else ctx)
     mc = int(case.context_lens.max()) if max_context is None else max_context
     q1t = dev(case.q1 if q1 is None else q1)
     q2t = (dev(case.q2 if q2v is None else q2v) if q2 else None)

@@ -185,6 +185,19 @@ def test_layouts_bit_identical_and_cache_read_only():
         assert np.array_equal(x, y) and np.array_equal(x, z) and np.array_equal(x, w)
 
 
+@pytest.mark.parametrize("paged,splits", [(True, 0), (True, 3), (False, 2)])
+def test_context_lengths_above_max_context_are_clamped(paged, splits):
+    """A sequence whose context_lens entry exceeds max_context attends to max_context
+    positions (n_b = min(context_lens[b], max_context)); negative entries count as 0."""
+    case = gen.attention_case(615, 4, 16, 4, 128, [300, 90, 250, 5], dtype="bf16", paged=paged)
+    mc = 200
+    lens = np.array([300, 90, 250, -7], np.int32)
+    got = run_attn(case, num_splits=splits, max_context=mc, ctx=lens)
+    clamped = gen.attention_case(615, 4, 16, 4, 128, [300, 90, 250, 5], dtype="bf16", paged=paged)
+    clamped.context_lens = np.minimum(np.maximum(lens, 0), mc).astype(np.int32)
+    check(clamped, got, oracle(clamped))
+
+
 def test_one_token_returns_v_and_constant_v():
     case = gen.attention_case(606, 4, 32, 8, 128, [1, 1, 1, 1], dtype="bf16")
     o1, o2, _ = run_attn(case)
