@@ -29,6 +29,7 @@ __global__ void __launch_bounds__(1024) moe_route_kernel(MoeArgs a) {
   __shared__ float red[2][16];
   __shared__ float lg[2][kMoeMaxExperts];
   __shared__ int32_t sel[kMoeMaxK];
+  extern __shared__ u32x2 s_h[];  // the normed bf16 rows of both flows, 4 values per entry
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int F = a.F, E = a.E, H = a.H;
   for (int f = 0; f < F; ++f) {
@@ -45,16 +46,29 @@ __global__ void __launch_bounds__(1024) moe_route_kernel(MoeArgs a) {
       }
     }
     const float r = norm_scale(v, H, a.eps, red[f]);
-    norm_store(v, gg, r, H, (uint16_t *)a.h, 0, f, b, row);
+    // h = bf16(v * r * gain), to the workspace (the experts' rows are gathered from it) and
+    // to LDS for the router's dot products
+#pragma unroll
+    for (int u = 0; u < kNormSlices; ++u) {
+      const int i = threadIdx.x + 1024 * u;
+      if (4 * i >= H) continue;
+      const u32x2 o{pack_bf16x2(v[u][0] * r * gg[u][0], v[u][1] * r * gg[u][1]),
+                    pack_bf16x2(v[u][2] * r * gg[u][2], v[u][3] * r * gg[u][3])};
+      *(u32x2 *)(a.h + row * H + 4 * i) = o;
+      s_h[f * (H / 4) + i] = o;
+    }
   }
-  __syncthreads();  // this work-group's normed rows are written
+  __syncthreads();  // the normed rows are in LDS
   for (int d = wave; d < F * E; d += 16) {
     const int f = d / E, e = d % E;
-    const uint16_t *hr = a.h + ((int64_t)f * a.B + b) * H;
+    const u32x2 *hr = s_h + f * (H / 4);
     const uint16_t *wr = a.w_router + (int64_t)e * H;
     float acc = 0.f;
+#pragma unroll 8
     for (int k = lane * 8; k < H; k += 512) {
-      const u32x4 hv = *(const u32x4 *)(hr + k), wv = *(const u32x4 *)(wr + k);
+      const u32x2 h0 = hr[k / 4], h1 = hr[k / 4 + 1];
+      const u32x4 wv = *(const u32x4 *)(wr + k);
+      const uint32_t hv[4] = {h0[0], h0[1], h1[0], h1[1]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc = fmaf(bf16_lo(hv[i]), bf16_lo(wv[i]), acc);
@@ -217,7 +231,7 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(MoeArgs a) {
 hipError_t launch_moe(int which, const MoeArgs &a, hipStream_t s) {
   switch (which) {
     case kMoeRoute:
-      moe_route_kernel<<<a.B, 1024, 0, s>>>(a);
+      moe_route_kernel<<<a.B, 1024, (size_t)a.F * a.H * sizeof(uint16_t), s>>>(a);
       break;
     case kMoeLists:
       moe_lists_kernel<<<1, 1024, (size_t)a.E * ((a.B + 31) / 32) * sizeof(uint32_t), s>>>(a);
