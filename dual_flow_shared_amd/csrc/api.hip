@@ -959,7 +959,7 @@ dfx_status prefill_plan(const dfx_layer_weights *w, const dfx_kv_cache *kv, int3
 }
 
 // One projection of the prefill rows (one flow): the LDS-staged dense kernel when there is more
-// than one row group and K is a multiple of 64, else the grouped linear with every 64-row group
+// than one row group (K a multiple of 32), else the grouped linear with every 64-row group
 // its own work-group slice. fp32 out (optionally plus residual, in place), or SwiGLU bf16 rows.
 dfx_status prefill_linear(int32_t rows, int32_t K, int32_t N, const uint16_t *x_packed, const uint16_t *w,
                           void *y, const float *residual, int swiglu, hipStream_t s) {

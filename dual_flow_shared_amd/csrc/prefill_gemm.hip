@@ -7,8 +7,9 @@
 // A work-group owns 256 output features x 128 rows as 2 x 4 waves of 64 features x 64 rows
 // (two waves per SIMD, so one can issue MFMAs while the other waits). Per k-step it stages the 24
 // fragments it needs (16 of W, 8 of X; 24 KiB) in LDS, each loaded once from global memory
-// kDensePipe k-steps ahead through registers; every wave then reads its 8 fragments from LDS and
-// issues 16 MFMAs. LDS holds two k-steps (a barrier per k-step).
+// straight into LDS (global_load_lds, no register staging) two k-steps ahead; every wave reads
+// its 8 fragments from LDS and issues 16 MFMAs. LDS holds three k-steps: the one being read and
+// the two in flight (one barrier per k-step).
 //
 // Work-group i runs on XCD i % 8; all row tiles of one feature tile go to one XCD back to back,
 // so the tile's weights are fetched from HBM about once and re-read from that XCD's L2.
@@ -21,7 +22,7 @@
 
 namespace dfx {
 
-constexpr int kDensePipe = 2;  // k-steps of fragments in flight per thread (registers)
+constexpr int kDenseAhead = 2;  // k-steps of fragments in flight (LDS slots: kDenseAhead + 1)
 // feature waves (64 features each) per work-group; 2 (128 x 128 per work-group, 4 waves) ran
 // the prefill layer in 2.59 ms against 2.10
 constexpr int kFeatWaves = 4;
@@ -34,7 +35,7 @@ static_assert(kDenseFrags % kDenseWaves == 0, "staging");
 
 template <bool SWIGLU>
 __global__ void __launch_bounds__(64 * kDenseWaves) prefill_gemm_kernel(PrefillGemmArgs p) {
-  __shared__ u32x4 lds[2][kDenseFrags][64];
+  __shared__ u32x4 lds[kDenseAhead + 1][kDenseFrags][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
   const int wr = wave / kFeatWaves, wc = wave % kFeatWaves;  // row group of the tile, feature wave
@@ -70,16 +71,6 @@ __global__ void __launch_bounds__(64 * kDenseWaves) prefill_gemm_kernel(PrefillG
       sstep[r] = 4 * 512;
     }
   }
-  u32x4 stage[kDensePipe][kDenseStage];
-  auto gload = [&](int s, u32x4 *d) {
-    const int sc = min(s, nks - 1);  // past the last k-step: re-read it (never used)
-#pragma unroll
-    for (int r = 0; r < kDenseStage; ++r) d[r] = *(const u32x4 *)(src[r] + sc * sstep[r]);
-  };
-  auto lstore = [&](int slot, const u32x4 *d) {
-#pragma unroll
-    for (int r = 0; r < kDenseStage; ++r) lds[slot][wave + kDenseWaves * r][lane] = d[r];
-  };
   // this wave's weight fragments in LDS (gate/up mode: 2 gate groups and their 2 up groups)
   int wfrag[4];
 #pragma unroll
@@ -92,31 +83,44 @@ __global__ void __launch_bounds__(64 * kDenseWaves) prefill_gemm_kernel(PrefillG
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Fragments go from global memory straight to LDS (16 bytes per lane; a fragment's 64 lanes
+  // are 1 KiB contiguous in LDS) kDenseAhead k-steps ahead. Waits are explicit: this thread's
+  // loads of k-step s are done once at most kDenseStage loads (those of s + 1) are outstanding;
+  // the barrier then makes k-step s's slot complete for every wave, and every wave has finished
+  // reading the slot that the loads of s + 2 overwrite. Those loads are issued after this
+  // wave's LDS reads of k-step s (measured: 2% faster than before them).
+  static_assert(kDenseAhead == 2 && kDenseStage < 16, "one k-step of loads outstanding at each wait");
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto dma = [&](int st, int slot) {
+    const int sc = min(st, nks - 1);  // past the last k-step: re-read it (never used)
 #pragma unroll
-  for (int u = 0; u < kDensePipe; ++u) gload(u, stage[u]);
-  lstore(0, stage[0]);
-  gload(kDensePipe, stage[0]);
-  __syncthreads();
-  // k-step s = base + u: LDS slot s & 1 holds it; stage[(u + 1) % kDensePipe] holds s + 1
-  for (int base = 0; base < nks; base += kDensePipe) {
+    for (int r = 0; r < kDenseStage; ++r)
+      __builtin_amdgcn_global_load_lds((const void *)(src[r] + sc * sstep[r]),
+                                       (lds_void *)&lds[slot][wave + kDenseWaves * r][0], 16, 0, 0);
+  };
+  // s_waitcnt immediates (vmcnt in bits 3:0, expcnt and lgkmcnt fields at their no-wait maxima)
+  constexpr int kWaitNext = kDenseStage | (0x7 << 4) | (0xF << 8);
+  constexpr int kWaitAll = 0 | (0x7 << 4) | (0xF << 8);
+  dma(0, 0);
+  dma(1, 1);
+  int slot = 0;
+  for (int s = 0; s < nks; ++s) {
+    __builtin_amdgcn_s_waitcnt(kWaitNext);
+    __builtin_amdgcn_s_barrier();
+    u32x4 wf[4], xf[4];
 #pragma unroll
-    for (int u = 0; u < kDensePipe; ++u) {
-      const int s = base + u, slot = u & 1;  // kDensePipe is even
-      u32x4 wf[4], xf[4];
+    for (int c = 0; c < 4; ++c) wf[c] = lds[slot][wfrag[c]][lane];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) wf[c] = lds[slot][wfrag[c]][lane];
+    for (int nb = 0; nb < 4; ++nb) xf[nb] = lds[slot][kWFrags + 4 * wr + nb][lane];
+    dma(s + 2, slot == 0 ? 2 : slot - 1);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) xf[nb] = lds[slot][kWFrags + 4 * wr + nb][lane];
-      lstore(slot ^ 1, stage[(u + 1) % kDensePipe]);
-      gload(s + 1 + kDensePipe, stage[(u + 1) % kDensePipe]);
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[c][nb] = mfma16x16x32(as_bf16x8(wf[c]), as_bf16x8(xf[nb]), acc[c][nb]);
-      __syncthreads();
-    }
+      for (int nb = 0; nb < 4; ++nb)
+        acc[c][nb] = mfma16x16x32(as_bf16x8(wf[c]), as_bf16x8(xf[nb]), acc[c][nb]);
+    slot = slot == 2 ? 0 : slot + 1;
   }
+  __builtin_amdgcn_s_waitcnt(kWaitAll);  // no load into LDS in flight when the work-group ends
 
   // C layout: lane holds row 16 nb + n of its group and features 16 cg + 4 j .. + 3
   const int grp = 2 * rt + wr;
@@ -159,7 +163,7 @@ __global__ void __launch_bounds__(64 * kDenseWaves) prefill_gemm_kernel(PrefillG
 }
 
 bool prefill_gemm_fits(int32_t K, int32_t N, bool swiglu) {
-  return K % (32 * kDensePipe) == 0 && N % (swiglu ? 32 : 16) == 0;
+  return K % 32 == 0 && N % (swiglu ? 32 : 16) == 0;
 }
 
 hipError_t launch_prefill_gemm(const PrefillGemmArgs &a, bool swiglu, hipStream_t s) {

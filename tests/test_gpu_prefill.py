@@ -121,6 +121,24 @@ def test_prefill_layer_parity_and_appended_rows():
         assert np.all(np.abs(g - r) <= np.ldexp(1.0, e - 8))
 
 
+def test_prefill_layer_odd_k_steps():
+    """hidden 288 and intermediate 544: every projection's K is an odd number of 32-wide
+    k-steps (9, 17, 32 for W_o), and 3 x 50 rows make three 64-row groups with a ragged tail."""
+    B, start, T = 3, 4, 50
+    c = gen.layer_case(703, batch=B, context=start + 1, capacity=start + T + 8, hidden=288, num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, intermediate=544, w_std=0.05)
+    x = np.random.default_rng(7).standard_normal((B, T, c.hidden)).astype(np.float32)
+    cache = cache_of(c.cache)
+    st = np.full(B, start, np.int32)
+    xt = dev(x)
+    dfx.prefill_layer(xt, weights_of(c), cache, dev(st), start + T + 8)
+    torch.cuda.synchronize()
+    want, _, _, _ = prefill_layer(x, c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.eps,
+                                  c.cache.k_pool, c.cache.v_pool, c.cache.block_table, st, c.num_q_heads,
+                                  c.num_kv_heads, c.head_dim)
+    layer_close(xt.cpu().numpy(), want)
+
+
 def test_chunked_prefill_is_bit_identical_to_one_chunk():
     B, start, T, T1 = 2, 6, 40, 17
     c = gen.layer_case(702, batch=B, context=start + 1, capacity=start + T + 8, **SMALL)
