@@ -32,28 +32,33 @@ __global__ void __launch_bounds__(1024) moe_route_kernel(MoeArgs a) {
   extern __shared__ u32x2 s_h[];  // the normed bf16 rows of both flows, 4 values per entry
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int F = a.F, E = a.E, H = a.H;
-  for (int f = 0; f < F; ++f) {
-    const int64_t row = (int64_t)f * a.B + b;
-    const float *xr = a.x + row * H;
-    f32x4 v[kNormSlices], gg[kNormSlices];
+  // Both flows' rows and the gain are loaded together (one memory round trip), then each
+  // row is normed.
+  f32x4 v[2][kNormSlices], gg[kNormSlices];
 #pragma unroll
-    for (int u = 0; u < kNormSlices; ++u) {
-      const int i = threadIdx.x + 1024 * u;
-      v[u] = gg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (4 * i < H) {
-        v[u] = *(const f32x4 *)(xr + 4 * i);
-        gg[u] = *(const f32x4 *)(a.gain + 4 * i);
-      }
+  for (int u = 0; u < kNormSlices; ++u) {
+    const int i = threadIdx.x + 1024 * u;
+    v[0][u] = v[1][u] = gg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (4 * i < H) {
+      gg[u] = *(const f32x4 *)(a.gain + 4 * i);
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+        if (f < F) v[f][u] = *(const f32x4 *)(a.x + ((int64_t)f * a.B + b) * H + 4 * i);
     }
-    const float r = norm_scale(v, H, a.eps, red[f]);
+  }
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    if (f >= F) break;
+    const int64_t row = (int64_t)f * a.B + b;
+    const float r = norm_scale(v[f], H, a.eps, red[f]);
     // h = bf16(v * r * gain), to the workspace (the experts' rows are gathered from it) and
     // to LDS for the router's dot products
 #pragma unroll
     for (int u = 0; u < kNormSlices; ++u) {
       const int i = threadIdx.x + 1024 * u;
       if (4 * i >= H) continue;
-      const u32x2 o{pack_bf16x2(v[u][0] * r * gg[u][0], v[u][1] * r * gg[u][1]),
-                    pack_bf16x2(v[u][2] * r * gg[u][2], v[u][3] * r * gg[u][3])};
+      const u32x2 o{pack_bf16x2(v[f][u][0] * r * gg[u][0], v[f][u][1] * r * gg[u][1]),
+                    pack_bf16x2(v[f][u][2] * r * gg[u][2], v[f][u][3] * r * gg[u][3])};
       *(u32x2 *)(a.h + row * H + 4 * i) = o;
       s_h[f * (H / 4) + i] = o;
     }
