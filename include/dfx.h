@@ -85,7 +85,7 @@ typedef struct dfx_kv_cache {
   int32_t reserved;           /* must be 0 */
 } dfx_kv_cache;
 
-/* Library version (DFX_VERSION of the build). */
+/* Library version (the DFX_VERSION it was compiled with). */
 int dfx_version(void);
 
 /* Message of the last failing call on this thread ("" if none). The pointer is

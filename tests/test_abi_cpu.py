@@ -342,3 +342,13 @@ def test_prefill_rejects():
     assert lib.dfx_prefill_step_workspace_size(ws, ks, 1, 2, 16, 64, ctypes.byref(n)) == 0
     assert lib.dfx_prefill_step(ws, ks, 1, FAKE, 0, FAKE, FAKE, 2, 16, 64, FAKE, FAKE, n.value, None) == 1
     assert lib.dfx_prefill_step(ws, ks, 0, FAKE, 10, FAKE, FAKE, 2, 16, 64, FAKE, FAKE, n.value, None) == 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it exits with status 2 and says so, before
+    touching a GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(HEADER), "..", "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
