@@ -36,6 +36,8 @@ Functions and their pins (tests/test_oracle_*.py):
        prefill_step            aux started at the last prompt position = aux at every position
   prefill.prefill_dual_      -- torch causal SDPA per flow with Q2 materialised (per-head a);
        attention               primary rows = prefill_attention's; Q2 = Q1 -> O2 = O1
+  prefill.prefill_layer_rows -- prefill_layer (from position 0) at the sampled rows, and the
+                               keys and values it appends
 The placement of the b and c coupling vectors is a reading of the pages (they
 name the levels, not the formula); it is pinned only by the identities above:
 "parity unpinned" beyond this reading. So is the mixture weight alpha_t = (1 + c_t) / 2

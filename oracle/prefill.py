@@ -101,3 +101,33 @@ def prefill_step(tokens, table_primary, layers, start_pos, dtype=np.float64):
                                      L.num_kv_heads, L.head_dim, dtype=dtype)
         pools.append((kp, vp))
     return x, pools
+
+
+def prefill_layer_rows(x, g_attn, g_mlp, w_qkv, w_o, w_gate_up, w_down, eps, num_q_heads, num_kv_heads,
+                       head_dim, samples, dtype=np.float64):
+    """prefill_layer's output rows at the (sequence, position) pairs ``samples`` of a chunk that
+    starts at position 0 (nothing cached before it), for chunks too long to run whole: the same
+    steps and rounding points, with every row normed and projected to Q/K/V (the chunk's keys
+    and values), and attention, W_o with the residual, the MLP norm, gate/up with SwiGLU and
+    W_down run for the sampled rows only. The chunk's keys and values are held as a cache of one
+    block per sequence. Returns (x_out [len(samples)][hidden] fp64, k, v) with k, v bf16 bits
+    [B][T][Hkv][D]."""
+    x = np.asarray(x, np.float64)
+    B, T, H = x.shape
+    Hq, Hkv, D = num_q_heads, num_kv_heads, head_dim
+    rows = x.reshape(1, B * T, H)
+    qkv = grouped_linear(rmsnorm(rows, g_attn, eps, dtype), w_qkv, dtype=dtype)[0].reshape(B, T, -1)
+    k = bf16_bits(qkv[..., Hq * D: (Hq + Hkv) * D]).reshape(B, T, Hkv, D)
+    v = bf16_bits(qkv[..., (Hq + Hkv) * D:]).reshape(B, T, Hkv, D)
+    k_pool = np.ascontiguousarray(k.transpose(0, 2, 1, 3))  # block b = sequence b
+    v_pool = np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+    o = np.empty((1, len(samples), Hq * D))
+    for i, (b, t) in enumerate(samples):
+        o1, _, _ = decode_attention(qkv[b, t, : Hq * D].reshape(1, Hq, D), None, None, 0, k_pool, v_pool,
+                                    np.array([[b]], np.int32), np.array([t + 1], np.int32), dtype=dtype)
+        o[0, i] = o1.reshape(-1)
+    res = rows[:, [b * T + t for b, t in samples]]
+    x1 = grouped_linear(o, w_o, residual=res, dtype=dtype)
+    inter = swiglu_couple(grouped_linear(rmsnorm(x1, g_mlp, eps, dtype), w_gate_up, dtype=dtype), None, dtype)
+    x2 = grouped_linear(inter, w_down, residual=x1, dtype=dtype)
+    return x2[0], k, v

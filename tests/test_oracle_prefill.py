@@ -12,7 +12,8 @@ import torch
 import dfx_inputs as gen
 from oracle.layer import dual_flow_layer
 from oracle.numerics import widen
-from oracle.prefill import prefill_attention, prefill_dual_attention, prefill_layer, prefill_step
+from oracle.prefill import (prefill_attention, prefill_dual_attention, prefill_layer, prefill_layer_rows,
+                            prefill_step)
 from oracle.step import dual_flow_step
 
 SMALL = dict(hidden=64, num_q_heads=4, num_kv_heads=2, head_dim=32, intermediate=64, w_std=0.1)
@@ -92,6 +93,29 @@ def test_prefill_layer_equals_token_by_token_decode():
                                        c.num_q_heads, c.num_kv_heads, c.head_dim)
         assert np.allclose(got[:, t], y[0], rtol=0, atol=1e-9)
     assert np.array_equal(kp, kq) and np.array_equal(vp, vq)
+
+
+def test_sampled_prefill_rows_equal_the_whole_layer():
+    """The sampled-row composition (for chunks too long to run whole) reproduces prefill_layer
+    from position 0 at every sampled row, and its keys and values are the ones prefill_layer
+    appends, gathered through the block table."""
+    T = 11
+    c = prefill_case(44, start=0, T=T)
+    xs = np.random.default_rng(5).standard_normal((2, T, c.hidden)).astype(np.float32)
+    kv = c.cache
+    whole, kp, vp, _ = prefill_layer(xs, c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.eps,
+                                     kv.k_pool, kv.v_pool, kv.block_table, np.zeros(2), c.num_q_heads,
+                                     c.num_kv_heads, c.head_dim)
+    samples = [(0, 0), (0, 5), (1, 10), (1, 3), (0, 10)]
+    rows, k, v = prefill_layer_rows(xs, c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.eps,
+                                    c.num_q_heads, c.num_kv_heads, c.head_dim, samples)
+    for i, (b, t) in enumerate(samples):
+        assert np.allclose(rows[i], whole[b, t], rtol=0, atol=1e-12)
+    bs = kv.k_pool.shape[2]
+    for b in range(2):
+        for t in range(T):
+            blk = kv.block_table[b, t // bs]
+            assert np.array_equal(k[b, t], kp[blk, :, t % bs]) and np.array_equal(v[b, t], vp[blk, :, t % bs])
 
 
 def test_chunked_prefill_equals_one_chunk():
