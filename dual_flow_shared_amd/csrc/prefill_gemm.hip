@@ -108,9 +108,9 @@ prefill_gemm_kernel(PrefillGemmArgs p) {
   // Fragments go from global memory straight to LDS (16 bytes per lane; a fragment's 64 lanes
   // are 1 KiB contiguous in LDS) Ahead k-steps ahead. Waits are explicit: this thread's loads
   // of k-step s are done once at most (Ahead - 1) kStage loads (those of s + 1 ..) are
-  // outstanding; the barrier then makes k-step s's slot complete for every wave, and every wave
-  // has finished reading the slot that the loads of s + Ahead overwrite. Those loads are issued after this
-  // wave's LDS reads of k-step s (measured: 2% faster than before them).
+  // outstanding; the barrier then makes k-step s's slot complete for every wave, and every
+  // wave has finished reading the slot that the loads of s + Ahead overwrite. Those loads are
+  // issued after this wave's LDS reads of k-step s (measured: 2% faster than before them).
   typedef __attribute__((address_space(3))) void lds_void;
   auto dma = [&](int st, int slot) {
     const int sc = min(st, nks - 1);  // past the last k-step: re-read it (never used)
