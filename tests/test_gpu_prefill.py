@@ -87,6 +87,37 @@ def test_prefill_dual_attention(paged, D, Hq, Hkv, T, starts, per_head):
     assert torch.equal(s1, s2) and torch.equal(s1, p1)
 
 
+def test_prefill_attention_full_size_sampled_positions():
+    """The prefill benchmark's attention calls (2 sequences x 2048 positions from position 0,
+    32/8 heads x 128, paged bf16 cache of 16-token blocks in a permuted pool): every head of
+    both sequences at sampled positions against the oracle's one-position chunk starting there,
+    for the primary-only call and both flows; the two calls' primary rows bit-identical."""
+    B, T, Hq, Hkv, D = 2, 2048, 32, 8, 128
+    st = np.zeros(B, np.int32)
+    c = gen.attention_case(690, B, Hq, Hkv, D, np.full(B, T, np.int32), "bf16", paged=True, block_size=16,
+                           capacity=T + 16)
+    rng = np.random.default_rng(12)
+    q1 = rng.standard_normal((B, T, Hq, D)).astype(np.float32)
+    q2 = rng.standard_normal((B, T, Hq, D)).astype(np.float32)
+    a = rng.uniform(-1, 1, D).astype(np.float32)
+    cache = cache_of(c)
+    q1t, stt = dev(q1), dev(st)
+    print(f"prefill attention B={B} T={T}", flush=True)
+    p1, pl = dfx.prefill_attn(q1t, cache, stt, T + 16, want_lse=True)
+    o1, o2, lse = dfx.prefill_dual_attn(q1t, dev(q2), dev(a), cache, stt, T + 16, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, p1)
+    p1, pl, o2, lse = p1.cpu().numpy(), pl.cpu().numpy(), o2.cpu().numpy(), lse.cpu().numpy()
+    for t in [0, 1, 15, 16, 31, 32, 1000, T - 2, T - 1] + [int(u) for u in rng.integers(0, T, 5)]:
+        w1, wl1 = prefill_attention(q1[:, [t]], c.k_pool, c.v_pool, c.block_table, st + t)
+        d1, d2, dl = prefill_dual_attention(q1[:, [t]], q2[:, [t]], a, 0, c.k_pool, c.v_pool, c.block_table, st + t)
+        for got, want in ((p1[:, t], w1[:, 0]), (p1[:, t], d1[:, 0]), (o2[:, t], d2[:, 0])):
+            err = np.abs(got - want).max()
+            assert err < 2e-3 and err < 5e-5, (t, err)
+        assert np.abs(pl[:, t] - wl1[:, 0]).max() < 1e-4
+        assert np.abs(lse[:, :, t] - dl[:, :, 0]).max() < 1e-4
+
+
 SMALL = dict(hidden=256, num_q_heads=8, num_kv_heads=2, head_dim=128, intermediate=512, w_std=0.05)
 
 
