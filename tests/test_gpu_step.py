@@ -38,6 +38,48 @@ def test_step_equals_layer_calls_bit_for_bit():
         assert np.array_equal(host_bits(a.k), host_bits(b.k)) and np.array_equal(host_bits(a.v), host_bits(b.v))
 
 
+def test_full_size_step_equals_layer_calls_bit_for_bit():
+    """The decode step in the one-layer workload's shape and the benchmark's launch
+    configuration (batch 32, context 8192, hidden 4096, 32/8 heads x 128, SwiGLU 14336, paged
+    bf16 caches in permuted pools), three layers, seeded weights drawn on the device: the
+    output rows and every cache equal one layer call per layer, bit for bit. Each layer is
+    checked against the oracle at this size in the layer tests."""
+    g = torch.Generator(device="cuda").manual_seed(77)
+    B, H, Hq, Hkv, D, I, ctx_len, bs, vocab = 32, 4096, 32, 8, 128, 14336, 8192, 16, 1000
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+
+    def unif(n, lo, hi):
+        return torch.rand(n, generator=g, device="cuda") * (hi - lo) + lo
+
+    layers, caches, refs = [], [], []
+    nblk = B * ctx_len // bs
+    for _ in range(3):
+        layers.append(dfx.LayerWeights.from_row_major(
+            unif(H, 0.9, 1.1), randn((Hq + 2 * Hkv) * D, H, std=0.02), randn(H, Hq * D, std=0.02),
+            unif(H, 0.9, 1.1), randn(2 * I, H, std=0.02), randn(H, I, std=0.02), Hq, Hkv, D, 1e-5,
+            unif(D, -1, 1), unif(I, -1, 1), unif(H, -1, 1)))
+        table = torch.randperm(nblk, generator=g, device="cuda").to(torch.int32).view(B, ctx_len // bs)
+        kv = dfx.KVCache(randn(nblk, Hkv, bs, D), randn(nblk, Hkv, bs, D), table)
+        caches.append(kv)
+        refs.append(dfx.KVCache(kv.k.clone(), kv.v.clone(), table))
+    e1, e2 = randn(vocab, H), randn(vocab, H)
+    tokens = torch.randint(0, vocab, (B,), generator=g, device="cuda", dtype=torch.int32)
+    ctx = torch.full((B,), ctx_len, dtype=torch.int32, device="cuda")
+    print("full-size step, 3 layers", flush=True)
+    x = dfx.dual_flow_decode_step(tokens, e1, e2, layers, caches, ctx, ctx_len)
+    xr = torch.stack([e1[tokens.long()].float(), e2[tokens.long()].float()]).contiguous()
+    for w, kv in zip(layers, refs):
+        dfx.dual_flow_decode_layer(xr, w, kv, ctx, ctx_len)
+    torch.cuda.synchronize()
+    assert torch.isfinite(x).all()
+    assert torch.equal(x, xr)
+    for a, b in zip(caches, refs):
+        assert torch.equal(a.k.view(torch.int16), b.k.view(torch.int16))
+        assert torch.equal(a.v.view(torch.int16), b.v.view(torch.int16))
+
+
 def test_step_primary_only_and_against_the_oracle():
     c = gen.step_case(902, 2, **KW)
     layers, caches, ctx, maxc, tokens, e1, e2 = inputs(c)
