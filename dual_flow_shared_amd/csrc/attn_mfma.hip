@@ -9,9 +9,9 @@
 // Per 32-token tile a wave computes
 //   S^T[tok][row] = K[tok][:] . Q[row][:]       (16x16x32 bf16 MFMA, two 16-token blocks)
 //   O^T[d][row]  += V^T[d][tok] . P^T[tok][row] (one MFMA per 16 head-dim rows)
-// with fp32 accumulation. Q and P are fp32 values; each is split into bf16 hi + lo and
-// multiplied twice, so products carry ~16 significant bits more than one bf16 pass
-// (K and V are exact bf16 already). The softmax is online (running max m, sum l) in the
+// with fp32 accumulation. Q and P are fp32 values; each is split into bf16 terms and
+// multiplied once per term (K and V are exact bf16 already): three terms for fp32 queries
+// carry every bit of Q and P, two for bf16 queries about 16 significant bits. The softmax is online (running max m, sum l) in the
 // log2 domain; a row's statistics live in the same lane as its O^T column, so the
 // per-tile rescale needs no cross-lane traffic.
 //
@@ -101,7 +101,11 @@ template <int D, bool QBF16, bool PAGED, bool KROWS>
 __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) {
   constexpr int KS = D / 32;  // k-steps of the score contraction
   constexpr int VEC = D / 16; // head-dim elements one lane loads per V row; also O^T blocks
-  constexpr int W = kAttnWaves, NT = 64 * kAttnWaves;
+  constexpr int W = kAttnWaves, NTH = 64 * kAttnWaves;
+  // bf16 terms of Q and P per MFMA operand: three for fp32 queries (every fp32 bit, so the
+  // scores and the P.V products carry fp32 precision), two for bf16 queries (whose
+  // auxiliary query is fp32 only through the coupling; about 16 significant bits)
+  constexpr int NT = QBF16 ? 2 : 3;
   __shared__ float s_o[W][16][D];
   __shared__ float s_m[W][16], s_l[W][16];
   __shared__ int32_t s_tbl[kMaxChunkBlocks];
@@ -117,7 +121,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) 
   const int G = p.group, R = p.n_flows * G;
 
   // ---- query tile: lane holds query row n, head-dim chunks 4s + j; Q2 coupled here.
-  u32x4 qh[KS], ql[KS];
+  u32x4 q3[NT][KS];
   {
     const bool valid = n < R;
     const int f = valid ? n / G : 0;
@@ -142,11 +146,11 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) 
       }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        uint32_t h0, l0, h1, l1;
-        split_bf16(valid ? q[2 * w] : 0.f, h0, l0);
-        split_bf16(valid ? q[2 * w + 1] : 0.f, h1, l1);
-        qh[s][w] = h0 | (h1 << 16);
-        ql[s][w] = l0 | (l1 << 16);
+        uint32_t t0[NT], t1[NT];
+        split_terms<NT>(valid ? q[2 * w] : 0.f, t0);
+        split_terms<NT>(valid ? q[2 * w + 1] : 0.f, t1);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) q3[t][s][w] = t0[t] | (t1[t] << 16);
       }
     }
   }
@@ -162,7 +166,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) 
   const int first_blk = PAGED ? (start >> p.block_shift) : 0;
   if constexpr (PAGED) {
     const int nblk = end > start ? ((end - 1) >> p.block_shift) - first_blk + 1 : 0;
-    for (int i = threadIdx.x; i < nblk; i += NT) {
+    for (int i = threadIdx.x; i < nblk; i += NTH) {
       const uint32_t e = (uint32_t)p.table[(int64_t)b * p.max_blocks + first_blk + i];
       s_tbl[i] = (uint64_t)e < (uint64_t)p.num_blocks ? (int32_t)e : (int32_t)(p.num_blocks - 1);
     }
@@ -188,9 +192,9 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) 
       for (; t0 + 32 * W < end; t0 += 32 * W) {
         half_bases<PAGED>(p, s_tbl, first_blk, b, g, t0 + 32 * W, end, hb, lx);
         read_k_frags<D>(s_k[wave], n, j, tr);
-        tile_scores<D>(tr, qh, ql, sacc);
+        tile_scores<D, NT>(tr, q3, sacc);
         load_k_rows<D>(kp, hb, lx, lane, kr);
-        tile_softmax_pv<D>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
+        tile_softmax_pv<D, NT>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
         load_v<D>(vp, hb, lx, n, j, tr);
         store_k_rows<D>(s_k[wave], lane, kr);  // after this wave's reads of the current rows
       }
@@ -200,14 +204,14 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) 
       load_v<D>(vp, hb, lx, n, j, tr);
       for (; t0 + 32 * W < end; t0 += 32 * W) {
         half_bases<PAGED>(p, s_tbl, first_blk, b, g, t0 + 32 * W, end, hb, lx);
-        tile_scores<D>(tr, qh, ql, sacc);
+        tile_scores<D, NT>(tr, q3, sacc);
         load_k<D>(kp, hb, lx, n, j, tr);
-        tile_softmax_pv<D>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
+        tile_softmax_pv<D, NT>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
         load_v<D>(vp, hb, lx, n, j, tr);
       }
     }
-    tile_scores<D>(tr, qh, ql, sacc);
-    tile_softmax_pv<D>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
+    tile_scores<D, NT>(tr, q3, sacc);
+    tile_softmax_pv<D, NT>(p, tr, sacc, t0, end, j, m_run, l_run, oacc);
   }
 
   // ---- combine the W waves (fixed order), then store output or split partial
@@ -222,7 +226,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_o[wave][n][VEC * (4 * j + i) + mb] = oacc[mb][i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < R * D; idx += NT) {
+  for (int idx = threadIdx.x; idx < R * D; idx += NTH) {
     const int r = idx / D, d = idx % D;
     float M = s_m[0][r];
 #pragma unroll

@@ -102,25 +102,24 @@ __device__ __forceinline__ void load_v(const uint16_t *vp, const int64_t *hb, co
   }
 }
 
-// Scores of one loaded tile (S^T blocks for its two 16-token halves).
-template <int D>
-__device__ __forceinline__ void tile_scores(const TileRegs<D> &r, const u32x4 *qh, const u32x4 *ql,
-                                            f32x4 *sacc) {
+// Scores of one loaded tile (S^T blocks for its two 16-token halves); the query rows are the
+// sum of NT bf16 terms q[0..NT-1] (split_terms), one MFMA pass per term.
+template <int D, int NT>
+__device__ __forceinline__ void tile_scores(const TileRegs<D> &r, const u32x4 (&q)[NT][D / 32], f32x4 *sacc) {
   constexpr int KS = D / 32;
   sacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      sacc[mb] = mfma16x16x32(as_bf16x8(r.kf[mb][s]), as_bf16x8(qh[s]), sacc[mb]);
-      sacc[mb] = mfma16x16x32(as_bf16x8(r.kf[mb][s]), as_bf16x8(ql[s]), sacc[mb]);
-    }
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sacc[mb] = mfma16x16x32(as_bf16x8(r.kf[mb][s]), as_bf16x8(q[t][s]), sacc[mb]);
 }
 
 // Online-softmax update for query row n (the lane holds 8 of the tile's 32 tokens) and
-// P.V accumulation into O^T.
-template <int D>
+// P.V accumulation into O^T, with P split into NT bf16 terms (one MFMA pass per term).
+template <int D, int NT>
 __device__ __forceinline__ void tile_softmax_pv(const AttnArgs &p, const TileRegs<D> &r,
                                                 const f32x4 *sacc, int t0, int end, int j,
                                                 float &m_run, float &l_run, f32x4 *oacc) {
@@ -141,21 +140,20 @@ __device__ __forceinline__ void tile_softmax_pv(const AttnArgs &p, const TileReg
   const float m_new = fmaxf(m_run, mx);
   const float alpha = exp2f(m_run - m_new);
   float psum = 0.f;
-  uint32_t phi[8], plo[8];
+  uint32_t pt[8][NT];
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
     const float pv = exp2f(sv[v] - m_new);
     psum += pv;
-    split_bf16(pv, phi[v], plo[v]);
+    split_terms<NT>(pv, pt[v]);
   }
   l_run = l_run * alpha + psum;
   m_run = m_new;
-  u32x4 pH, pL;
+  u32x4 pk[NT];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    pH[w] = phi[2 * w] | (phi[2 * w + 1] << 16);
-    pL[w] = plo[2 * w] | (plo[2 * w + 1] << 16);
-  }
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pk[t][w] = pt[2 * w][t] | (pt[2 * w + 1][t] << 16);
 #pragma unroll
   for (int mb = 0; mb < VEC; ++mb) {
     oacc[mb] *= alpha;
@@ -166,8 +164,8 @@ __device__ __forceinline__ void tile_softmax_pv(const AttnArgs &p, const TileReg
       const uint32_t x0 = r.vr[2 * w][mb >> 1], x1 = r.vr[2 * w + 1][mb >> 1];
       af[w] = (mb & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
     }
-    oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pH), oacc[mb]);
-    oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pL), oacc[mb]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pk[t]), oacc[mb]);
   }
 }
 

@@ -32,13 +32,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-// Splits x into hi + lo, both bf16, with |x - hi - lo| <= 2^-16 |x| (hi is x truncated to
-// bf16, lo is the remainder rounded to nearest even). Two bf16 MFMA passes with hi and lo
-// give products accurate to about fp32's level where a single bf16 pass would lose 8 bits.
-__device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) {
-  uint32_t h = __float_as_uint(x) & 0xffff0000u;
-  hi = h >> 16;
-  lo = f32_to_bf16_rne(x - __uint_as_float(h));
+// Splits x into NT bf16 terms t[0] + t[1] + ... : every term but the last is the remainder
+// so far truncated to bf16, the last is the remainder rounded to nearest even. Each
+// truncation keeps the next 8 significant bits, so the terms carry 8 NT bits of x: NT = 2
+// leaves |error| <= 2^-16 |x|, and NT = 3 holds every bit of an fp32 x exactly (the
+// last remainder has at most 8 significant bits), so NT bf16 MFMA passes multiply an fp32
+// value at fp32 precision.
+template <int NT>
+__device__ __forceinline__ void split_terms(float x, uint32_t *t) {
+  float r = x;
+#pragma unroll
+  for (int i = 0; i < NT - 1; ++i) {
+    const uint32_t h = __float_as_uint(r) & 0xffff0000u;
+    t[i] = h >> 16;
+    r -= __uint_as_float(h);
+  }
+  t[NT - 1] = f32_to_bf16_rne(r);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -199,7 +208,9 @@ struct LayerGlueArgs {
   float eps;
   const float *couple; // c coupling vector of the down projection, or NULL
   dfx_kv_cache kv;     // cache written by the Q/K/V finish (primary rows only)
-  const int32_t *ctx;  // context lengths after the step (append position = ctx - 1)
+  const int32_t *ctx;  // context lengths after the step, clamped to [1, max_context] as the
+                       // attention clamps them (append position = clamped length - 1)
+  int32_t max_context;
   int32_t num_q_heads, head_dim;
 };
 

@@ -59,11 +59,16 @@ hipError_t launch_prefill_append(const PrefillGlueArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Per-flow state of a wave's 16 query rows: the queries split into bf16 hi + lo, O^T
+// bf16 terms of the queries and of P in the causal attention: three, every bit of the fp32
+// values (the attention rows are rounded to bf16 before W_o; with fp32-exact operands the
+// rounding decisions are those of an fp32 evaluation).
+constexpr int kPrefillTerms = 3;
+
+// Per-flow state of a wave's 16 query rows: the queries split into bf16 terms, O^T
 // accumulators and the online-softmax statistics of the lane's row.
 template <int D>
 struct FlowAcc {
-  u32x4 qh[D / 32], ql[D / 32];
+  u32x4 q[kPrefillTerms][D / 32];
   f32x4 oacc[D / 16];
   float m_run, l_run;
 };
@@ -90,11 +95,11 @@ __device__ __forceinline__ void prefill_query(const AttnArgs &p, int f, int b, i
     }
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t h0, l0, h1, l1;
-      split_bf16(valid ? q[2 * w] : 0.f, h0, l0);
-      split_bf16(valid ? q[2 * w + 1] : 0.f, h1, l1);
-      fa.qh[s][w] = h0 | (h1 << 16);
-      fa.ql[s][w] = l0 | (l1 << 16);
+      uint32_t t0[kPrefillTerms], t1[kPrefillTerms];
+      split_terms<kPrefillTerms>(valid ? q[2 * w] : 0.f, t0);
+      split_terms<kPrefillTerms>(valid ? q[2 * w + 1] : 0.f, t1);
+#pragma unroll
+      for (int t = 0; t < kPrefillTerms; ++t) fa.q[t][s][w] = t0[t] | (t1[t] << 16);
     }
   }
 #pragma unroll
@@ -187,13 +192,13 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(AttnArgs p) {
     load_v<D>(vp, hb, lx, n, j, tr);
     for (; t + 32 < ce; t += 32) {
       half_bases<PAGED>(p, s_tbl, first_blk, b, g, t + 32, ce, hb, lx);
-      tile_scores<D>(tr, fa.qh, fa.ql, sacc);
+      tile_scores<D, kPrefillTerms>(tr, fa.q, sacc);
       load_k<D>(kp, hb, lx, n, j, tr);
-      tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
+      tile_softmax_pv<D, kPrefillTerms>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
       load_v<D>(vp, hb, lx, n, j, tr);
     }
-    tile_scores<D>(tr, fa.qh, fa.ql, sacc);
-    tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
+    tile_scores<D, kPrefillTerms>(tr, fa.q, sacc);
+    tile_softmax_pv<D, kPrefillTerms>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
   }
 
   prefill_store<D>(p, f, b, t0, n, j, rows, h, fa);
@@ -276,8 +281,8 @@ __global__ void __launch_bounds__(256) prefill_attn_shared_kernel(AttnArgs p) {
         tr.vr[v][0] = y[0]; tr.vr[v][1] = y[1]; tr.vr[v][2] = y[2]; tr.vr[v][3] = y[3];
       }
       f32x4 sacc[2];
-      tile_scores<D>(tr, fa.qh, fa.ql, sacc);
-      tile_softmax_pv<D>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
+      tile_scores<D, kPrefillTerms>(tr, fa.q, sacc);
+      tile_softmax_pv<D, kPrefillTerms>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_img[slot ^ 1][4 * wave + i][lane] = st[i];
       __syncthreads();

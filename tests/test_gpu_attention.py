@@ -35,7 +35,7 @@ def check(case, got, want, rows=None):
     e2 = max_err(o2, w2, rows) if w2 is not None else 0.0
     el = lse_err(lse[:, rows] if rows is not None else lse, wl[:, rows] if rows is not None else wl)
     assert e1 < tol and e2 < tol, (e1, e2)
-    assert el < max(tol, 1e-4), el
+    assert el < tol, el
     return e1, e2
 
 
@@ -246,8 +246,12 @@ def test_peaked_softmax_and_far_apart_split_maxima(gain, splits):
 
 
 def test_ragged_paged_full_size_sampled():
+    """The ragged 64-sequence workload: the shortest and the longest sequence and ten more
+    seeded ones against the oracle."""
     case = gen.config_attention(3)
-    rows = [0, 17, 63]
+    n = case.context_lens
+    rows = sorted({int(np.argmin(n)), int(np.argmax(n))} | set(int(r) for r in np.random.default_rng(3).choice(64, 10, replace=False)))
+    print("ragged workload: sequences", rows, "contexts", [int(n[r]) for r in rows], flush=True)
     got = run_attn(case)
     want = oracle(case, batches=rows)
     check(case, got, want, rows=rows)
@@ -275,8 +279,8 @@ def test_long_context_reduced_twin():
     check(case, run_attn(case), oracle(case))
 
 
-def test_long_context_full_size_sampled():
+def test_long_context_full_size_all_sequences():
+    """The 131072-token workload, every sequence of the batch against the oracle."""
     case = gen.config_attention(4)
-    rows = [0, 7]
     got = run_attn(case)
-    check(case, got, oracle(case, batches=rows), rows=rows)
+    check(case, got, oracle(case))

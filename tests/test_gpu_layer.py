@@ -10,6 +10,7 @@ from oracle.attention import decode_attention, gather_kv
 from oracle.layer import dual_flow_layer
 from oracle.linear import grouped_linear, rmsnorm, swiglu_couple
 from oracle.numerics import widen
+from twins import assert_twin_close, twin_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -40,18 +41,23 @@ def run_oracle(c, flows=2, x=None, couple=True, batches=None, dtype=np.float64):
                            dtype=dtype)
 
 
-def layer_close(y, want):
-    """End-to-end sanity against the fp64 oracle. The five bf16 rounding points make this
-    comparison discontinuous (an intermediate next to a rounding midpoint may land on either
-    neighbour, moving its row's downstream outputs by ulp * |w|), so it only bounds gross
-    deviations; the per-stage chain check below carries the precise claim."""
-    err = np.abs(np.asarray(y, np.float64) - np.asarray(want, np.float64))
-    print("layer error vs fp64 oracle: max %.3g mean %.3g p50 %.3g" % (err.max(), err.mean(), np.median(err)))
-    assert np.median(err) < 2e-3 and err.max() < 5e-2
+def layer_close(c, y, flows=2, couple=True, rows=None, x=None, want=None):
+    """End-to-end parity against the fp64 oracle on ``rows`` (all by default): within
+    K_TWIN times the distance of an ensemble of fp32 evaluations of the oracle's definition
+    (tests/twins.py). Returns the fp64 result."""
+    sel = slice(None) if rows is None else list(rows)
+    if want is None:
+        want = run_oracle(c, flows, x=x, couple=couple, batches=rows)[0]
+    exact = want[:, sel]
+    errs = twin_errors(lambda d, ph: run_oracle(d, flows, x=None if x is None else x[..., ph], couple=couple,
+                                                batches=rows, dtype=np.float32)[0][:, sel], c, exact)
+    assert_twin_close(np.asarray(y)[:, sel], exact, errs)
+    return want
 
 
 U = 2.0 ** -24                 # fp32 unit roundoff
-SPLIT = 2.0 ** -16             # relative error of a value split into two bf16 terms
+SPLIT = 0.0                    # the layer's attention splits its fp32 Q and P into three bf16
+                               # terms, which hold every fp32 bit: no split error
 
 
 def gamma(k):
@@ -178,7 +184,7 @@ def test_small_layer_parity_and_cache_diff():
     c = gen.layer_case(801, **SMALL)
     y, kp, vp = check_layer_chain(c)
     want, wk, wv, mid = run_oracle(c)
-    layer_close(y, want)
+    layer_close(c, y, want=want)
     # the pool changed exactly at the primary's new slots
     changed = np.argwhere(np.any(kp != c.cache.k_pool, axis=-1))
     assert len(changed) == c.batch * c.num_kv_heads
@@ -192,7 +198,7 @@ def test_layer_two_row_groups(seed):
     c = gen.layer_case(seed, batch=40, context=200, hidden=256, num_q_heads=4, num_kv_heads=2,
                        head_dim=64, intermediate=512, w_std=0.05)
     y, _, _ = check_layer_chain(c)
-    layer_close(y, run_oracle(c)[0])
+    layer_close(c, y)
     y1, _, _ = check_layer_chain(c, flows=1)
     assert np.array_equal(y1[0], y[0])
 
@@ -204,7 +210,7 @@ def test_layer_vector_attention_path(heads, block):
     c = gen.layer_case(807, batch=3, context=100, hidden=256, num_q_heads=heads[0], num_kv_heads=heads[1],
                        head_dim=64, intermediate=256, block_size=block, w_std=0.05)
     y, _, _ = check_layer_chain(c)
-    layer_close(y, run_oracle(c)[0])
+    layer_close(c, y)
 
 
 def test_layer_primary_only_chain():
@@ -231,12 +237,14 @@ def test_aux_equals_primary_without_coupling():
     assert np.array_equal(y[0], y[1])
 
 
-def test_full_size_layer_sampled():
+def test_full_size_layer_all_rows():
+    """The one-layer workload at full size (batch 32 x context 8192, hidden 4096, SwiGLU 14336):
+    every stage of all 32 sequences of both flows against the oracle, and the end-to-end rows
+    against the fp32 ensemble."""
     c = gen.config_layer()
-    rows = [0, 31]
-    y, kp, _ = check_layer_chain(c, rows=rows)
-    want = run_oracle(c, batches=rows)[0]
-    layer_close(y[:, rows], want[:, rows])
+    print("full-size layer: chain check over all 32 sequences", flush=True)
+    y, kp, _ = check_layer_chain(c)
+    layer_close(c, y)
     assert np.all(np.isfinite(y))
     changed = np.argwhere(np.any(kp != c.cache.k_pool, axis=-1))
     assert len(changed) == c.batch * c.num_kv_heads
@@ -248,5 +256,29 @@ def test_layer_single_sequence(flows):
     c = gen.layer_case(806, batch=1, context=1, hidden=256, num_q_heads=8, num_kv_heads=2, head_dim=128,
                        intermediate=512, w_std=0.05)
     y, kp, _ = check_layer_chain(c, flows=flows)
-    layer_close(y, run_oracle(c, flows=flows)[0])
+    layer_close(c, y, flows=flows)
     assert np.sum(np.any(kp != c.cache.k_pool, axis=-1)) == c.num_kv_heads
+
+
+def test_layer_clamps_context_lengths_like_the_attention():
+    """Context lengths above max_context attend max_context positions and append the new row at
+    position max_context - 1 (the same clamping as the attention's, so the appended row is one
+    the step attends); a negative length acts as 0: nothing attended, the row appended at
+    position 0."""
+    c = gen.layer_case(808, **SMALL)
+    maxc = int(c.cache.context_lens.max()) + 1
+    w = weights_of(c)
+
+    def run(ctx):
+        cache = cache_of(c.cache)
+        x = dev(c.x.copy())
+        dfx.dual_flow_decode_layer(x, w, cache, dev(np.asarray(ctx, np.int32)), maxc)
+        torch.cuda.synchronize()
+        return x.cpu().numpy(), host_bits(cache.k), host_bits(cache.v)
+
+    base = c.cache.context_lens + 1
+    wild, tame = base.copy(), base.copy()
+    wild[0], tame[0] = maxc + 7, maxc
+    wild[1], tame[1] = -3, 0
+    for got, want in zip(run(wild), run(tame)):
+        assert np.array_equal(got, want)

@@ -3,11 +3,13 @@ of the auxiliary flow's start at the last prompt position, and of the causal att
 both flows at every position (dfx_prefill_dual_attn, the training-time forward).
 
 Tolerances: the causal attention outputs against the oracle at max-abs 2e-3 (bf16 cache) and,
-tighter, 5e-5 (Q and P are split into two bf16 terms, so the kernel carries about 16 more bits
-than one bf16 pass); the layer and step outputs as the decode layer's (median 2e-3, max 5e-2
-after five bf16 rounding points), the appended keys and values equal bit for bit but for rare
-rounding decisions one bf16 step apart (fp32 against fp64 projections); chunked prefill
+tighter, 5e-5 (Q and P are split into three bf16 terms, every fp32 bit); the layer and step
+outputs within twice the distance of an ensemble of fp32 evaluations of the oracle
+(tests/twins.py), as the decode layer's; the appended keys and values equal bit for bit but for
+rare rounding decisions one bf16 step apart (fp32 against fp64 projections); chunked prefill
 bit-identical to one chunk."""
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -20,13 +22,17 @@ from oracle.prefill import (prefill_attention, prefill_dual_attention, prefill_l
 from oracle.linear import rmsnorm
 from oracle.numerics import widen
 from oracle.step import dual_flow_step
+from twins import assert_twin_close, twin_errors
 
 pytestmark = pytest.mark.gpu
 
 
-def layer_close(y, want, median=2e-3):
-    err = np.abs(np.asarray(y, np.float64) - want)
-    assert np.median(err) < median and err.max() < 5e-2, (np.median(err), err.max())
+def prefill_twins(c, x, st, want):
+    """fp32 ensemble distances of prefill_layer on the chunk x (tests/twins.py)."""
+    return twin_errors(lambda d, ph: prefill_layer(x[..., ph], d.g_attn, d.g_mlp, d.w_qkv, d.w_o, d.w_gate_up,
+                                                   d.w_down, d.eps, d.cache.k_pool, d.cache.v_pool, d.cache.block_table,
+                                                   st, d.num_q_heads, d.num_kv_heads, d.head_dim, dtype=np.float32)[0],
+                       c, want)
 
 
 @pytest.mark.parametrize("paged,D,Hq,Hkv,T,starts", [
@@ -138,7 +144,7 @@ def test_prefill_layer_parity_and_appended_rows():
     want, kp, vp, _ = prefill_layer(x, c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.eps,
                                     c.cache.k_pool, c.cache.v_pool, c.cache.block_table, st, c.num_q_heads,
                                     c.num_kv_heads, c.head_dim)
-    layer_close(xt.cpu().numpy(), want)
+    assert_twin_close(xt.cpu().numpy(), want, prefill_twins(c, x, st, want), "prefill layer")
     gk, gv = host_bits(cache.k), host_bits(cache.v)
     # the pool changed exactly at the chunk's slots, and agrees with the oracle's appended rows
     changed = np.any(gk != c.cache.k_pool, axis=(1, 3))
@@ -170,7 +176,7 @@ def test_prefill_layer_odd_k_steps():
     want, _, _, _ = prefill_layer(x, c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.eps,
                                   c.cache.k_pool, c.cache.v_pool, c.cache.block_table, st, c.num_q_heads,
                                   c.num_kv_heads, c.head_dim)
-    layer_close(xt.cpu().numpy(), want)
+    assert_twin_close(xt.cpu().numpy(), want, prefill_twins(c, x, st, want), "prefill layer")
 
 
 def kv_step_bound(x, c):
@@ -224,7 +230,10 @@ def test_prefill_layer_long_chunk_sampled_rows(B, T, shape):
     want, k, v = prefill_layer_rows(x, c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.eps,
                                     c.num_q_heads, c.num_kv_heads, c.head_dim, samples)
     got = xt.cpu().numpy()
-    layer_close(np.stack([got[b, t] for b, t in samples]), want, median=4e-3)
+    errs = twin_errors(lambda d, ph: prefill_layer_rows(x[..., ph], d.g_attn, d.g_mlp, d.w_qkv, d.w_o, d.w_gate_up,
+                                                        d.w_down, d.eps, d.num_q_heads, d.num_kv_heads, d.head_dim,
+                                                        samples, dtype=np.float32)[0], c, want)
+    assert_twin_close(np.stack([got[b, t] for b, t in samples]), want, errs, "prefill layer rows")
     bs, tbl, t = c.cache.k_pool.shape[2], c.cache.block_table, np.arange(T)
     bound = kv_step_bound(x, c)
     for i, (pool, ref) in enumerate(((host_bits(cache.k), k), (host_bits(cache.v), v))):
@@ -276,8 +285,23 @@ def test_prefill_then_aux_start_matches_oracle():
     torch.cuda.synchronize()
     # oracle: the same composition
     want_p, pools = prefill_step(tokens[:, : n - 1], e1, layers, np.zeros(B))
-    layer_close(xp.cpu().numpy(), want_p)
+    errs = twin_errors(lambda ds, ph: prefill_step(tokens[:, : n - 1], e1[:, ph], ds, np.zeros(B), dtype=np.float32)[0],
+                       None, want_p, layers=layers)
+    assert_twin_close(xp.cpu().numpy(), want_p, errs, "prefill step")
+
+    def twin_start(ds, ph):
+        # the fp32 evaluation's own prefill fills the caches its decode step reads
+        _, own = prefill_step(tokens[:, : n - 1], e1[:, ph], ds, np.zeros(B), dtype=np.float32)
+        for d, (kp, vp) in zip(ds, own):
+            d.cache.k_pool, d.cache.v_pool = kp, vp
+        return dual_flow_step(tokens[:, n - 1], e1[:, ph], e2[:, ph], ds, np.full(B, n - 1), dtype=np.float32)[0]
+
+    done = []
     for Lc, (kp, vp) in zip(layers, pools):
-        Lc.cache.k_pool, Lc.cache.v_pool = kp, vp
-    want, _ = dual_flow_step(tokens[:, n - 1], e1, e2, layers, np.full(B, n - 1))
-    layer_close(x_last.cpu().numpy(), want)
+        d = copy.copy(Lc)
+        d.cache = copy.copy(Lc.cache)
+        d.cache.k_pool, d.cache.v_pool = kp, vp
+        done.append(d)
+    want, _ = dual_flow_step(tokens[:, n - 1], e1, e2, done, np.full(B, n - 1))
+    assert_twin_close(x_last.cpu().numpy(), want, twin_errors(twin_start, None, want, layers=layers),
+                      "auxiliary start")

@@ -7,7 +7,8 @@ import dfx_inputs as gen
 import dual_flow_shared_amd as dfx
 from gpu_util import cache_of, dev, host_bits
 from oracle.step import dual_flow_step
-from test_gpu_layer import layer_close, weights_of
+from test_gpu_layer import weights_of
+from twins import assert_twin_close, twin_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -92,8 +93,11 @@ def test_step_primary_only_and_against_the_oracle():
     assert torch.equal(x1[0], x[0])
     for a, kv in zip(k_dual, caches1):
         assert np.array_equal(a, host_bits(kv.k))
-    want, pools = dual_flow_step(c.tokens, c.embed_primary, c.embed_aux, c.layers, c.layers[0].cache.context_lens)
-    layer_close(x.cpu().numpy(), want)
+    before = c.layers[0].cache.context_lens
+    want, pools = dual_flow_step(c.tokens, c.embed_primary, c.embed_aux, c.layers, before)
+    errs = twin_errors(lambda ds, ph: dual_flow_step(c.tokens, c.embed_primary[:, ph], c.embed_aux[:, ph], ds, before,
+                                                     dtype=np.float32)[0], None, want, layers=c.layers)
+    assert_twin_close(x.cpu().numpy(), want, errs, "decode step")
     for (wk, _), got, L in zip(pools, k_dual, c.layers):
         # each layer's pool changes exactly at the primary's new slots, the oracle's too
         changed = np.argwhere(np.any(got != L.cache.k_pool, axis=-1))
