@@ -15,7 +15,7 @@ import torch
 from ._abi import (DFX_BF16, DFX_F32, DFX_W_PACKED, DFX_W_ROW_MAJOR, DfxError, KVCacheStruct,
                    LayerTapsStruct, LayerWeightsStruct, MoeTapsStruct, MoeWeightsStruct, check, lib)
 
-__all__ = ["DfxError", "KVCache", "LayerWeights", "decode_attn", "decode_attn_plan",
+__all__ = ["DfxError", "KVCache", "LayerWeights", "decode_attn", "decode_attn_plan", "decode_attn_workspace_size",
            "kv_append_primary", "grouped_linear", "pack_weight", "rmsnorm", "swiglu_couple",
            "dual_flow_decode_layer", "layer_workspace_size", "copy_bytes", "read_bytes", "fill_bytes",
            "layer_taps", "dual_flow_decode_step", "step_workspace_size", "output_head",
@@ -125,6 +125,15 @@ def decode_attn_plan(cache: KVCache, batch: int, num_q_heads: int, n_flows: int,
     return s.value, n.value
 
 
+def decode_attn_workspace_size(cache: KVCache, batch: int, num_q_heads: int, n_flows: int, max_context: int,
+                               num_splits: int = 0) -> int:
+    n = ctypes.c_size_t()
+    st = cache.struct()
+    check(lib().dfx_decode_attn_workspace_size(batch, num_q_heads, n_flows, ctypes.byref(st), max_context,
+                                               num_splits, ctypes.byref(n)))
+    return n.value
+
+
 def decode_attn(q1: torch.Tensor, q2_raw: Optional[torch.Tensor] = None, a: Optional[torch.Tensor] = None,
                 *, cache: KVCache, context_lens: torch.Tensor, max_context: int, num_splits: int = 0,
                 softmax_scale: float = 0.0, want_lse: bool = True, out=None,
@@ -229,7 +238,7 @@ def swiglu_couple(gate_up: torch.Tensor, b: Optional[torch.Tensor] = None, out=N
     F, rows, two_i = gate_up.shape
     y = out if out is not None else torch.empty(F, rows, two_i // 2, dtype=torch.bfloat16,
                                                 device=gate_up.device)
-    check(lib().dfx_swiglu_couple(F, rows, two_i // 2, _ptr(gate_up), _ptr(b), _ptr(y), _stream(stream)))
+    check(lib().dfx_swiglu_couple(rows, F, two_i // 2, _ptr(gate_up), _ptr(b), _ptr(y), _stream(stream)))
     return y
 
 

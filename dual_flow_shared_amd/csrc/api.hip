@@ -340,6 +340,15 @@ dfx_status dfx_decode_attn_plan(const dfx_kv_cache *kv, int32_t batch, int32_t n
   DFX_END
 }
 
+dfx_status dfx_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t n_flows,
+                                          const dfx_kv_cache *kv, int32_t max_context, int32_t num_splits,
+                                          size_t *bytes) {
+  DFX_BEGIN
+  if (!bytes) return fail(DFX_EINVAL, "bytes is NULL");
+  return dfx_decode_attn_plan(kv, batch, num_q_heads, n_flows, max_context, num_splits, nullptr, bytes);
+  DFX_END
+}
+
 dfx_status dfx_decode_attn(const dfx_kv_cache *kv, const int32_t *context_lens, int32_t batch,
                            int32_t max_context, int32_t num_q_heads, int32_t q_dtype,
                            const void *q1, const void *q2_raw, int64_t q_batch_stride,
@@ -430,7 +439,7 @@ dfx_status dfx_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *g
   DFX_END
 }
 
-dfx_status dfx_swiglu_couple(int32_t n_flows, int32_t rows, int32_t dim, const float *gate_up,
+dfx_status dfx_swiglu_couple(int32_t rows, int32_t n_flows, int32_t dim, const float *gate_up,
                              const float *b, uint16_t *out, void *stream) {
   DFX_BEGIN
   if ((n_flows != 1 && n_flows != 2) || rows < 0 || dim < 4 || dim % 4)
@@ -540,7 +549,7 @@ dfx_status run_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv, const i
   dfx_status r;
   LayerGlueArgs g{};
   g.n_flows = F; g.batch = B; g.tiles = tiles; g.x = x; g.eps = w->rms_eps;
-  g.kv = *kv; g.ctx = context_lens; g.num_q_heads = Hq; g.head_dim = D;
+  g.kv = *kv; g.ctx = context_lens; g.max_context = max_context; g.num_q_heads = Hq; g.head_dim = D;
   auto ksplit = [&](int K, int N) { return gemm_plan(F, B, K, N).ksplit; };
   // attention block: norm, shared Q/K/V projection, primary-only append, dual attention
   if (norm_in && (r = hip_status(launch_rmsnorm(F * B, H, x, w->attn_norm_gain, w->rms_eps, h1, s, F), "rmsnorm launch")))

@@ -15,7 +15,7 @@ __device__ __forceinline__ f32x4 sum_tiles(const float *tiles, int ksplit, int g
 }
 
 // Q columns of both flows -> qkv rows (fp32); K and V columns of flow 0 -> the cache at
-// position context_lens[b] - 1 as bf16 (the auxiliary flow's K/V columns are dropped: only
+// position min(max(context_lens[b], 1), max_context) - 1 as bf16 (the auxiliary flow's K/V columns are dropped: only
 // the primary flow writes the cache). One thread per 4 columns of one (flow, row).
 __global__ void __launch_bounds__(256) qkv_finish_kernel(LayerGlueArgs a) {
   const int F = a.n_flows, B = a.batch, N = a.N;
@@ -40,9 +40,9 @@ __global__ void __launch_bounds__(256) qkv_finish_kernel(LayerGlueArgs a) {
   const int cc = is_v ? c - kvcols : c;
   const int g = cc / kv.head_dim, d = cc % kv.head_dim;
   const bool paged = kv.block_table != nullptr;
-  const int64_t cap = paged ? (int64_t)kv.max_blocks_per_seq * kv.block_size : kv.block_size;
-  int64_t pos = (int64_t)a.ctx[b] - 1;
-  pos = pos < 0 ? 0 : (pos >= cap ? cap - 1 : pos);
+  // the attention of this step reads positions [0, min(max(ctx, 0), max_context)); the new
+  // row goes to the last of them (max_context <= capacity, checked on the host)
+  const int64_t pos = (int64_t)min(max(a.ctx[b], 1), a.max_context) - 1;
   int64_t blk, slot;
   if (paged) {
     const uint32_t e = (uint32_t)kv.block_table[(int64_t)b * kv.max_blocks_per_seq + pos / kv.block_size];

@@ -92,12 +92,33 @@ int dfx_version(void);
  * valid until the next dfx_* call on the same thread. */
 const char *dfx_last_error(void);
 
-/* Number of context splits dfx_decode_attn will use for these arguments
- * (num_splits = 0 asks for the automatic plan) and the workspace it needs in
- * bytes (0 when the plan has a single split). Pure host arithmetic. */
+/*
+ * Split plan of dfx_decode_attn. Attention over one sequence's context is cut into
+ * context splits whose partial softmax states are merged by a log-sum-exp combine; the
+ * auxiliary flow reads the same cache positions as the primary (Sintesi Tecnica:
+ * Dual-Flow Transformers, section "Meccanismi Chiave"), so both flows share every split.
+ * Reports the number of context splits dfx_decode_attn will use for these arguments
+ * (num_splits = 0 asks for the automatic plan) and the workspace it needs in bytes (0
+ * when the plan has a single split). Pure host arithmetic; splits_out and
+ * workspace_bytes may each be NULL. Errors: DFX_EINVAL for an invalid cache descriptor,
+ * batch < 0, num_q_heads < 1, n_flows not 1 or 2, max_context outside [0, capacity] or
+ * num_splits < 0.
+ */
 dfx_status dfx_decode_attn_plan(const dfx_kv_cache *kv, int32_t batch, int32_t num_q_heads,
                                 int32_t n_flows, int32_t max_context, int32_t num_splits,
                                 int32_t *splits_out, size_t *workspace_bytes);
+
+/*
+ * Workspace bytes dfx_decode_attn needs for these arguments: the fp32 partial outputs
+ * and log-sum-exp values of every context split ([splits][n_flows][batch][num_q_heads]
+ * x (head_dim + 1) floats, 256-byte aligned regions), 0 when the plan has one split.
+ * The same plan as dfx_decode_attn_plan (same page and section). *bytes receives the
+ * size; bytes == NULL is DFX_EINVAL, and so is every argument dfx_decode_attn_plan
+ * rejects. Pure host arithmetic.
+ */
+dfx_status dfx_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t n_flows,
+                                          const dfx_kv_cache *kv, int32_t max_context,
+                                          int32_t num_splits, size_t *bytes);
 
 /*
  * Dual-query decode attention over the primary cache (same page, section
@@ -218,13 +239,13 @@ dfx_status dfx_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *g
  * SwiGLU activation with the MLP-intermediate coupling b (same page, section
  * "Meccanismi Chiave": one-way primary -> auxiliary vectors at the
  * MLP-intermediate level; the formula is this library's reading):
- *   inter[f][r][i] = silu(gu[f][r][i]) * gu[f][r][dim + i]
+ *   inter[f][r][i] = silu(gu[f][r][i]) * gu[f][r][dim + i]     (r < rows, rows per flow)
  *   if b && n_flows == 2:  inter[1][r][i] += b[i] * inter[0][r][i]
  *   out = bf16(inter)
  *  gate_up device fp32 [n_flows][rows][2*dim] ([gate | up] per row),
  *  b device fp32 [dim] or NULL, out device bf16 [n_flows][rows][dim]; dim % 4 == 0.
  */
-dfx_status dfx_swiglu_couple(int32_t n_flows, int32_t rows, int32_t dim, const float *gate_up,
+dfx_status dfx_swiglu_couple(int32_t rows, int32_t n_flows, int32_t dim, const float *gate_up,
                              const float *b, uint16_t *out, void *stream);
 
 /*

@@ -21,7 +21,7 @@ def declared():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = _abi.lib()
     names = declared()
-    assert len(names) == 30
+    assert len(names) == 31
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, n
@@ -83,6 +83,36 @@ def test_grid_extent_limits():
     kc = kv(dtype=0, table=None, bs=1 << 22, nb=1, heads=1, D=64)
     st, msg = attn(kc, batch=1, maxc=1 << 22, hq=1, q2=None, o2=None, a=None, splits=65536, qdt=0)
     assert st == 2 and "splits" in msg, msg
+
+
+def test_attention_workspace_size():
+    """dfx_decode_attn_workspace_size: the plan's partials (every split's fp32 outputs and
+    log-sum-exp values), and the plan's error paths."""
+    lib = _abi.lib()
+    s, n, w = ctypes.c_int32(), ctypes.c_size_t(), ctypes.c_size_t()
+    k = kv(mb=8192, nb=65536)
+    for batch, hq, flows, maxc, req in ((8, 64, 2, 131072, 0), (8, 64, 1, 131072, 3), (32, 32, 2, 16384, 0),
+                                        (2, 32, 2, 100, 1), (0, 32, 2, 0, 0)):
+        assert lib.dfx_decode_attn_workspace_size(batch, hq, flows, ctypes.byref(k), maxc, req, ctypes.byref(w)) == 0
+        assert lib.dfx_decode_attn_plan(ctypes.byref(k), batch, hq, flows, maxc, req, ctypes.byref(s),
+                                        ctypes.byref(n)) == 0
+        assert w.value == n.value
+        rows = s.value * flows * batch * hq
+        if s.value == 1:
+            assert w.value == 0
+        else:
+            up = lambda x: -(-x // 256) * 256
+            assert w.value == up(rows * 128 * 4) + up(rows * 4)
+    for args, needle in (((8, 64, 2, ctypes.byref(k), 131072, 0, None), "bytes"),
+                         ((8, 64, 3, ctypes.byref(k), 131072, 0, ctypes.byref(w)), ""),
+                         ((8, 64, 2, ctypes.byref(k), 8192 * 16 + 1, 0, ctypes.byref(w)), "capacity"),
+                         ((8, 64, 2, ctypes.byref(k), 1024, -2, ctypes.byref(w)), ""),
+                         ((-1, 64, 2, ctypes.byref(k), 1024, 0, ctypes.byref(w)), ""),
+                         ((8, 64, 2, None, 1024, 0, ctypes.byref(w)), "kv")):
+        assert lib.dfx_decode_attn_workspace_size(*args) == 1
+        assert needle in lib.dfx_last_error().decode()
+    bad = kv(D=96, mb=64)
+    assert lib.dfx_decode_attn_workspace_size(2, 32, 2, ctypes.byref(bad), 100, 0, ctypes.byref(w)) == 2
 
 
 def test_plan_is_host_arithmetic():
@@ -151,7 +181,9 @@ def test_linear_and_glue_reject():
     assert lib.dfx_pack_weight(32, 64, FAKE, FAKE + 1024, None) == 1      # overlapping buffers
     assert lib.dfx_rmsnorm(4, 30, FAKE, FAKE, 1e-5, FAKE, None) == 1
     assert lib.dfx_rmsnorm(4, 64, None, FAKE, 1e-5, FAKE, None) == 1
-    assert lib.dfx_swiglu_couple(3, 4, 64, FAKE, None, FAKE, None) == 1
+    assert lib.dfx_swiglu_couple(4, 3, 64, FAKE, None, FAKE, None) == 1       # n_flows 3
+    assert lib.dfx_swiglu_couple(-1, 2, 64, FAKE, None, FAKE, None) == 1      # rows per flow < 0
+    assert lib.dfx_swiglu_couple(4, 2, 62, FAKE, None, FAKE, None) == 1       # dim % 4
     assert lib.dfx_copy_bytes(FAKE, FAKE, 17, None) == 1
     assert lib.dfx_fill_bytes(FAKE + 4, 32, 0, None) == 1
     assert lib.dfx_read_bytes(FAKE, 32, None, None) == 1
