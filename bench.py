@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--splits", type=int, default=0, help="attention context splits (0 = plan)")
     p.add_argument("--kernel-reps", type=int, default=20)
+    p.add_argument("--no-attention-workloads", action="store_true",
+                   help="skip timing the four attention-only workloads in the layer line")
     p.add_argument("--no-split-sweep", action="store_true",
                    help="skip timing dual and single flow at each split count (own-best-split ratio)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -131,6 +133,98 @@ def best_split_ratio(dfx, kv, B, Hq, F, mc, q1, q2, a, caches, turn, ctx_t, aws,
         best[name] = {"splits": n_best, "ms": round(t[n_best], 4)}
     best["ratio"] = round(best["dual"]["ms"] / best["single"]["ms"], 3)
     return best
+
+
+# The four attention-only workloads (dual-query decode attention alone), with the shapes,
+# context lengths and cache layouts of the parity tests; the values are drawn on the GPU
+# (timing needs the shapes, not the seeded values).
+ATTN_WORKLOADS = {
+    1: dict(B=1, Hq=8, Hkv=8, D=64, ctx=("fixed", 512), kv="f32", paged=False, pool=None),
+    2: dict(B=16, Hq=32, Hkv=8, D=128, ctx=("fixed", 4096), kv="bf16", paged=False, pool=None),
+    3: dict(B=64, Hq=32, Hkv=8, D=128, ctx=("ragged", 303, 1024, 16384), kv="bf16", paged=True, pool=70000),
+    4: dict(B=8, Hq=64, Hkv=8, D=128, ctx=("fixed", 131072), kv="bf16", paged=True, pool=65536),
+}
+
+
+def attention_workloads(dfx, gen, stream, reps, which=(1, 2, 3, 4)):
+    """Dual-query attention of each attention workload at the planned split count: dual-flow
+    and primary-only time (HIP events on the launch stream, back-to-back calls rotating cache
+    replicas of >= 1 GB in total), algorithmic bytes, GB/s and the fraction of 8 TB/s."""
+    import numpy as np
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(4242)
+    out = []
+    for idx in which:
+        w = ATTN_WORKLOADS[idx]
+        B, Hq, Hkv, D = w["B"], w["Hq"], w["Hkv"], w["D"]
+        ctx_np = (np.full(B, w["ctx"][1], np.int32) if w["ctx"][0] == "fixed"
+                  else gen.ragged_lengths(w["ctx"][1], B, w["ctx"][2], w["ctx"][3]))
+        el = 4 if w["kv"] == "f32" else 2
+        kdt = torch.float32 if el == 4 else torch.bfloat16
+        if w["paged"]:
+            bs = 16
+            nblk = w["pool"]
+            mb = -(-int(ctx_np.max()) // bs)
+            perm = torch.randperm(nblk, generator=g, device="cuda").to(torch.int32)
+            need = -(-ctx_np // bs)
+            table = torch.zeros(B, mb, dtype=torch.int32, device="cuda")
+            off = 0
+            for b in range(B):
+                table[b, : need[b]] = perm[off: off + need[b]]
+                off += int(need[b])
+            shape = (nblk, Hkv, bs, D)
+        else:
+            bs, table = int(ctx_np.max()), None
+            shape = (B, Hkv, bs, D)
+        pool_bytes = 2 * int(np.prod(shape)) * el
+        n_rep = -(-REPLICA_BYTES // pool_bytes) if pool_bytes < REPLICA_BYTES else 1
+        caches = [dfx.KVCache(torch.randn(*shape, generator=g, device="cuda", dtype=kdt),
+                              torch.randn(*shape, generator=g, device="cuda", dtype=kdt), table)
+                  for _ in range(n_rep)]
+        qdt = kdt
+        q1 = torch.randn(B, Hq, D, generator=g, device="cuda", dtype=qdt)
+        q2 = torch.randn(B, Hq, D, generator=g, device="cuda", dtype=qdt)
+        a = torch.rand(D, generator=g, device="cuda") * 2 - 1
+        ctx_t = torch.from_numpy(ctx_np).cuda()
+        mc = int(ctx_np.max())
+        aws = dfx.Workspace()
+        turn = itertools.cycle(range(n_rep))
+
+        def call(qq, aa):
+            dfx.decode_attn(q1, qq, aa, cache=caches[next(turn)], context_lens=ctx_t, max_context=mc,
+                            want_lse=False, workspace=aws)
+
+        # one pass over the replicas with each flow count first (first touch of every replica),
+        # then dual and single flow timed twice each, interleaved; the mean of the two
+        for _ in range(min(n_rep, 64)):
+            call(q2, a)
+            call(None, None)
+        t = {"dual": [], "single": []}
+        for _ in range(2):
+            t["dual"].append(timed(lambda: call(q2, a), reps, stream))
+            t["single"].append(timed(lambda: call(None, None), reps, stream))
+        dual, single = sum(t["dual"]) / 2, sum(t["single"]) / 2
+        case_like = dict(Hkv=Hkv, D=D, Hq=Hq, B=B, kv_el=el, bs=16, paged=w["paged"])
+        nbytes = attn_bytes(case_like, ctx_np, 2, el)
+        gbps = nbytes / (dual * 1e-3) / 1e9
+        splits, _ = dfx.decode_attn_plan(caches[0], B, Hq, 2, mc, 0)
+        rec = {"config": idx,
+               "workload": (f"batch {B}, {Hq}/{Hkv} heads x {D}, context "
+                            + (f"{mc}" if w["ctx"][0] == "fixed" else f"ragged {int(ctx_np.min())}-{mc}")
+                            + f", {'paged (16-token blocks)' if w['paged'] else 'contiguous'} {w['kv']} KV"),
+               "ms": round(dual, 4), "single_flow_ms": round(single, 4),
+               "dual_single_ratio": round(dual / single, 3), "splits": splits, "bytes": int(nbytes),
+               "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4), "kv_replicas": n_rep,
+               "steps_per_s": round(1000.0 / dual, 1)}
+        if idx == 1:
+            rec["target"] = "none: 2 MB per call, launch-latency bound"
+        else:
+            rec["target_0.70"] = "met" if gbps / HBM_PEAK_GBPS >= 0.70 else "missed"
+        out.append(rec)
+        del caches, q1, q2
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 def timed_each(fn, reps, stream, flush=None):
@@ -312,6 +406,20 @@ def main():
     ms = start.elapsed_time(end) / args.steps
     steps_per_s = 1000.0 / ms
 
+    if args.workload == "layer":
+        # the same step with the primary flow alone (the auxiliary flow's cost), and each step
+        # timed alone with 512 MB written between steps (outside the event pairs)
+        x1 = x0[:1].clone()
+        single_step_ms = timed(lambda: dfx.dual_flow_decode_layer(x1, w, kv, ctx, max_ctx, workspace=ws),
+                               args.steps, stream)
+        each_step = np.array(timed_each(step, args.steps, stream, flush=hbm_flush(dfx)))
+        extra.update({"layer_single_flow_ms": round(single_step_ms, 4),
+                      "layer_dual_single_ratio": round(ms / single_step_ms, 3),
+                      "ms_per_step_flushed": {"median": round(float(np.median(each_step)), 4),
+                                              "p10": round(float(np.percentile(each_step, 10)), 4),
+                                              "p90": round(float(np.percentile(each_step, 90)), 4),
+                                              "steps": int(each_step.size), "flush_bytes_between": 512 << 20}})
+
     # ---- dominant kernel: dual-query attention, events on its stream
     ctx_t, mc = attn_ctx
 
@@ -338,6 +446,8 @@ def main():
                   "step_bytes": int(step_bytes), "wall_s": round(wall, 3)})
 
     extra["stream_read"] = stream_read(dfx, stream)
+    if args.workload == "layer" and not args.no_attention_workloads:
+        extra["attention_workloads"] = attention_workloads(dfx, gen, stream, args.kernel_reps)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic_from_profiles("attn_mfma.hip", args.workload),
@@ -689,43 +799,88 @@ def bench_prefill(args):
     print(json.dumps(line))
 
 
+def host_cores():
+    """Host cores this process may run on (the machine's CPU share, not the machine's count)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def parallel_oracle(fn, parts, workers):
+    """Runs fn(part) for every part on `workers` threads, each with one BLAS thread (numpy
+    releases the GIL in its array kernels); returns the wall seconds of the whole set."""
+    from concurrent.futures import ThreadPoolExecutor
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    t0 = time.perf_counter()
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            with ThreadPoolExecutor(workers) as ex:
+                list(ex.map(fn, parts))
+    else:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fn, parts))
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(workload, env):
-    """Time the oracle (fp64 numpy, as it stands) on a bounded sample of the workload and
-    scale to steps/s of the full workload."""
+    """Time the oracle as it stands on a bounded sample of the workload and scale to steps/s
+    of the full workload. The layer and attention workloads time the oracle's fp32 evaluation
+    (the same definition in single precision), spread over the host's cores by sequence; the
+    layer also reports the fp64 oracle on the BLAS threads alone."""
     import numpy as np
     from oracle.attention import decode_attention
     from oracle.layer import dual_flow_layer
+    cores = host_cores()
     if workload == "layer":
         c = env["c"]
         kv = c.cache
+        B = c.batch
+        chunks = [list(range(i, B, cores)) for i in range(min(cores, B))]
+
+        def rows(idx, dtype):
+            return dual_flow_layer(c.x[:, idx], c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.a,
+                                   c.b, c.c, c.eps, kv.k_pool, kv.v_pool, kv.block_table[idx], kv.context_lens[idx],
+                                   c.num_q_heads, c.num_kv_heads, c.head_dim, dtype=dtype)
+
         times = []
-        while len(times) < 12 and sum(times) < 12.0:
-            t0 = time.perf_counter()
-            dual_flow_layer(c.x, c.g_attn, c.g_mlp, c.w_qkv, c.w_o, c.w_gate_up, c.w_down, c.a, c.b,
-                            c.c, c.eps, kv.k_pool, kv.v_pool, kv.block_table, kv.context_lens,
-                            c.num_q_heads, c.num_kv_heads, c.head_dim)
-            times.append(time.perf_counter() - t0)
+        while len(times) < 12 and sum(times) < 10.0:
+            times.append(parallel_oracle(lambda idx: rows(idx, np.float32), chunks, len(chunks)))
         full = float(np.median(times))
-        sample = (f"the whole layer step (all {c.batch} sequences, both flows), median of "
-                  f"{len(times)} runs, {sum(times):.1f} s in total")
-    else:
-        case = env["case"]
-        # whole sequences, one at a time and cycling through the batch, until about 10 s of
-        # oracle work; scaled to the full batch by the share of context tokens done
-        ctx = case.context_lens.astype(np.int64)
-        t, tokens, calls = 0.0, 0, 0
-        while (t < 10.0 or calls == 0) and calls < 1_000_000:
-            b = calls % case.batch
+        sample = (f"the oracle's fp32 evaluation of the whole layer step (all {B} sequences, both flows), "
+                  f"the sequences spread over {len(chunks)} threads, median of {len(times)} runs, "
+                  f"{sum(times):.1f} s in total")
+        t64 = []
+        while len(t64) < 6 and sum(t64) < 8.0:
             t0 = time.perf_counter()
-            decode_attention(case.q1, case.q2, case.a, case.a_head_stride, case.k_pool, case.v_pool,
-                             case.block_table, case.context_lens, batches=[b])
-            t += time.perf_counter() - t0
-            tokens += int(ctx[b])
-            calls += 1
-        full = t * float(ctx.sum()) / max(tokens, 1)
-        sample = (f"oracle attention, one sequence per call, {calls} calls ({tokens / float(ctx.sum()):.2f} "
-                  f"passes over the batch, {t:.1f} s), scaled by the share of context tokens")
-    return {"value": round(1.0 / full, 4), "unit": "steps/s", "cores": cpu_threads(), "kind": "oracle",
+            rows(list(range(B)), np.float64)
+            t64.append(time.perf_counter() - t0)
+        return {"value": round(1.0 / full, 4), "unit": "steps/s", "cores": len(chunks), "kind": "oracle",
+                "sample": sample, "cpu_model": cpu_model(),
+                "fp64": {"value": round(1.0 / float(np.median(t64)), 4), "unit": "steps/s",
+                         "threads": cpu_threads(), "runs": len(t64),
+                         "sample": "the fp64 oracle, the whole layer step in one call on the BLAS threads"}}
+    case = env["case"]
+    # whole sequences, cycling through the batch, the calls spread over the host cores until
+    # about 10 s of oracle work; scaled to the full batch by the share of context tokens done
+    ctx = case.context_lens.astype(np.int64)
+    dtype = np.float32
+    t, tokens, calls = 0.0, 0, 0
+    while (t < 10.0 or calls == 0) and calls < 1_000_000:
+        part = [(calls + i) % case.batch for i in range(cores)]
+        t += parallel_oracle(lambda b: decode_attention(case.q1, case.q2, case.a, case.a_head_stride, case.k_pool,
+                                                        case.v_pool, case.block_table, case.context_lens,
+                                                        batches=[b], dtype=dtype), part, cores)
+        tokens += int(ctx[part].sum())
+        calls += len(part)
+    full = t * float(ctx.sum()) / max(tokens, 1)
+    sample = (f"the oracle's fp32 attention, one sequence per call on {cores} threads, {calls} calls "
+              f"({tokens / float(ctx.sum()):.2f} passes over the batch, {t:.1f} s), scaled by the share "
+              f"of context tokens")
+    return {"value": round(1.0 / full, 4), "unit": "steps/s", "cores": cores, "kind": "oracle",
             "sample": sample, "cpu_model": cpu_model()}
 
 
