@@ -63,6 +63,7 @@ SIGNATURES = {
     "dfx_decode_attn_plan": (I32, [KVP, I32, I32, I32, I32, I32, PI32, PSZ]),
     "dfx_decode_attn_workspace_size": (I32, [I32, I32, I32, KVP, I32, I32, PSZ]),
     "dfx_decode_attn": (I32, [KVP, P, I32, I32, I32, I32, P, P, I64, P, I32, F32, P, P, P, I32, P, SZ, P]),
+    "dfx_decode_attn_noalloc": (I32, [KVP, P, I32, I32, I32, I32, P, P, I64, P, I32, F32, P, P, P, I32, P]),
     "dfx_kv_append_primary": (I32, [KVP, I32, P, I32, P, P, I64, P]),
     "dfx_grouped_linear_workspace_size": (I32, [I32, I32, I32, I32, PSZ]),
     "dfx_grouped_linear": (I32, [I32, I32, I32, I32, I32, P, P, I32, I32, P, P, P, P, SZ, P]),

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -1159,3 +1160,67 @@ dfx_status dfx_fill_bytes(void *dst, size_t bytes, uint32_t pattern, void *strea
 }
 
 }  // extern "C"
+
+// ---- allocation-free decode attention -------------------------------------------------
+
+namespace {
+
+// Scratch of dfx_decode_attn_noalloc: the split partials live in this file-scope device array
+// (each device holds its own copy, from module load to process end). Host code never uses the
+// array's name as an address: its device address is looked up once per device.
+constexpr size_t kNoallocScratch = (size_t)DFX_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratch];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (hipGetSymbolAddress once per device,
+// with that device current).
+dfx_status scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DFX_EUNSUPPORTED, "device %d (at most %d devices)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(DFX_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DFX_OK;
+}
+
+}  // namespace
+
+extern "C" dfx_status dfx_decode_attn_noalloc(const dfx_kv_cache *kv, const int32_t *context_lens, int32_t batch,
+                                              int32_t max_context, int32_t num_q_heads, int32_t q_dtype,
+                                              const void *q1, const void *q2_raw, int64_t q_batch_stride,
+                                              const float *a, int32_t a_head_stride, float softmax_scale,
+                                              float *o1, float *o2, float *lse, int32_t num_splits,
+                                              void *stream) {
+  DFX_BEGIN
+  AttnCall c{kv, context_lens, batch, max_context, num_q_heads, q_dtype, q1, q2_raw, q_batch_stride,
+             a, a_head_stride, softmax_scale, o1, o2, lse, num_splits, nullptr, 0, 0};
+  dfx_status st = validate_attn(c);
+  if (st) return st;
+  // the plan's scratch, checked against the array before any HIP call
+  const int F = q2_raw ? 2 : 1, G = num_q_heads / kv->num_kv_heads;
+  int splits, chunk;
+  attn_plan(batch, kv->num_kv_heads, max_context, num_splits, paged_bs(kv), attn_mfma_path(kv, F, G), &splits,
+            &chunk);
+  const size_t need = attn_ws_bytes(splits, F, batch, num_q_heads, kv->head_dim);
+  if (need > kNoallocScratch)
+    return fail(DFX_EWORKSPACE, "decode_attn_noalloc needs %zu bytes of scratch for %d splits; the library's "
+                "array holds %zu (DFX_NOALLOC_SCRATCH_BYTES)", need, splits, kNoallocScratch);
+  if (batch == 0) return DFX_OK;
+  if (need > 0) {
+    if ((st = scratch_address(&c.ws))) return st;
+    c.ws_bytes = kNoallocScratch;
+  }
+  return run_attn(c, (hipStream_t)stream);
+  DFX_END
+}

@@ -163,6 +163,30 @@ dfx_status dfx_decode_attn(const dfx_kv_cache *kv, const int32_t *context_lens, 
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * dfx_decode_attn without a workspace argument, for callers that cannot allocate device
+ * memory around the call: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Same arguments (minus workspace / workspace_bytes), same plan, same
+ * kernels and the same results bit for bit. The split partials go to a file-scope device
+ * array of DFX_NOALLOC_SCRATCH_BYTES inside the library (one per device, held from the
+ * library's load until the process ends); the call itself allocates nothing. The first
+ * call on a device looks the array's address up (hipGetSymbolAddress) with that device
+ * current. Nothing in the array needs initial contents: every split the merge reads is
+ * written by the same call. All calls on one device share that device's array, so calls
+ * that overlap in time on one device (different streams, or host threads) race on it:
+ * serialize them. Errors: as dfx_decode_attn, plus DFX_EWORKSPACE (before any HIP call)
+ * when the plan's partials exceed DFX_NOALLOC_SCRATCH_BYTES (dfx_decode_attn_workspace_size
+ * gives that size), DFX_EUNSUPPORTED for a device index above 63, DFX_EHIP if the address
+ * lookup fails.
+ */
+#define DFX_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+dfx_status dfx_decode_attn_noalloc(const dfx_kv_cache *kv, const int32_t *context_lens, int32_t batch,
+                                   int32_t max_context, int32_t num_q_heads, int32_t q_dtype,
+                                   const void *q1, const void *q2_raw, int64_t q_batch_stride,
+                                   const float *a, int32_t a_head_stride, float softmax_scale,
+                                   float *o1, float *o2, float *lse, int32_t num_splits, void *stream);
+
+/*
  * Append the primary flow's new key and value rows to the cache (same page,
  * section "Architettura Core": the primary flow writes the persistent cache,
  * the auxiliary flow never does -- this call has no flow argument, so no

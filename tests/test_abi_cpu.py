@@ -21,7 +21,7 @@ def declared():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = _abi.lib()
     names = declared()
-    assert len(names) == 31
+    assert len(names) == 32
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, n
@@ -70,6 +70,24 @@ def attn(k, **over):
 def test_attention_rejects(kvover, over, status, needle):
     st, msg = attn(kv(**kvover), **over)
     assert st == status and needle in msg, (st, msg)
+
+
+def test_noalloc_attention_refuses_plans_beyond_its_scratch():
+    """dfx_decode_attn_noalloc checks the plan's partials against its fixed scratch array (16 MiB)
+    before any HIP call, and validates its arguments as dfx_decode_attn does."""
+    lib = _abi.lib()
+    k = kv(mb=8192, nb=65536)
+    # 64 sequences x 64 heads x 2 flows x 16 splits x 129 floats = 33.8 MB of partials
+    st = lib.dfx_decode_attn_noalloc(ctypes.byref(k), FAKE, 64, 131072, 64, 1, FAKE, FAKE, 0, FAKE, 0, 0.0,
+                                     FAKE, FAKE, None, 16, None)
+    msg = lib.dfx_last_error().decode()
+    assert st == 3 and "scratch" in msg and str(16 << 20) in msg, (st, msg)
+    st = lib.dfx_decode_attn_noalloc(ctypes.byref(kv(D=96)), FAKE, 2, 100, 32, 1, FAKE, FAKE, 0, FAKE, 0, 0.0,
+                                     FAKE, FAKE, None, 0, None)
+    assert st == 2 and "head_dim" in lib.dfx_last_error().decode()
+    st = lib.dfx_decode_attn_noalloc(ctypes.byref(k), None, 2, 100, 32, 1, FAKE, FAKE, 0, FAKE, 0, 0.0,
+                                     FAKE, FAKE, None, 0, None)
+    assert st == 1 and "context_lens" in lib.dfx_last_error().decode()
 
 
 def test_grid_extent_limits():
