@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="layer",
                    choices=["layer", "attn-b16", "attn-ragged", "attn-long", "attn-fp32", "step", "head", "moe",
-                            "prefill"])
+                            "prefill", "read-floor"])
     p.add_argument("--prompt", type=int, default=2048, help="prompt chunk of the 'prefill' workload")
     p.add_argument("--prefill-batch", type=int, default=2, help="sequences of the 'prefill' workload")
     p.add_argument("--layers", type=int, default=8, help="layers of the 'step' workload")
@@ -305,6 +305,8 @@ def main():
         return bench_moe(args)
     if args.workload == "prefill":
         return bench_prefill(args)
+    if args.workload == "read-floor":
+        return bench_read_floor(args)
     if args.copy_calibration:
         n = args.copy_calibration - args.copy_calibration % 16
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -467,6 +469,39 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": cfg, "roofline": roofline, "cpu_baseline": cpu, **extra}
     print(json.dumps(line))
+
+
+def bench_read_floor(args):
+    """The floor a streaming kernel of the step can reach: the library's read helper (contiguous
+    non-temporal 1 KiB loads) over the byte counts of the step's kernels, each call alone after
+    512 MB were written (per-call events, median of 9) and back to back; and the per-launch time
+    of a kernel that writes 16 bytes, back to back."""
+    import numpy as np
+    import torch
+
+    import dual_flow_shared_amd as dfx
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    flush = hbm_flush(dfx)
+    sizes = {"1 MB": 1e6, "8 MB": 8e6, "W_o 33.5 MB": 33554432, "W_qkv 50.3 MB": 50331648,
+             "W_down 117.4 MB": 117440512, "W_gate_up 234.9 MB": 234881024, "layer KV 1076 MB": 1075838976}
+    out = {}
+    for name, nb in sizes.items():
+        n = int(nb) // 16384 * 16384
+        buf = torch.empty(n // 4, dtype=torch.int32, device="cuda")
+        dfx.fill_bytes(buf, 0x01010101)
+        call = lambda: dfx.read_bytes(buf, sink)
+        each = np.array(timed_each(call, 9, stream, flush=flush))
+        b2b = timed(call, 20, stream)
+        out[name] = {"bytes": n, "flushed_us": round(float(np.median(each)) * 1e3, 2),
+                     "flushed_gbps": round(n / (float(np.median(each)) * 1e-3) / 1e9, 1),
+                     "back_to_back_us": round(b2b * 1e3, 2)}
+        del buf
+    tiny = torch.empty(4, dtype=torch.int32, device="cuda")
+    out["16-byte fill, back to back (us per launch)"] = round(timed(lambda: dfx.fill_bytes(tiny, 0), 200, stream) * 1e3, 2)
+    print(json.dumps({"metric": "read helper time at the step's byte counts", "unit": "us", "n_gpus": 1,
+                      "results": out}))
 
 
 def bench_step(args):

@@ -98,7 +98,7 @@ __device__ __forceinline__ void read_k_frags(u32x4 (*sk)[KRows<D>::CPR + 1], int
 constexpr int kAttnWaves = DFX_ATTN_WAVES;  // waves per work-group, interleaved over the tiles
 
 template <int D, bool QBF16, bool PAGED, bool KROWS>
-__global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) {
+__device__ __forceinline__ void attn_mfma_body(const AttnArgs &p) {
   constexpr int KS = D / 32;  // k-steps of the score contraction
   constexpr int VEC = D / 16; // head-dim elements one lane loads per V row; also O^T blocks
   constexpr int W = kAttnWaves, NTH = 64 * kAttnWaves;
@@ -244,23 +244,36 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) 
   }
 }
 
+// bf16 queries (two bf16 terms of Q and P)
+template <int D, bool PAGED, bool KROWS>
+__global__ void __launch_bounds__(64 * kAttnWaves) attn_mfma_kernel(AttnArgs p) {
+  attn_mfma_body<D, true, PAGED, KROWS>(p);
+}
+
+// fp32 queries (three terms): the bound keeps two waves per SIMD, which the register allocator
+// gives up for the third term's registers on some variants otherwise.
+template <int D, bool PAGED, bool KROWS>
+__global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_mfma_f32q_kernel(AttnArgs p) {
+  attn_mfma_body<D, false, PAGED, KROWS>(p);
+}
+
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s) {
   // The hardware hands work-group i to XCD i % 8. With the KV head fastest, XCD k serves
   // head k of every sequence (an equal share whatever the context lengths), and each XCD
   // dispatches all first splits (the longest pieces of ragged batches) before the later ones.
   const dim3 grid(a.num_kv_heads, a.batch, a.num_splits), block(64 * kAttnWaves);
   const bool paged = a.block_shift >= 0;
-#define DFX_ATTN_LAUNCH(D, QB, PG)                                           \
-  do {                                                                       \
-    if (a.k_rows) attn_mfma_kernel<D, QB, PG, true><<<grid, block, 0, s>>>(a); \
-    else attn_mfma_kernel<D, QB, PG, false><<<grid, block, 0, s>>>(a);         \
+#define DFX_ATTN_LAUNCH(KERNEL, D, PG)                                 \
+  do {                                                                 \
+    if (a.k_rows) KERNEL<D, PG, true><<<grid, block, 0, s>>>(a);        \
+    else KERNEL<D, PG, false><<<grid, block, 0, s>>>(a);                \
   } while (0)
   if (a.head_dim == 128) {
-    if (a.q_bf16) { if (paged) DFX_ATTN_LAUNCH(128, true, true); else DFX_ATTN_LAUNCH(128, true, false); }
-    else { if (paged) DFX_ATTN_LAUNCH(128, false, true); else DFX_ATTN_LAUNCH(128, false, false); }
+    if (a.q_bf16) { if (paged) DFX_ATTN_LAUNCH(attn_mfma_kernel, 128, true); else DFX_ATTN_LAUNCH(attn_mfma_kernel, 128, false); }
+    else { if (paged) DFX_ATTN_LAUNCH(attn_mfma_f32q_kernel, 128, true); else DFX_ATTN_LAUNCH(attn_mfma_f32q_kernel, 128, false); }
   } else {
-    if (a.q_bf16) { if (paged) DFX_ATTN_LAUNCH(64, true, true); else DFX_ATTN_LAUNCH(64, true, false); }
-    else { if (paged) DFX_ATTN_LAUNCH(64, false, true); else DFX_ATTN_LAUNCH(64, false, false); }
+    if (a.q_bf16) { if (paged) DFX_ATTN_LAUNCH(attn_mfma_kernel, 64, true); else DFX_ATTN_LAUNCH(attn_mfma_kernel, 64, false); }
+    else { if (paged) DFX_ATTN_LAUNCH(attn_mfma_f32q_kernel, 64, true); else DFX_ATTN_LAUNCH(attn_mfma_f32q_kernel, 64, false); }
   }
 #undef DFX_ATTN_LAUNCH
   return hipGetLastError();
