@@ -450,11 +450,12 @@ def main():
     extra["stream_read"] = stream_read(dfx, stream)
     if args.workload == "layer" and not args.no_attention_workloads:
         extra["attention_workloads"] = attention_workloads(dfx, gen, stream, args.kernel_reps)
+    # the layer's attention takes fp32 queries (three bf16 terms); the attention workloads bf16
+    kname = "attn_mfma_f32q_kernel" if args.workload == "layer" else "attn_mfma_kernel"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic_from_profiles("attn_mfma.hip", args.workload),
-                "kernel": ("attn_mfma_kernel" if splits == 1 else
-                           f"attn_mfma_kernel + attn_merge_kernel ({splits} splits)")
+                "kernel": (kname if splits == 1 else f"{kname} + attn_merge_kernel ({splits} splits)")
                 if shape["kv_el"] == 2 else "attn_valu_kernel",
                 "bytes_per_launch": int(abytes)}
 
