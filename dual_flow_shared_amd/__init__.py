@@ -20,7 +20,7 @@ __all__ = ["DfxError", "KVCache", "LayerWeights", "decode_attn", "decode_attn_pl
            "dual_flow_decode_layer", "layer_workspace_size", "copy_bytes", "read_bytes", "fill_bytes",
            "layer_taps", "dual_flow_decode_step", "step_workspace_size", "output_head",
            "output_head_workspace_size", "output_head_taps", "MoeWeights", "moe_mlp", "moe_workspace_size",
-           "moe_taps", "prefill_attn", "prefill_layer", "prefill_step", "Workspace", "version"]
+           "moe_taps", "prefill_attn", "prefill_layer", "prefill_layer_taps", "prefill_step", "Workspace", "version"]
 
 
 def version() -> int:
@@ -501,6 +501,15 @@ def prefill_dual_attn(q1: torch.Tensor, q2_raw: torch.Tensor, a: Optional[torch.
     check(lib().dfx_prefill_dual_attn(ctypes.byref(c), _ptr(start_pos), B, T, max_context, Hq, _ptr(q1), _ptr(q2_raw),
                                       _ptr(a), stride, 0, _ptr(o1), _ptr(o2), _ptr(lse), _stream(stream)))
     return (o1, o2, lse) if want_lse else (o1, o2)
+
+
+def prefill_layer_taps(weights: LayerWeights, cache: KVCache, batch: int, chunk: int, max_context: int) -> dict:
+    """Byte offsets of a prefill layer call's intermediates in its workspace: h1, q, o, h2, inter
+    (layouts in include/dfx.h, dfx_prefill_layer_taps)."""
+    t = LayerTapsStruct()
+    w, c = weights.struct(), cache.struct()
+    check(lib().dfx_prefill_layer_taps(ctypes.byref(w), ctypes.byref(c), batch, chunk, max_context, ctypes.byref(t)))
+    return {name: getattr(t, name) for name, _ in t._fields_}
 
 
 def prefill_layer(x: torch.Tensor, weights: LayerWeights, cache: KVCache, start_pos: torch.Tensor,

@@ -1066,6 +1066,22 @@ dfx_status dfx_prefill_layer_workspace_size(const dfx_layer_weights *w, const df
   DFX_END
 }
 
+dfx_status dfx_prefill_layer_taps(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_t batch,
+                                  int32_t chunk, int32_t max_context, dfx_layer_taps *taps) {
+  DFX_BEGIN
+  PrefillPlan p;
+  dfx_status st = prefill_plan(w, kv, batch, chunk, max_context, &p);
+  if (st) return st;
+  if (!taps) return fail(DFX_EINVAL, "taps is NULL");
+  taps->h1 = 0;
+  taps->q = p.h1;
+  taps->o = taps->q + p.qkv;
+  taps->h2 = taps->o + p.o;
+  taps->inter = taps->h2 + p.h2;
+  return DFX_OK;
+  DFX_END
+}
+
 dfx_status dfx_prefill_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv, const int32_t *start_pos,
                              int32_t batch, int32_t chunk, int32_t max_context, float *x, void *workspace,
                              size_t workspace_bytes, void *stream) {

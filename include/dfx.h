@@ -557,6 +557,22 @@ dfx_status dfx_prefill_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv,
                              size_t workspace_bytes, void *stream);
 
 /*
+ * Where a completed dfx_prefill_layer call with the same sizes leaves its intermediates in the
+ * workspace (the same rounding points as the decode layer; Sintesi Tecnica: Dual-Flow
+ * Transformers, section "Architettura Core": during prefill the primary runs alone), byte
+ * offsets of, for the batch * chunk rows r = b * chunk + t:
+ *   h1     bf16 normed rows entering W_qkv, in the activation fragment order of
+ *          dfx_dual_flow_decode_layer_taps with one flow (64-row groups of r)  [hidden columns]
+ *   q      fp32 rows [batch * chunk][(Hq + 2 Hkv) * D]: the whole Q/K/V projection
+ *   o      bf16 attention rows entering W_o, fragment order                     [Hq * D]
+ *   h2     bf16 normed rows entering W_gate_up, fragment order                  [hidden]
+ *   inter  bf16 SwiGLU rows entering W_down, fragment order                     [intermediate]
+ * Pure host arithmetic; the arguments dfx_prefill_layer_workspace_size rejects are rejected.
+ */
+dfx_status dfx_prefill_layer_taps(const dfx_layer_weights *w, const dfx_kv_cache *kv, int32_t batch,
+                                  int32_t chunk, int32_t max_context, dfx_layer_taps *taps);
+
+/*
  * dfx_prefill_step: tokens (device int32 [batch][chunk], clamped to [0, vocab)) through the
  * primary's embedding table (bf16 [vocab][hidden], 8-byte aligned) and every layer
  * (dfx_prefill_layer with layers[l], caches[l]); x (device fp32 [batch][chunk][hidden]) is

@@ -21,7 +21,7 @@ def declared():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = _abi.lib()
     names = declared()
-    assert len(names) == 32
+    assert len(names) == 33
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, n
@@ -363,6 +363,14 @@ def test_prefill_rejects():
     assert lib.dfx_prefill_layer_workspace_size(ctypes.byref(w), ctypes.byref(k), 2, 2048, 8193 * 8, ctypes.byref(n)) == 1
     assert lib.dfx_prefill_layer(ctypes.byref(w), ctypes.byref(k), FAKE, 2, 2048, 8192, FAKE, None, 0, None) == 3
     assert lib.dfx_prefill_layer(ctypes.byref(w), ctypes.byref(k), FAKE, 2, 0, 8192, FAKE, None, 0, None) == 0
+    # the intermediates' offsets: regions in order h1, q, o, h2, inter, inside the workspace
+    t = _abi.LayerTapsStruct()
+    assert lib.dfx_prefill_layer_taps(ctypes.byref(w), ctypes.byref(k), 2, 2048, 8192, ctypes.byref(t)) == 0
+    assert t.h1 == 0 and t.q >= rows * 4096 * 2 and t.o >= t.q + rows * (32 + 16) * 128 * 4
+    assert t.h2 >= t.o + rows * 32 * 128 * 2 and t.inter >= t.h2 + rows * 4096 * 2
+    assert t.inter + rows * 14336 * 2 <= n.value
+    assert lib.dfx_prefill_layer_taps(ctypes.byref(w), ctypes.byref(k), 2, 2048, 8192, None) == 1
+    assert lib.dfx_prefill_layer_taps(ctypes.byref(w), ctypes.byref(k), 2, 2048, 8193 * 8, ctypes.byref(t)) == 1
     w.num_q_heads = 6
     assert lib.dfx_prefill_layer_workspace_size(ctypes.byref(w), ctypes.byref(k), 2, 16, 8192, ctypes.byref(n)) == 2
     k32 = kv(dtype=0, mb=512, nb=16384)

@@ -67,6 +67,27 @@ def gamma(k):
     return (k / 32 + 64) * U
 
 
+def norm_bound(xin, err_in, gain, y, eps):
+    """Error bound of y = x r g (RMSNorm before its bf16 rounding): the input's error (through x
+    and through r) and the fp32 norm (sum of squares over H terms, reciprocal square root, two
+    products)."""
+    H = xin.shape[-1]
+    r = 1.0 / np.sqrt(np.mean(xin * xin, axis=-1, keepdims=True) + eps)
+    rel_r = np.linalg.norm(err_in, axis=-1, keepdims=True) / np.linalg.norm(xin, axis=-1, keepdims=True)
+    return np.abs(widen(gain)) * r * (err_in + np.abs(xin) * (rel_r + (H / 2 + 8) * U)) + 4 * U * np.abs(y)
+
+
+def attention_row_bound(q, K, V, w, D):
+    """Error bound of one attention row (query q, keys K [n][D], values V, exact weights w):
+    score error max_p scale sum|q||k| (D/32 + 64) u (Q and P are split into bf16 terms exactly),
+    doubled through the softmax, plus (n/32 + 64) u, times sum_p w_p |v_p|."""
+    n = K.shape[0]
+    sabs = np.abs(q) @ np.abs(K).T / np.sqrt(D)
+    ds = sabs.max() * (SPLIT + (D / 32 + 64) * U)
+    rel = 2 * ds + 2 * SPLIT + (n / 32 + 64) * U
+    return rel * (w @ np.abs(V))
+
+
 def check_layer_chain(c, flows=2, couple=True, rows=None):
     """Runs the layer and checks every stage against the oracle applied to the GPU's own
     previous stage (read from the workspace through dfx_dual_flow_decode_layer_taps): each
@@ -103,11 +124,7 @@ def check_layer_chain(c, flows=2, couple=True, rows=None):
     absw = lambda m: np.abs(widen(m))
 
     def norm_scale(xin, err_in, gain, y):
-        # y = x r g: error from the input's error (through x and through r) and from the
-        # fp32 norm (sum of squares over H terms, reciprocal square root, two products)
-        r = 1.0 / np.sqrt(np.mean(xin * xin, axis=-1, keepdims=True) + c.eps)
-        rel_r = np.linalg.norm(err_in, axis=-1, keepdims=True) / np.linalg.norm(xin, axis=-1, keepdims=True)
-        return np.abs(widen(gain)) * r * (err_in + np.abs(xin) * (rel_r + (H / 2 + 8) * U)) + 4 * U * np.abs(y)
+        return norm_bound(xin, err_in, gain, y, c.eps)
 
     # R1: normed rows from the exact input
     h1_exact = rmsnorm(x0, c.g_attn, c.eps, rounded=False)
@@ -142,10 +159,7 @@ def check_layer_chain(c, flows=2, couple=True, rows=None):
             for f in range(F):
                 for hh in range(G):
                     h = g * G + hh
-                    sabs = np.abs(Qs[f][i, h]) @ np.abs(K[g]).T / np.sqrt(D)  # [n]
-                    ds = sabs.max() * (SPLIT + (D / 32 + 64) * U)
-                    rel = 2 * ds + 2 * SPLIT + (n / 32 + 64) * U
-                    o_scale[f, i, h * D:(h + 1) * D] = rel * (Wt[f * G + hh] @ np.abs(V[g]))
+                    o_scale[f, i, h * D:(h + 1) * D] = attention_row_bound(Qs[f][i, h], K[g], V[g], Wt[f * G + hh], D)
     same["o"] = bf16_decisions_agree(o, o_exact, rel=1.0, scale=o_scale)
     # x1 (not kept by the layer) from the GPU's attention rows, R4 from it
     wo_abs = absw(o) @ absw(c.w_o).T

@@ -23,6 +23,10 @@ from oracle.linear import rmsnorm
 from oracle.numerics import widen
 from oracle.step import dual_flow_step
 from twins import assert_twin_close, twin_errors
+from gpu_util import bf16_decisions_agree, unpack_rows
+from oracle.attention import decode_attention, gather_kv
+from oracle.linear import grouped_linear, swiglu_couple
+from test_gpu_layer import U, attention_row_bound, gamma, norm_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -305,3 +309,116 @@ def test_prefill_then_aux_start_matches_oracle():
     want, _ = dual_flow_step(tokens[:, n - 1], e1, e2, done, np.full(B, n - 1))
     assert_twin_close(x_last.cpu().numpy(), want, twin_errors(twin_start, None, want, layers=layers),
                       "auxiliary start")
+
+
+def check_prefill_chain(c, x, st, samples, tag):
+    """Runs the prefill layer on chunk x [B][T][hidden] from positions st and checks every stage of
+    the sampled rows (b, t) against the oracle applied to the GPU's own previous stage, read from
+    the workspace (dfx_prefill_layer_taps): the normed rows' bf16 decisions, the whole Q/K/V
+    projection row (fp32, accumulation bound), the appended key and value rows' decisions, the
+    attention rows' decisions (GPU queries over the GPU's cache), the MLP's normed rows, the SwiGLU
+    rows and the output rows (each projection within its accumulation bound). Returns the output."""
+    B, T, H = x.shape
+    Hq, Hkv, D, I = c.num_q_heads, c.num_kv_heads, c.head_dim, c.intermediate
+    HqD, Nqkv = Hq * D, (Hq + 2 * Hkv) * D
+    mc = int(st.max()) + T + 8
+    cache = cache_of(c.cache)
+    w = weights_of(c)
+    ws = dfx.Workspace()
+    xt = dev(x)
+    print(f"prefill chain ({tag}): B={B} T={T} hidden={H}, {len(samples)} rows", flush=True)
+    dfx.prefill_layer(xt, w, cache, dev(st), mc, workspace=ws)
+    torch.cuda.synchronize()
+    taps = dfx.prefill_layer_taps(w, cache, B, T, mc)
+    buf = ws.buf.cpu().numpy()
+    rows = np.array([b * T + t for b, t in samples])
+    padded = -(-(B * T) // 64) * 64
+
+    def bf16_region(name, K):
+        return unpack_rows(buf[taps[name]: taps[name] + padded * K * 2].view(np.uint16), 1, B * T, K)[0, rows]
+
+    h1, o, h2, inter = bf16_region("h1", H), bf16_region("o", HqD), bf16_region("h2", H), bf16_region("inter", I)
+    qkv = buf[taps["q"]: taps["q"] + B * T * Nqkv * 4].view(np.float32).reshape(B * T, Nqkv)[rows]
+    kp, vp = host_bits(cache.k), host_bits(cache.v)
+    y = xt.cpu().numpy().reshape(B * T, H)[rows].astype(np.float64)
+    x0 = x.reshape(B * T, H)[rows].astype(np.float64)
+    absw = lambda m: np.abs(widen(m))
+    same = {}
+    # normed rows from the exact input
+    h1_exact = rmsnorm(x0, c.g_attn, c.eps, rounded=False)
+    same["h1"] = bf16_decisions_agree(h1, h1_exact, rel=1.0, scale=norm_bound(x0, 0 * x0, c.g_attn, h1_exact, c.eps))
+    # the Q/K/V projection of the GPU's normed rows, and the appended key / value rows
+    qkv_ref = grouped_linear(h1[None], c.w_qkv)[0]
+    qkv_abs = absw(h1) @ absw(c.w_qkv).T
+    assert np.all(np.abs(qkv - qkv_ref) <= gamma(H) * qkv_abs + 1e-30)
+    tbl, bs = c.cache.block_table, c.cache.k_pool.shape[2]
+    for i, (b, t) in enumerate(samples):
+        pos = int(st[b]) + t
+        for pool, lo in ((kp, HqD), (vp, HqD + Hkv * D)):
+            got = pool[tbl[b, pos // bs], :, pos % bs, :].reshape(1, Hkv * D)
+            same.setdefault("kv", []).append(bf16_decisions_agree(got, qkv_ref[i: i + 1, lo: lo + Hkv * D],
+                                                                  rel=gamma(H), scale=qkv_abs[i: i + 1, lo: lo + Hkv * D]))
+    same["kv"] = float(np.mean(same["kv"]))
+    # attention rows: the GPU's queries over the GPU's cache
+    o_exact = np.empty((len(samples), HqD))
+    o_scale = np.empty_like(o_exact)
+    G = Hq // Hkv
+    for i, (b, t) in enumerate(samples):
+        n = int(st[b]) + t + 1
+        q = qkv[i, :HqD].reshape(1, Hq, D)
+        o1, _, _, wts = decode_attention(q, None, None, 0, kp, vp, tbl[b: b + 1], np.array([n]), return_weights=True)
+        o_exact[i] = o1.reshape(-1)
+        K = widen(gather_kv(kp, tbl[b: b + 1], 0, n))
+        V = widen(gather_kv(vp, tbl[b: b + 1], 0, n))
+        for g in range(Hkv):
+            for hh in range(G):
+                h = g * G + hh
+                o_scale[i, h * D:(h + 1) * D] = attention_row_bound(widen(q[0, h]), K[g], V[g], wts[(0, g)][hh], D)
+    same["o"] = bf16_decisions_agree(o, o_exact, rel=1.0, scale=o_scale)
+    # W_o and the residual (not kept), the MLP norm of that
+    x1 = grouped_linear(o[None], c.w_o, residual=x0[None])[0]
+    e1 = gamma(HqD) * (absw(o) @ absw(c.w_o).T) + U * np.abs(x1)
+    h2_exact = rmsnorm(x1, c.g_mlp, c.eps, rounded=False)
+    same["h2"] = bf16_decisions_agree(h2, h2_exact, rel=1.0, scale=norm_bound(x1, e1, c.g_mlp, h2_exact, c.eps))
+    # gate/up with SwiGLU from the GPU's normed rows
+    gu = grouped_linear(h2[None], c.w_gate_up)[0]
+    gu_err = gamma(H) * (absw(h2) @ absw(c.w_gate_up).T)
+    gate, up = gu[..., :I], gu[..., I:]
+    sig = 1.0 / (1.0 + np.exp(-gate))
+    e_int = 1.1 * gu_err[..., :I] * np.abs(up) + np.abs(gate * sig) * gu_err[..., I:] + 6 * U * np.abs(gate * sig * up)
+    inter_exact = swiglu_couple(gu[None], None, rounded=False)[0]
+    same["inter"] = bf16_decisions_agree(inter, inter_exact, rel=1.0, scale=e_int + U * np.abs(inter_exact))
+    # W_down and the residual from the GPU's SwiGLU rows
+    x2 = grouped_linear(inter[None], c.w_down, residual=x1[None])[0]
+    bound = e1 + gamma(I) * (absw(inter) @ absw(c.w_down).T) + U * np.abs(x2)
+    err = np.abs(y - x2)
+    print("prefill chain: bf16 decisions equal to the oracle's:", {k: round(v, 5) for k, v in same.items()},
+          "| output error / bound: max %.3g" % float((err / bound).max()), flush=True)
+    assert np.all(err <= bound), float((err / bound).max())
+    return xt
+
+
+@pytest.mark.parametrize("B,T,start,shape,tiles", [
+    # 3 x 50 rows from position 4: three 64-row groups with a ragged tail; every projection on the
+    # 256 x 128 tile (hidden 288: Q/K/V 1536 features, W_o and W_down 288 = one full and one
+    # ragged feature tile, gate/up 544 gate features = four full tiles of 128 and a ragged one;
+    # down K = 17 k-steps)
+    (3, 50, 4, dict(hidden=288, num_q_heads=8, num_kv_heads=2, head_dim=128, intermediate=544, w_std=0.05),
+     "256 x 128"),
+    # 2 x 3995 rows from position 0: gate/up, W_o and W_down on the 256 x 256 tile with a ragged
+    # last row group (7990 rows) and ragged feature tiles
+    (2, 3995, 0, dict(hidden=288, num_q_heads=4, num_kv_heads=2, head_dim=64, intermediate=1504, w_std=0.05),
+     "256 x 256, ragged"),
+    # the prefill benchmark's shape: 2 x 2048 rows, hidden 4096, 32/8 x 128, SwiGLU 14336 (gate/up,
+    # W_o, W_down on the 256 x 256 tile, Q/K/V on the 256 x 128 one)
+    (2, 2048, 0, dict(hidden=4096, num_q_heads=32, num_kv_heads=8, head_dim=128, intermediate=14336, w_std=0.02),
+     "benchmark shape"),
+])
+def test_prefill_layer_chain(B, T, start, shape, tiles):
+    c = gen.layer_case(720 + T % 97, batch=B, context=start + 1, capacity=start + T + 8, **shape)
+    x = np.random.default_rng(T).standard_normal((B, T, c.hidden)).astype(np.float32)
+    st = np.full(B, start, np.int32)
+    rng = np.random.default_rng(31)
+    samples = [(0, 0), (0, T - 1), (B - 1, 0), (B - 1, T - 1), (B - 1, T // 2)]
+    samples += [(int(b), int(t)) for b, t in zip(rng.integers(0, B, 11), rng.integers(0, T, 11))]
+    check_prefill_chain(c, x, st, samples, tiles)
