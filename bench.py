@@ -1,7 +1,7 @@
 """Benchmark of the dual-flow decode step on one MI355X.
 
 python bench.py [--steps K] [--warmup W]
-                [--workload layer|attn-b16|attn-ragged|attn-long|attn-fp32|step|head|moe|prefill]
+                [--workload layer|attn-b16|attn-ragged|attn-long|attn-fp32|step|head|moe|prefill|read-floor]
 
 A step of the default workload is one full dual-flow decode layer (both flows, batch
 32, context 8192, hidden 4096, 32/8 heads x 128, SwiGLU 14336, paged bf16 cache of
