@@ -670,7 +670,7 @@ def bench_head(args):
                        "batch": B, "hidden": H, "vocab": V, "flows": F},
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                         "kernel": "whole head call (5 launches); algorithmic bytes = W_out + rows + gain + outputs",
+                         "kernel": "whole head call (4 launches; 5 when the projection splits K); algorithmic bytes = W_out + rows + gain + outputs",
                          "bytes_per_launch": int(alg)},
             "cpu_baseline": cpu}
     print(json.dumps(line))

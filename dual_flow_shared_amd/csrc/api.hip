@@ -185,10 +185,11 @@ dfx_status check_linear(int32_t n_flows, int32_t rows, int32_t K, int32_t N) {
 dfx_status run_linear_parts(int32_t n_flows, int32_t rows, int32_t K, int32_t N, int x_f32,
                             const void *x, const uint16_t *w, int w_packed, int y_bf16, void *y,
                             const float *couple, const float *residual, float *partial,
-                            hipStream_t s, int tiles_only = 0) {
+                            hipStream_t s, int tiles_only = 0, float *mix_stats = nullptr) {
   if (rows == 0) return DFX_OK;
   const GemmPlan g = gemm_plan(n_flows, rows, K, N);
   GemmArgs a{};
+  a.mix_stats = g.ksplit == 1 ? mix_stats : nullptr;
   a.n_flows = n_flows; a.rows = rows; a.K = K; a.N = N;
   a.x_f32 = x_f32 == 1; a.x_packed = x_f32 == 2;
   a.x = x; a.w = w; a.w_packed = w_packed; a.y_bf16 = y_bf16; a.y = y;
@@ -757,10 +758,14 @@ dfx_status dfx_dual_flow_output_head(int32_t n_flows, int32_t batch, int32_t hid
   float *stats = (float *)(base + p.h + p.logits + p.partial);
   dfx_status r = hip_status(launch_rmsnorm(n_flows * batch, hidden, x, norm_gain, eps, h, s, n_flows), "rmsnorm launch");
   if (r) return r;
-  // one pass over the shared vocabulary matrix for both flows' rows
-  if ((r = run_linear_parts(n_flows, batch, hidden, vocab, 2, h, w_out, 1, 0, logits, nullptr, nullptr, partial, s)))
+  // one pass over the shared vocabulary matrix for both flows' rows; in one K split the
+  // projection also writes the softmax statistics of each 128-logit tile
+  const bool tile_stats = gemm_plan(n_flows, batch, hidden, vocab).ksplit == 1;
+  if ((r = run_linear_parts(n_flows, batch, hidden, vocab, 2, h, w_out, 1, 0, logits, nullptr, nullptr, partial, s,
+                            0, stats)))
     return r;
-  return hip_status(launch_mixture(n_flows, batch, vocab, logits, uniform_noise, stats, next_token, alpha, p_mix, s),
+  return hip_status(launch_mixture(n_flows, batch, vocab, logits, uniform_noise, stats, next_token, alpha, p_mix,
+                                   tile_stats, s),
                     "mixture launch");
   DFX_END
 }

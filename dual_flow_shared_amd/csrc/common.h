@@ -181,7 +181,15 @@ struct GemmArgs {
   // many row groups (prefill), one split: grid z = group_split slices of the row groups, each
   // work-group streams its weight columns once per group of its slice
   int32_t group_split;
+  // output-head mode (one split, plain outputs, packed X and W): softmax statistics of every
+  // (128-feature tile, row) of the fp32 outputs, from the accumulators: record
+  // [row][tile][kMixStat] = tile max and sum of e^(l - max) of each flow, and for the primary
+  // the sum of e^(2 (l - max)) (the layout the mixture's apply pass reads)
+  float *mix_stats;
 };
+// per (sequence, statistics chunk): m0, s0, q0, m1, s1, 3 unused
+constexpr int kMixStat = 8;
+constexpr int kHeadTile = 128;  // output features per grouped-linear work-group (plain mode)
 
 // Destination of attention output (flow f, sequence b, column c = head * D + d): rows
 // [B][Hq * D] of o1 / o2, or, with o_packed, both flows in o1 in the fragment order of
@@ -280,9 +288,14 @@ hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float
 hipError_t launch_embed_norm(int32_t n_flows, int32_t batch, int32_t dim, const int32_t *tokens,
                              int32_t vocab, const uint16_t *embed0, const uint16_t *embed1,
                              const float *gain, float eps, float *x, uint16_t *h1, hipStream_t s);
+// Mixture workspace: per-sequence statistics records (enough for either chunking) and the
+// apply pass's per-chunk results.
 size_t mixture_stats_bytes(int32_t batch, int32_t vocab);
+// stats_per_tile: the projection already wrote one statistics record per 128-logit tile
+// (output-head mode of the grouped linear); otherwise a statistics pass runs first.
 hipError_t launch_mixture(int32_t n_flows, int32_t batch, int32_t vocab, const float *logits, const float *noise,
-                          float *stats, int32_t *token, float *alpha, float *p_mix, hipStream_t s);
+                          float *stats, int32_t *token, float *alpha, float *p_mix, bool stats_per_tile,
+                          hipStream_t s);
 hipError_t launch_swiglu(int32_t n_flows, int32_t rows, int32_t dim, const float *gu,
                          const float *b, uint16_t *out, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
