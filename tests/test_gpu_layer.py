@@ -264,6 +264,20 @@ def test_full_size_layer_all_rows():
     assert len(changed) == c.batch * c.num_kv_heads
 
 
+@pytest.mark.parametrize("shape", [dict(hidden=2048, num_q_heads=32, num_kv_heads=8, intermediate=4096),
+                                   dict(hidden=4096, num_q_heads=8, num_kv_heads=4, intermediate=1024)])
+def test_layer_sixteen_split_finishes(shape):
+    """Shapes whose projections split K 16 ways, so the finish kernels sum their tiles in the
+    16-split form: hidden 2048 with 32 query heads (W_o and W_down over 16 feature tiles of
+    K = 4096: 16 splits each), and hidden 4096 with 8/4 heads (the Q/K/V projection's 2048
+    outputs over K = 4096: 16 splits)."""
+    c = gen.layer_case(809, batch=4, context=300, head_dim=128, w_std=0.03, **shape)
+    y, _, _ = check_layer_chain(c)
+    layer_close(c, y)
+    y1, _, _ = check_layer_chain(c, flows=1)
+    assert np.array_equal(y1[0], y[0])
+
+
 @pytest.mark.parametrize("flows", [2, 1])
 def test_layer_single_sequence(flows):
     # one sequence: a 64-row group holding one row per flow, context 1 (the appended token only)

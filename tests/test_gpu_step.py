@@ -39,6 +39,21 @@ def test_step_equals_layer_calls_bit_for_bit():
         assert np.array_equal(host_bits(a.k), host_bits(b.k)) and np.array_equal(host_bits(a.v), host_bits(b.v))
 
 
+def test_step_sixteen_split_finish_equals_layer_calls():
+    """The down projection's finish into the next layer's norm with 16 K splits (hidden 2048,
+    SwiGLU 4096: 16 feature tiles of K = 4096) gives exactly what the layer calls give."""
+    c = gen.step_case(902, 2, vocab=300, batch=4, context=120, hidden=2048, num_q_heads=16, num_kv_heads=4,
+                      head_dim=128, intermediate=4096, w_std=0.03)
+    layers, caches, ctx, maxc, tokens, e1, e2 = inputs(c)
+    x = dfx.dual_flow_decode_step(tokens, e1, e2, layers, caches, ctx, maxc)
+    ref_caches = [cache_of(L.cache) for L in c.layers]
+    xr = torch.stack([e1[tokens.long()].float(), e2[tokens.long()].float()]).contiguous()
+    for w, kv in zip(layers, ref_caches):
+        dfx.dual_flow_decode_layer(xr, w, kv, ctx, maxc)
+    torch.cuda.synchronize()
+    assert torch.equal(x, xr)
+
+
 def test_full_size_step_equals_layer_calls_bit_for_bit():
     """The decode step in the one-layer workload's shape and the benchmark's launch
     configuration (batch 32, context 8192, hidden 4096, 32/8 heads x 128, SwiGLU 14336, paged
