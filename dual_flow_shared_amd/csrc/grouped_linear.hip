@@ -19,6 +19,11 @@
 // When K is split over several work-groups each writes its fp32 tile to a workspace and a
 // second kernel (or the layer's finish kernel) sums the splits in split order; either way
 // the reduction order of an output element depends only on (K, N), never on rows or flows.
+//
+// Output-head mode (one split, fp32 logits): after storing its tile a work-group also writes
+// the softmax statistics of every row over its 128 outputs (max, sum of e^(l - max), and for
+// the primary sum of e^(2 (l - max))), which the mixture's apply pass combines; the logits are
+// stored non-temporally.
 #include "common.h"
 
 namespace dfx {
