@@ -117,52 +117,96 @@ __device__ __forceinline__ void tile_scores(const TileRegs<D> &r, const u32x4 (&
       for (int t = 0; t < NT; ++t) sacc[mb] = mfma16x16x32(as_bf16x8(r.kf[mb][s]), as_bf16x8(q[t][s]), sacc[mb]);
 }
 
+// Lazy running max (prefill): a row keeps its running max m until a tile's max exceeds it by
+// more than kLazyMax (log2 units), so that P = 2^(s - m) stays below 2^kLazyMax -- exact in
+// fp32 and in the bf16 terms, and far from overflow -- and most tiles need no rescale of O.
+constexpr float kLazyMax = 8.f;
+
 // Online-softmax update for query row n (the lane holds 8 of the tile's 32 tokens) and
 // P.V accumulation into O^T, with P split into NT bf16 terms (one MFMA pass per term).
-template <int D, int NT>
+// LAZY: the running max moves only by more than kLazyMax, the rescale of O is skipped when
+// no row of the wave moved it (a factor of exactly 1 for the rows that did not), and P is
+// 2^x from the hardware exponential (P below 2^-126, flushed to zero, is below the fp32
+// resolution of the row sum, which is >= 1).
+template <int D, int NT, bool LAZY = false>
 __device__ __forceinline__ void tile_softmax_pv(const AttnArgs &p, const TileRegs<D> &r,
                                                 const f32x4 *sacc, int t0, int end, int j,
                                                 float &m_run, float &l_run, f32x4 *oacc) {
   constexpr int VEC = D / 16;
   float sv[8];
   float mx = -INFINITY;
+  // (LAZY: a tile inside every row's range, i.e. all but the last of a causal row, skips the
+  // per-token test)
+  const bool whole = LAZY && __all(t0 + 32 <= end);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = t0 + 16 * mb + 4 * j + i;
-      const float x = tok < end ? sacc[mb][i] * p.scale_log2 : -INFINITY;
+      const float x = whole || tok < end ? sacc[mb][i] * p.scale_log2 : -INFINITY;
       sv[4 * mb + i] = x;
       mx = fmaxf(mx, x);
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m_run, mx);
-  const float alpha = exp2f(m_run - m_new);
+  float m_new, alpha;
+  if constexpr (LAZY) {
+    m_new = mx > m_run + kLazyMax ? mx : m_run;
+    alpha = m_new == m_run ? 1.f : exp2f(m_run - m_new);
+  } else {
+    m_new = fmaxf(m_run, mx);
+    alpha = exp2f(m_run - m_new);
+  }
   float psum = 0.f;
-  uint32_t pt[8][NT];
+  u32x4 pk[NT];
+  if constexpr (NT >= 3) {
+    // every term a truncation (split_terms: exact with three terms); the bf16 halves of two
+    // tokens' remainders go into one word by a byte permute
+    uint32_t rem[8][NT];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    const float pv = exp2f(sv[v] - m_new);
-    psum += pv;
-    split_terms<NT>(pv, pt[v]);
+    for (int v = 0; v < 8; ++v) {
+      const float pv = LAZY ? __builtin_amdgcn_exp2f(sv[v] - m_new) : exp2f(sv[v] - m_new);
+      psum += pv;
+      float r = pv;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        rem[v][t] = __float_as_uint(r);
+        if (t + 1 < NT) r -= __uint_as_float(rem[v][t] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pk[t][w] = __builtin_amdgcn_perm(rem[2 * w + 1][t], rem[2 * w][t], 0x07060302u);
+  } else {
+    uint32_t pt[8][NT];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const float pv = LAZY ? __builtin_amdgcn_exp2f(sv[v] - m_new) : exp2f(sv[v] - m_new);
+      psum += pv;
+      split_terms<NT>(pv, pt[v]);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pk[t][w] = pt[2 * w][t] | (pt[2 * w + 1][t] << 16);
   }
   l_run = l_run * alpha + psum;
   m_run = m_new;
-  u32x4 pk[NT];
+  if (!LAZY || __any(alpha != 1.f)) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) pk[t][w] = pt[2 * w][t] | (pt[2 * w + 1][t] << 16);
+    for (int mb = 0; mb < VEC; ++mb) oacc[mb] *= alpha;
+  }
 #pragma unroll
   for (int mb = 0; mb < VEC; ++mb) {
-    oacc[mb] *= alpha;
-    // V^T rows d = VEC*n + mb over tokens tau(j, 0..7): element mb of each loaded row
+    // V^T rows d = VEC*n + mb over tokens tau(j, 0..7): element mb of each loaded row, two
+    // tokens' halves per word (one byte permute: the low halves for even mb, the high halves
+    // for odd mb)
     u32x4 af;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t x0 = r.vr[2 * w][mb >> 1], x1 = r.vr[2 * w + 1][mb >> 1];
-      af[w] = (mb & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+      af[w] = __builtin_amdgcn_perm(x1, x0, (mb & 1) ? 0x07060302u : 0x05040100u);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) oacc[mb] = mfma16x16x32(as_bf16x8(af), as_bf16x8(pk[t]), oacc[mb]);

@@ -38,6 +38,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // leaves |error| <= 2^-16 |x|, and NT = 3 holds every bit of an fp32 x exactly (the
 // last remainder has at most 8 significant bits), so NT bf16 MFMA passes multiply an fp32
 // value at fp32 precision.
+// (With NT >= 3 the last remainder is already a bf16 value -- its low 16 bits are zero for
+// every x from 2^-110 up -- so it is taken by truncation, which is then exact.)
 template <int NT>
 __device__ __forceinline__ void split_terms(float x, uint32_t *t) {
   float r = x;
@@ -47,7 +49,7 @@ __device__ __forceinline__ void split_terms(float x, uint32_t *t) {
     t[i] = h >> 16;
     r -= __uint_as_float(h);
   }
-  t[NT - 1] = f32_to_bf16_rne(r);
+  t[NT - 1] = NT >= 3 ? __float_as_uint(r) >> 16 : f32_to_bf16_rne(r);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -194,11 +194,11 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(AttnArgs p) {
       half_bases<PAGED>(p, s_tbl, first_blk, b, g, t + 32, ce, hb, lx);
       tile_scores<D, kPrefillTerms>(tr, fa.q, sacc);
       load_k<D>(kp, hb, lx, n, j, tr);
-      tile_softmax_pv<D, kPrefillTerms>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
+      tile_softmax_pv<D, kPrefillTerms, true>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
       load_v<D>(vp, hb, lx, n, j, tr);
     }
     tile_scores<D, kPrefillTerms>(tr, fa.q, sacc);
-    tile_softmax_pv<D, kPrefillTerms>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
+    tile_softmax_pv<D, kPrefillTerms, true>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
   }
 
   prefill_store<D>(p, f, b, t0, n, j, rows, h, fa);
@@ -282,7 +282,7 @@ __global__ void __launch_bounds__(256) prefill_attn_shared_kernel(AttnArgs p) {
       }
       f32x4 sacc[2];
       tile_scores<D, kPrefillTerms>(tr, fa.q, sacc);
-      tile_softmax_pv<D, kPrefillTerms>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
+      tile_softmax_pv<D, kPrefillTerms, true>(p, tr, sacc, t, my_end, j, fa.m_run, fa.l_run, fa.oacc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_img[slot ^ 1][4 * wave + i][lane] = st[i];
       __syncthreads();
