@@ -49,7 +49,13 @@ __device__ __forceinline__ void half_bases(const AttnArgs &p, const int32_t *tbl
     int64_t blk;
     int slot;
     if constexpr (PAGED) {
-      blk = tbl[(hs >> p.block_shift) - first_blk];
+      // the same block id for the whole wave (t0 is the wave's): moved into a scalar register
+      // (an asm operand, which the compiler cannot fold back into the vector value), so that
+      // the address arithmetic of the tile runs on the scalar unit
+      const int bv = tbl[(hs >> p.block_shift) - first_blk];
+      int bs_;
+      asm("v_readfirstlane_b32 %0, %1" : "=s"(bs_) : "v"(bv));
+      blk = bs_;
       slot = hs & (p.block_size - 1);
     } else {
       blk = b;

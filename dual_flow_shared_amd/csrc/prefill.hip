@@ -149,7 +149,7 @@ __device__ __forceinline__ void prefill_store(const AttnArgs &p, int f, int b, i
 template <int D, bool PAGED, int F>
 __global__ void __launch_bounds__(256) prefill_attn_kernel(AttnArgs p) {
   __shared__ int32_t s_tbl[kMaxChunkBlocks];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // a scalar
   const int n = lane & 15, j = lane >> 4;
   const int h = blockIdx.x * (4 / F) + wave / F, f = wave % F, b = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;  // the longest tiles are dispatched first
@@ -225,7 +225,9 @@ __global__ void __launch_bounds__(256) prefill_attn_shared_kernel(AttnArgs p) {
   constexpr int D = 128;
   __shared__ int32_t s_tbl[kMaxChunkBlocks];
   __shared__ u32x4 s_img[2][16][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index in a scalar register: the head, the flow and every address base derived
+  // from it are then the wave's scalars, and their arithmetic runs on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
   // wave w: flow w % F of query head (4 / F) x + w / F
   const int h = blockIdx.x * (4 / F) + wave / F, f = wave % F, b = blockIdx.y;
