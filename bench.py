@@ -253,9 +253,16 @@ def hbm_flush(dfx, nbytes=512 << 20):
     return lambda: dfx.fill_bytes(buf, 0)
 
 
+# the headers a kernel source includes: a change in any of them is a change of the kernel
+KERNEL_HEADERS = {"attn_mfma.hip": ("attn_tiles.h", "common.h")}
+
+
 def source_sha(name):
-    path = os.path.join(ROOT, "dual_flow_shared_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of a kernel source together with the headers it includes."""
+    h = hashlib.sha256()
+    for f in (name,) + KERNEL_HEADERS.get(name, ()):
+        h.update(open(os.path.join(ROOT, "dual_flow_shared_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(kernel_file, workload):
