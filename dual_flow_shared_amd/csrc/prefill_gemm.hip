@@ -27,9 +27,11 @@ namespace dfx {
 // Work-group tile: FWAVES x RWAVES waves, each owning FW feature fragments (16 features each)
 // x RW row fragments (16 rows each; a multiple of 4, i.e. whole 64-row groups), with the
 // fragments of AHEAD k-steps in flight (LDS slots: AHEAD + 1).
-template <int FW_, int RW_, int FWAVES_, int RWAVES_, int AHEAD_ = 2>
+// REGBUF: fragments are read from LDS one k-step ahead into a second register set (AHEAD >= 3).
+template <int FW_, int RW_, int FWAVES_, int RWAVES_, int AHEAD_ = 2, bool REGBUF_ = false>
 struct DenseTile {
   static constexpr int FW = FW_, RW = RW_, FWAVES = FWAVES_, RWAVES = RWAVES_, Ahead = AHEAD_;
+  static constexpr bool RegBuf = REGBUF_;
   static constexpr int Slots = Ahead + 1;
   static constexpr int WFrags = FW * FWAVES;          // W fragments per k-step
   static constexpr int XFrags = RW * RWAVES;          // X fragments per k-step
@@ -40,12 +42,21 @@ struct DenseTile {
   static constexpr int Features = 16 * WFrags;        // output features per tile (gate/up: half gate)
   static_assert(Frags % Waves == 0 && RW % 4 == 0 && FW % 2 == 0, "tile shape");
   static_assert(Ahead >= 2 && (Ahead - 1) * Stage < 16, "loads outstanding at each wait (vmcnt bits 3:0)");
+  static_assert(!RegBuf || Ahead >= 3, "a register-buffered k-loop reads LDS one step ahead of the MFMAs");
 };
 // 256 features x 128 rows over 8 waves of 64 x 64 (two work-groups per CU)
 using TileNarrow = DenseTile<4, 4, 4, 2>;
 // 256 features x 256 rows over 8 waves of 128 x 64 (one work-group per CU, 96 KiB of LDS):
 // 1.5x the flops per byte staged through LDS, 1.37x per byte read from LDS
+#ifndef DFX_PREFILL_REGBUF
+#define DFX_PREFILL_REGBUF 1
+#endif
+#if DFX_PREFILL_REGBUF
+// the same with a register double buffer: four LDS slots (128 KiB)
+using TileWide = DenseTile<8, 4, 2, 4, 3, true>;
+#else
 using TileWide = DenseTile<8, 4, 2, 4>;
+#endif
 
 template <class T>
 __device__ __forceinline__ int dense_col_tiles(int N, bool swiglu) {
@@ -124,6 +135,43 @@ prefill_gemm_kernel(PrefillGemmArgs p) {
   constexpr int kWaitAll = 0 | (0x7 << 4) | (0xF << 8);
 #pragma unroll
   for (int st = 0; st < T::Ahead; ++st) dma(st, st);
+  if constexpr (T::RegBuf) {
+    // Fragments of k-step s + 1 are read from LDS while the MFMAs of k-step s run from the
+    // other register set. LDS holds four k-steps: s + 1 (being read), s + 2 and s + 3 (in
+    // flight), and the slot of s (already in registers), which the loads of s + 4 overwrite
+    // one step later. At the top of step s this thread's loads of s + 1 are done (those of
+    // s + 2 may be outstanding); the barrier makes s + 1 complete for every wave and shows
+    // that every wave has read k-step s's slot into registers.
+    constexpr int kWaitRead = (T::Ahead - 2) * kStage | (0x7 << 4) | (0xF << 8);
+    u32x4 wa[FW], xa[RW], wb[FW], xb[RW];
+    auto read = [&](int st, u32x4 (&wd)[FW], u32x4 (&xd)[RW]) {
+      const int sl = st % T::Slots;
+#pragma unroll
+      for (int c = 0; c < FW; ++c) wd[c] = lds[sl][wfrag[c]][lane];
+#pragma unroll
+      for (int nb = 0; nb < RW; ++nb) xd[nb] = lds[sl][kWFrags + RW * wr + nb][lane];
+    };
+    auto step = [&](int s, const u32x4 (&wc)[FW], const u32x4 (&xc)[RW], u32x4 (&wn)[FW], u32x4 (&xn)[RW]) {
+      __builtin_amdgcn_s_waitcnt(kWaitRead);
+      __builtin_amdgcn_s_barrier();
+      dma(s + T::Ahead, (s + T::Ahead) % T::Slots);
+      read(s + 1, wn, xn);  // past the last k-step: the re-read copy of it (never used)
+#pragma unroll
+      for (int c = 0; c < FW; ++c)
+#pragma unroll
+        for (int nb = 0; nb < RW; ++nb)
+          acc[c][nb] = mfma16x16x32(as_bf16x8(wc[c]), as_bf16x8(xc[nb]), acc[c][nb]);
+    };
+    __builtin_amdgcn_s_waitcnt(kWaitNext);  // k-step 0 is in LDS
+    __builtin_amdgcn_s_barrier();
+    read(0, wa, xa);
+    int s = 0;
+    for (; s + 1 < nks; s += 2) {
+      step(s, wa, xa, wb, xb);
+      step(s + 1, wb, xb, wa, xa);
+    }
+    if (s < nks) step(s, wa, xa, wb, xb);
+  } else {
   int slot = 0;
   for (int s = 0; s < nks; ++s) {
     __builtin_amdgcn_s_waitcnt(kWaitNext);
@@ -140,6 +188,7 @@ prefill_gemm_kernel(PrefillGemmArgs p) {
       for (int nb = 0; nb < RW; ++nb)
         acc[c][nb] = mfma16x16x32(as_bf16x8(wf[c]), as_bf16x8(xf[nb]), acc[c][nb]);
     slot = slot == T::Slots - 1 ? 0 : slot + 1;
+  }
   }
   __builtin_amdgcn_s_waitcnt(kWaitAll);  // no load into LDS in flight when the work-group ends
 
