@@ -51,9 +51,12 @@ using TileNarrow = DenseTile<4, 4, 4, 2>;
 #ifndef DFX_PREFILL_REGBUF
 #define DFX_PREFILL_REGBUF 1
 #endif
+#ifndef DFX_PREFILL_AHEAD
+#define DFX_PREFILL_AHEAD 3
+#endif
 #if DFX_PREFILL_REGBUF
 // the same with a register double buffer: four LDS slots (128 KiB)
-using TileWide = DenseTile<8, 4, 2, 4, 3, true>;
+using TileWide = DenseTile<8, 4, 2, 4, DFX_PREFILL_AHEAD, true>;
 #else
 using TileWide = DenseTile<8, 4, 2, 4>;
 #endif
