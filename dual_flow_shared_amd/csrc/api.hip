@@ -1000,7 +1000,7 @@ dfx_status run_prefill_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv,
   uint16_t *h2 = (uint16_t *)((char *)ob + p.o);
   uint16_t *inter = (uint16_t *)((char *)h2 + p.h2);
   dfx_status r;
-  if (norm_in && (r = hip_status(launch_rmsnorm(rows, H, x, w->attn_norm_gain, w->rms_eps, h1, s, 1), "rmsnorm launch")))
+  if (norm_in && (r = hip_status(launch_rmsnorm_rows(rows, H, x, w->attn_norm_gain, w->rms_eps, h1, s), "rmsnorm launch")))
     return r;
   if ((r = prefill_linear(rows, H, Nqkv, h1, w->w_qkv, qkv, nullptr, 0, s))) return r;
   PrefillGlueArgs ga{B, T, Nqkv, Hq, D, qkv, *kv, start};
@@ -1008,7 +1008,8 @@ dfx_status run_prefill_layer(const dfx_layer_weights *w, const dfx_kv_cache *kv,
   AttnArgs a = prefill_attn_args(kv, start, B, T, max_context, Hq, qkv, Nqkv, (float *)ob, 1, nullptr);
   if ((r = hip_status(launch_prefill_attn(a, s), "prefill attention launch"))) return r;
   if ((r = prefill_linear(rows, Hq * D, H, ob, w->w_o, x, x, 0, s))) return r;
-  if ((r = hip_status(launch_rmsnorm(rows, H, x, w->mlp_norm_gain, w->rms_eps, h2, s, 1), "rmsnorm launch"))) return r;
+  if ((r = hip_status(launch_rmsnorm_rows(rows, H, x, w->mlp_norm_gain, w->rms_eps, h2, s), "rmsnorm launch")))
+    return r;
   if ((r = prefill_linear(rows, H, 2 * I, h2, w->w_gate_up, inter, nullptr, 1, s))) return r;
   return prefill_linear(rows, I, H, inter, w->w_down, x, x, 0, s);
 }

@@ -285,6 +285,10 @@ hipError_t launch_prefill_gemm(const PrefillGemmArgs &a, bool swiglu, hipStream_
 // flows x batch); 0: row-major.
 hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
                           uint16_t *y, hipStream_t s, int packed_flows = 0);
+// The same norm for many rows (one wave per row; its own reduction order), y in the fragment
+// order of xpack_offset for one flow.
+hipError_t launch_rmsnorm_rows(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
+                               uint16_t *y, hipStream_t s);
 // x[f][b] = widen(embed_f[tokens[b]]) (token ids clamped to the table) and h1 = bf16(rmsnorm
 // (x) * gain) in the fragment order of xpack_offset, for flows f < n_flows.
 hipError_t launch_embed_norm(int32_t n_flows, int32_t batch, int32_t dim, const int32_t *tokens,

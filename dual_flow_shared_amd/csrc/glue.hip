@@ -66,6 +66,52 @@ hipError_t launch_embed_norm(int32_t n_flows, int32_t batch, int32_t dim, const 
   return hipGetLastError();
 }
 
+// RMSNorm of many rows (a prefill chunk): one wave per row, four rows per work-group. Lane l
+// holds the float4 slices l, l + 64, ... of the row (the first kRowSlices in registers; a
+// longer row's remaining slices are read twice), sums their squares in slice order, then the
+// wave butterfly; y = bf16(x * r * gain) in the fragment order of xpack_offset (one flow).
+// Every load of the resident slices is issued before the first wait; the gains (the same
+// small vector for every row, cached) are read after the reduction.
+constexpr int kRowSlices = 16;  // rows up to 4096 wide held in registers
+
+__global__ void __launch_bounds__(256) rmsnorm_rows_kernel(int32_t rows, int32_t dim, const float *x,
+                                                           const float *gain, float eps, uint16_t *y) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const f32x4 *xr = (const f32x4 *)(x + (int64_t)row * dim);
+  const f32x4 *g4 = (const f32x4 *)gain;
+  const int n4 = dim / 4;
+  f32x4 v[kRowSlices];
+#pragma unroll
+  for (int u = 0; u < kRowSlices; ++u)  // a slice past the row re-reads slice 0 (masked below)
+    v[u] = xr[lane + 64 * u < n4 ? lane + 64 * u : 0];
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < kRowSlices; ++u)
+    if (lane + 64 * u < n4) ss += v[u][0] * v[u][0] + v[u][1] * v[u][1] + v[u][2] * v[u][2] + v[u][3] * v[u][3];
+  for (int i = lane + 64 * kRowSlices; i < n4; i += 64) {
+    const f32x4 w = xr[i];
+    ss += w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3];
+  }
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float r = 1.0f / sqrtf(ss / (float)dim + eps);
+  auto store = [&](int i, const f32x4 &a, const f32x4 &g) {
+    *(u32x2 *)(y + xpack_offset(1, 0, row, 4 * i, dim)) =
+        u32x2{pack_bf16x2(a[0] * r * g[0], a[1] * r * g[1]), pack_bf16x2(a[2] * r * g[2], a[3] * r * g[3])};
+  };
+#pragma unroll
+  for (int u = 0; u < kRowSlices; ++u)
+    if (lane + 64 * u < n4) store(lane + 64 * u, v[u], g4[lane + 64 * u]);
+  for (int i = lane + 64 * kRowSlices; i < n4; i += 64) store(i, xr[i], g4[i]);
+}
+
+hipError_t launch_rmsnorm_rows(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
+                               uint16_t *y, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  rmsnorm_rows_kernel<<<(rows + 3) / 4, 256, 0, s>>>(rows, dim, x, gain, eps, y);
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(int32_t rows, int32_t dim, const float *x, const float *gain, float eps,
                           uint16_t *y, hipStream_t s, int packed_flows) {
   if (rows == 0) return hipSuccess;

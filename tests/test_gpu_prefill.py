@@ -413,6 +413,10 @@ def check_prefill_chain(c, x, st, samples, tag):
     # W_o, W_down on the 256 x 256 tile, Q/K/V on the 256 x 128 one)
     (2, 2048, 0, dict(hidden=4096, num_q_heads=32, num_kv_heads=8, head_dim=128, intermediate=14336, w_std=0.02),
      "benchmark shape"),
+    # rows wider than the norm's 4096 register-resident values (hidden 5120: each row's last
+    # 1024 values are read a second time)
+    (2, 40, 3, dict(hidden=5120, num_q_heads=8, num_kv_heads=2, head_dim=128, intermediate=512, w_std=0.02),
+     "wide rows"),
 ])
 def test_prefill_layer_chain(B, T, start, shape, tiles):
     c = gen.layer_case(720 + T % 97, batch=B, context=start + 1, capacity=start + T + 8, **shape)
