@@ -130,10 +130,14 @@ constexpr float kLazyMax = 8.f;
 
 // Online-softmax update for query row n (the lane holds 8 of the tile's 32 tokens) and
 // P.V accumulation into O^T, with P split into NT bf16 terms (one MFMA pass per term).
-// LAZY: the running max moves only by more than kLazyMax, the rescale of O is skipped when
-// no row of the wave moved it (a factor of exactly 1 for the rows that did not), and P is
-// 2^x from the hardware exponential (P below 2^-126, flushed to zero, is below the fp32
-// resolution of the row sum, which is >= 1).
+// LAZY (prefill, where the vector instructions bound the kernel): the running max moves only
+// by more than kLazyMax, the rescale of O is skipped when no row of the wave moved it (a
+// factor of exactly 1 for the rows that did not, so a row's arithmetic does not depend on
+// its wave-mates), a tile inside every row's range skips the per-token test, and P is 2^x
+// from the hardware exponential (P below 2^-126, flushed to zero, is below the fp32
+// resolution of the row sum, which is >= 1). Decode, a memory stream, keeps the eager form:
+// the lazy one saved 1% of the decode layer step, and its different rounding of the rows left
+// the small decode layer's median error at the edge of the ensemble parity bar.
 template <int D, int NT, bool LAZY = false>
 __device__ __forceinline__ void tile_softmax_pv(const AttnArgs &p, const TileRegs<D> &r,
                                                 const f32x4 *sacc, int t0, int end, int j,
@@ -141,8 +145,6 @@ __device__ __forceinline__ void tile_softmax_pv(const AttnArgs &p, const TileReg
   constexpr int VEC = D / 16;
   float sv[8];
   float mx = -INFINITY;
-  // (LAZY: a tile inside every row's range, i.e. all but the last of a causal row, skips the
-  // per-token test)
   const bool whole = LAZY && __all(t0 + 32 <= end);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
