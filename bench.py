@@ -199,10 +199,12 @@ def attention_workloads(dfx, gen, stream, reps, which=(1, 2, 3, 4)):
         for _ in range(min(n_rep, 64)):
             call(q2, a)
             call(None, None)
+        # calls of a few microseconds are timed in longer runs (at least ~4 ms each)
+        n = reps if pool_bytes * n_rep >= REPLICA_BYTES and pool_bytes >= (1 << 28) else max(reps, 200)
         t = {"dual": [], "single": []}
         for _ in range(2):
-            t["dual"].append(timed(lambda: call(q2, a), reps, stream))
-            t["single"].append(timed(lambda: call(None, None), reps, stream))
+            t["dual"].append(timed(lambda: call(q2, a), n, stream))
+            t["single"].append(timed(lambda: call(None, None), n, stream))
         dual, single = sum(t["dual"]) / 2, sum(t["single"]) / 2
         case_like = dict(Hkv=Hkv, D=D, Hq=Hq, B=B, kv_el=el, bs=16, paged=w["paged"])
         nbytes = attn_bytes(case_like, ctx_np, 2, el)
