@@ -130,12 +130,12 @@ constexpr float kLazyMax = 8.f;
 
 // Online-softmax update for query row n (the lane holds 8 of the tile's 32 tokens) and
 // P.V accumulation into O^T, with P split into NT bf16 terms (one MFMA pass per term).
-// LAZY (prefill, where the vector instructions bound the kernel): the running max moves only
-// by more than kLazyMax, the rescale of O is skipped when no row of the wave moved it (a
-// factor of exactly 1 for the rows that did not, so a row's arithmetic does not depend on
-// its wave-mates), a tile inside every row's range skips the per-token test, and P is 2^x
-// from the hardware exponential (P below 2^-126, flushed to zero, is below the fp32
-// resolution of the row sum, which is >= 1). Decode, a memory stream, keeps the eager form:
+// Both forms skip the rescale of O when no row of the wave moved its max (the factor is then
+// exactly 1 for every row, so skipping it changes no bit) and the per-token test on a tile
+// inside every row's range. LAZY (prefill, where the vector instructions bound the kernel):
+// the running max moves only by more than kLazyMax, so that most tiles need no rescale, and P
+// is 2^x from the hardware exponential (P below 2^-126, flushed to zero, is below the fp32
+// resolution of the row sum, which is >= 1). Decode, a memory stream, keeps the eager max:
 // the lazy one saved 1% of the decode layer step, and its different rounding of the rows left
 // the small decode layer's median error at the edge of the ensemble parity bar.
 template <int D, int NT, bool LAZY = false>
@@ -145,7 +145,7 @@ __device__ __forceinline__ void tile_softmax_pv(const AttnArgs &p, const TileReg
   constexpr int VEC = D / 16;
   float sv[8];
   float mx = -INFINITY;
-  const bool whole = LAZY && __all(t0 + 32 <= end);
+  const bool whole = __all(t0 + 32 <= end);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -201,7 +201,7 @@ __device__ __forceinline__ void tile_softmax_pv(const AttnArgs &p, const TileReg
   }
   l_run = l_run * alpha + psum;
   m_run = m_new;
-  if (!LAZY || __any(alpha != 1.f)) {
+  if (__any(alpha != 1.f)) {
 #pragma unroll
     for (int mb = 0; mb < VEC; ++mb) oacc[mb] *= alpha;
   }
