@@ -845,7 +845,7 @@ def bench_prefill(args):
 
 
 def host_cores():
-    """Host cores this process may run on (the machine's CPU share, not the machine's count)."""
+    """Host cores this process may run on (the CPU share this process is given, not the machine's count)."""
     try:
         return len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
