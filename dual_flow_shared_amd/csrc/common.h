@@ -16,6 +16,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// e^x as 2^(x log2 e) on the hardware exponential (v_exp_f32), for the softmax statistics
+// and the mixture of the output head: the product adds one rounding of the argument (about
+// |x| 2^-24 relative in the result, the size of the rounding of x itself) and results below
+// 2^-126 flush to zero; a few instructions instead of the library's range-reduced expf.
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
 // ---- bf16 <-> fp32 on raw bit patterns ----------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(256) grouped_linear_kernel(GemmArgs p) {
           if (cg + h < ng)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float e = expf(acc[h][nb][i] - mt[nb]);
+              const float e = exp_hw(acc[h][nb][i] - mt[nb]);
               sum += e;
               sq = fmaf(e, e, sq);
             }

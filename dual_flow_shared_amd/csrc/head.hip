@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(kMixThreads) mix_stats_kernel(MixArgs a) {
     for (int r = 0; r < kMixRounds; ++r)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float e = expf(v[r][j] - m);
+        const float e = exp_hw(v[r][j] - m);
         s += e;
         q = fmaf(e, e, q);
       }
@@ -182,10 +182,10 @@ __global__ void __launch_bounds__(kMixThreads) mix_apply_kernel(MixArgs a) {
 #pragma unroll
     for (int t = 0; t < kFoldBatch; ++t)
       if (live(k0, t)) {
-        const float e = expf(r[t][0] - m0);
+        const float e = exp_hw(r[t][0] - m0);
         s0 = fmaf(r[t][1], e, s0);
         q0 = fmaf(r[t][2], e * e, q0);
-        if (a.F == 2) s1 = fmaf(rs1[t], expf(r[t][3] - m1), s1);
+        if (a.F == 2) s1 = fmaf(rs1[t], exp_hw(r[t][3] - m1), s1);
       }
   };
   if (a.nstat <= batch_recs) {
@@ -220,10 +220,10 @@ __global__ void __launch_bounds__(kMixThreads) mix_apply_kernel(MixArgs a) {
     if (i >= n) continue;
     f32x4 p;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = w0 * expf(x0[q][j] - m0);
+    for (int j = 0; j < 4; ++j) p[j] = w0 * exp_hw(x0[q][j] - m0);
     if (a.F == 2) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = fmaf(w1, expf(x1[q][j] - m1), p[j]);
+      for (int j = 0; j < 4; ++j) p[j] = fmaf(w1, exp_hw(x1[q][j] - m1), p[j]);
     }
     if (a.p_mix) *(f32x4 *)(a.p_mix + (int64_t)b * a.V + lo + i) = p;
     f32x4 score = p;
