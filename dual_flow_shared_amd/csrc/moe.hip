@@ -32,8 +32,17 @@ __global__ void __launch_bounds__(1024) moe_route_kernel(MoeArgs a) {
   extern __shared__ u32x2 s_h[];  // the normed bf16 rows of both flows, 4 values per entry
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int F = a.F, E = a.E, H = a.H;
-  // Both flows' rows and the gain are loaded together (one memory round trip), then each
-  // row is normed.
+  // This wave's first (flow, expert) router row does not depend on the norm: it is loaded
+  // now, together with both flows' rows and the gain (one memory round trip), and each row is
+  // then normed.
+  constexpr int kPre = 8;  // router values per lane held: rows up to 512 kPre = 4096 wide
+  const bool pre = wave < F * E && H <= 512 * kPre;
+  u32x4 wpre[kPre];
+  {
+    const uint16_t *wr = a.w_router + (int64_t)(wave < F * E ? wave % E : 0) * H;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) wpre[i] = *(const u32x4 *)(wr + min(lane * 8 + 512 * i, H - 8));
+  }
   f32x4 v[2][kNormSlices], gg[kNormSlices];
 #pragma unroll
   for (int u = 0; u < kNormSlices; ++u) {
@@ -69,16 +78,22 @@ __global__ void __launch_bounds__(1024) moe_route_kernel(MoeArgs a) {
     const u32x2 *hr = s_h + f * (H / 4);
     const uint16_t *wr = a.w_router + (int64_t)e * H;
     float acc = 0.f;
-#pragma unroll 8
-    for (int k = lane * 8; k < H; k += 512) {
+    auto dot8 = [&](int k, const u32x4 &wv) {
       const u32x2 h0 = hr[k / 4], h1 = hr[k / 4 + 1];
-      const u32x4 wv = *(const u32x4 *)(wr + k);
       const uint32_t hv[4] = {h0[0], h0[1], h1[0], h1[1]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc = fmaf(bf16_lo(hv[i]), bf16_lo(wv[i]), acc);
         acc = fmaf(bf16_hi(hv[i]), bf16_hi(wv[i]), acc);
       }
+    };
+    if (d == wave && pre) {  // the prefetched row, in the same k order
+#pragma unroll
+      for (int i = 0; i < kPre; ++i)
+        if (lane * 8 + 512 * i < H) dot8(lane * 8 + 512 * i, wpre[i]);
+    } else {
+#pragma unroll 8
+      for (int k = lane * 8; k < H; k += 512) dot8(k, *(const u32x4 *)(wr + k));
     }
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
     if (lane == 0) lg[f][e] = acc;
@@ -199,28 +214,49 @@ __global__ void __launch_bounds__(256) moe_gather_kernel(MoeArgs a) {
 
 // One thread per 4 columns of one sequence (both flows): each flow's experts in ranking
 // order, weight times the expert's output (its K-split tiles summed in split order), then the
-// auxiliary's c coupling and the residual add, in place.
+// auxiliary's c coupling and the residual add, in place. The experts are taken kCombineJ at a
+// time per flow: their ids, positions and weights in one round trip, then (one K split) their
+// output tiles and the residual rows in another.
+constexpr int kCombineJ = 4;
+
 __global__ void __launch_bounds__(256) moe_combine_kernel(MoeArgs a) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int n4 = a.H / 4;
   if (t >= (int64_t)a.B * n4) return;
   const int col = (int)(t % n4) * 4, b = (int)(t / n4);
   const int rpg = 64 / a.F;
-  f32x4 m[2];
-  for (int f = 0; f < a.F; ++f) {
-    const int k = f == 0 ? a.k1 : a.k2;
-    const int64_t o = ((int64_t)f * a.B + b) * kMoeMaxK;
-    f32x4 acc{0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int e = min(max(a.ids[o + j], 0), a.E - 1);
-      const int r = min(max(a.pos[o + j], 0), a.B - 1);
-      const float w = a.wts[o + j];
-      const f32x4 y = sum_split_tiles(a.tiles + (int64_t)e * a.ksplit * a.max_groups * 64 * a.H, a.ksplit,
-                                      a.max_groups, a.H, r / rpg, f * rpg + r % rpg, col);
+  const int kf[2] = {a.k1, a.F == 2 ? a.k2 : 0};
+  const int kmax = max(kf[0], kf[1]);
+  f32x4 m[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int j0 = 0; j0 < kmax; j0 += kCombineJ) {
+    int e[2][kCombineJ], r[2][kCombineJ];
+    float w[2][kCombineJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, y[i], acc[i]);
-    }
-    m[f] = acc;
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int u = 0; u < kCombineJ; ++u) {  // entries past a flow's fan-out re-read its first
+        const int64_t o = ((int64_t)min(f, a.F - 1) * a.B + b) * kMoeMaxK + (j0 + u < kf[f] ? j0 + u : 0);
+        e[f][u] = min(max(a.ids[o], 0), a.E - 1);
+        r[f][u] = min(max(a.pos[o], 0), a.B - 1);
+        w[f][u] = a.wts[o];
+      }
+    f32x4 y[2][kCombineJ];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int u = 0; u < kCombineJ; ++u) {
+        const float *tiles = a.tiles + (int64_t)e[f][u] * a.ksplit * a.max_groups * 64 * a.H;
+        const int ff = min(f, a.F - 1), grp = r[f][u] / rpg, q = ff * rpg + r[f][u] % rpg;
+        y[f][u] = a.ksplit == 1 ? *(const f32x4 *)(tiles + ((int64_t)grp * 64 + q) * a.H + col)
+                                : sum_split_tiles(tiles, a.ksplit, a.max_groups, a.H, grp, q, col);
+      }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int u = 0; u < kCombineJ; ++u)
+        if (j0 + u < kf[f])
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m[f][i] = fmaf(w[f][u], y[f][u][i], m[f][i]);
   }
   if (a.F == 2 && a.couple_c) {
     const f32x4 c = *(const f32x4 *)(a.couple_c + col);
