@@ -55,6 +55,9 @@ def parse():
                    help="skip timing the four attention-only workloads in the layer line")
     p.add_argument("--no-split-sweep", action="store_true",
                    help="skip timing dual and single flow at each split count (own-best-split ratio)")
+    p.add_argument("--library-gemms", action="store_true",
+                   help="'prefill' workload: also time torch's bf16 linear (the ROCm BLAS library) on the "
+                        "layer's four projection shapes, for context")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run the plain copy kernel on BYTES (5 launches): the reference "
                         "for scaling hardware traffic counters")
@@ -841,6 +844,17 @@ def bench_prefill(args):
             "attention": {"ms": round(attn_ms, 4), "tflops": round(atf, 1), "frac_of_bf16_peak": round(atf / 2500.0, 4)},
             "dual_attention": {"ms": round(dual_ms, 4), "tflops": round(2 * attn_flops / (dual_ms * 1e-3) / 1e12, 1),
                                "dual_over_single": round(dual_ms / attn_ms, 3)}}
+    if args.library_gemms:
+        # context only: the vendor library's bf16 GEMM (bf16 out, no residual) on the same shapes
+        xa, xi = randn(rows, H, std=1.0), randn(rows, I, std=1.0)
+        lib = {}
+        for name, (a_, w_) in {"qkv": (xa, rm["w_qkv"]), "o": (xa, rm["w_o"]), "gate_up": (xa, rm["w_gate_up"]),
+                               "down": (xi, rm["w_down"])}.items():
+            f = lambda: torch.nn.functional.linear(a_, w_)
+            f()
+            torch.cuda.synchronize()
+            lib[name] = round(timed(f, args.steps, stream) * 1e3, 1)
+        line["library_gemms_us"] = lib
     print(json.dumps(line))
 
 

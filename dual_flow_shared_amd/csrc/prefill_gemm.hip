@@ -4,14 +4,19 @@
 // Operands are the grouped linear's packed layouts: W [K/32][N/16][64 lanes][8] (the A
 // fragment of a 16x16x32 bf16 MFMA for 16 output features and one 32-wide k-step, 1 KiB
 // contiguous) and X [M/64][K/32][4][64 lanes][8] (the B fragment of 16 rows likewise).
-// Two work-group tiles, each putting two waves on every SIMD (one can issue MFMAs while the
-// other waits): 256 output features x 128 rows as 4 x 2 waves of 64 features x 64 rows (two
-// work-groups per CU), and 256 x 256 as 2 x 4 waves of 128 x 64 (one per CU). Per k-step a
-// work-group stages the fragments it needs (16 of W and 8 or 16 of X, 1 KiB each) in LDS,
-// each loaded once from global memory straight into LDS (global_load_lds, no register
-// staging) two k-steps ahead; every wave reads its fragments from LDS and issues 16 or 32
-// MFMAs. LDS holds three k-steps: the one being read and the two in flight (one barrier per
-// k-step).
+// Per k-step a work-group stages the fragments it needs (1 KiB each) in LDS, each loaded once
+// from global memory straight into LDS (global_load_lds, no register staging) k-steps ahead;
+// every wave reads its fragments from LDS and issues its MFMAs; one barrier per k-step.
+// Work-group tiles:
+// - 256 output features x 256 rows as 2 x 2 waves of 128 x 128 (and 192 x 256 as 2 x 2 waves of
+//   96 x 128), one wave per SIMD. Per k-step a wave reads 16 (14) fragments from LDS for 64 (48)
+//   MFMAs: a third fewer LDS reads per MFMA than 8 waves of 128 x 64, which matters because the
+//   chip runs at a power-limited clock under matrix load. The accumulators fill (three quarters
+//   of) the 256 matrix registers; the k-loop is register-buffered (fragments of k-step s + 1 are
+//   read while the MFMAs of s run) with the loads spread between the MFMAs, since no second wave
+//   on the SIMD covers them.
+// - 256 x 128 as 4 x 2 waves of 64 x 64, two work-groups per CU, for grids that would end in a
+//   partly filled round of the larger tiles.
 //
 // Work-group i runs on XCD i % 8; all row tiles of one feature tile go to one XCD back to back,
 // so the tile's weights are fetched from HBM about once and re-read from that XCD's L2.
@@ -32,6 +37,8 @@ template <int FW_, int RW_, int FWAVES_, int RWAVES_, int AHEAD_ = 2, bool REGBU
 struct DenseTile {
   static constexpr int FW = FW_, RW = RW_, FWAVES = FWAVES_, RWAVES = RWAVES_, Ahead = AHEAD_;
   static constexpr bool RegBuf = REGBUF_;
+  // waves of the work-group per SIMD: the register budget (512 per lane over this count)
+  static constexpr int WavesPerSimd = (FWAVES_ * RWAVES_ + 3) / 4;
   static constexpr int Slots = Ahead + 1;
   static constexpr int WFrags = FW * FWAVES;          // W fragments per k-step
   static constexpr int XFrags = RW * RWAVES;          // X fragments per k-step
@@ -41,25 +48,27 @@ struct DenseTile {
   static constexpr int Groups = XFrags / 4;           // 64-row groups per row tile
   static constexpr int Features = 16 * WFrags;        // output features per tile (gate/up: half gate)
   static_assert(Frags % Waves == 0 && RW % 4 == 0 && FW % 2 == 0, "tile shape");
-  static_assert(Ahead >= 2 && (Ahead - 1) * Stage < 16, "loads outstanding at each wait (vmcnt bits 3:0)");
+  static_assert(Ahead >= 2 && (Ahead - 1) * Stage < 64, "loads outstanding at each wait (6-bit vmcnt)");
   static_assert(!RegBuf || Ahead >= 3, "a register-buffered k-loop reads LDS one step ahead of the MFMAs");
+  static_assert(!RegBuf || WavesPerSimd == 1, "the register-buffered k-loop keeps its accumulators in place by asm");
 };
 // 256 features x 128 rows over 8 waves of 64 x 64 (two work-groups per CU)
 using TileNarrow = DenseTile<4, 4, 4, 2>;
-// 256 features x 256 rows over 8 waves of 128 x 64 (one work-group per CU, 96 KiB of LDS):
-// 1.5x the flops per byte staged through LDS, 1.37x per byte read from LDS
-#ifndef DFX_PREFILL_REGBUF
-#define DFX_PREFILL_REGBUF 1
-#endif
-#ifndef DFX_PREFILL_AHEAD
-#define DFX_PREFILL_AHEAD 3
-#endif
-#if DFX_PREFILL_REGBUF
-// the same with a register double buffer: four LDS slots (128 KiB)
-using TileWide = DenseTile<8, 4, 2, 4, DFX_PREFILL_AHEAD, true>;
-#else
-using TileWide = DenseTile<8, 4, 2, 4>;
-#endif
+// 256 (192) features x 256 rows over 4 waves of 128 (96) x 128: one wave per SIMD, four LDS
+// slots (128 / 112 KiB)
+using TileQuad = DenseTile<8, 8, 2, 2, 3, true>;
+using TileQuad6 = DenseTile<6, 8, 2, 2, 3, true>;
+
+// s_waitcnt immediate on gfx9: vmcnt bits 3:0 and 15:14, expcnt and lgkmcnt at their no-wait maxima
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// acc += W.X^T with the accumulator tied in place to one matrix-register quadruple (with 256
+// accumulator registers the compiler's own allocation rotates them through copies). Only for
+// k-loops whose operands come straight from LDS loads: the compiler does not see the asm as a
+// matrix instruction, so the caller waits out its latency before anything reads the accumulators.
+__device__ __forceinline__ void mfma_agpr(f32x4 &acc, const u32x4 &a, const u32x4 &b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
 
 template <class T>
 __device__ __forceinline__ int dense_col_tiles(int N, bool swiglu) {
@@ -67,11 +76,12 @@ __device__ __forceinline__ int dense_col_tiles(int N, bool swiglu) {
 }
 
 template <class T, bool SWIGLU>
-__global__ void __launch_bounds__(64 * T::Waves) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64 * T::Waves) __attribute__((amdgpu_waves_per_eu(T::WavesPerSimd)))
 prefill_gemm_kernel(PrefillGemmArgs p) {
   constexpr int FW = T::FW, RW = T::RW, kWFrags = T::WFrags, kStage = T::Stage;
   __shared__ u32x4 lds[T::Slots][T::Frags][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index in a scalar register, so that the per-wave fragment strides and offsets are too
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
   const int wr = wave / T::FWAVES, wc = wave % T::FWAVES;  // row wave, feature wave
   const int M = p.M, K = p.K, N = p.N;
@@ -133,9 +143,8 @@ prefill_gemm_kernel(PrefillGemmArgs p) {
       __builtin_amdgcn_global_load_lds((const void *)(src[r] + sc * sstep[r]),
                                        (lds_void *)&lds[slot][wave + T::Waves * r][0], 16, 0, 0);
   };
-  // s_waitcnt immediates (vmcnt in bits 3:0, expcnt and lgkmcnt fields at their no-wait maxima)
-  constexpr int kWaitNext = (T::Ahead - 1) * kStage | (0x7 << 4) | (0xF << 8);
-  constexpr int kWaitAll = 0 | (0x7 << 4) | (0xF << 8);
+  constexpr int kWaitNext = waitcnt_vm((T::Ahead - 1) * kStage);
+  constexpr int kWaitAll = waitcnt_vm(0);
 #pragma unroll
   for (int st = 0; st < T::Ahead; ++st) dma(st, st);
   if constexpr (T::RegBuf) {
@@ -145,35 +154,60 @@ prefill_gemm_kernel(PrefillGemmArgs p) {
     // one step later. At the top of step s this thread's loads of s + 1 are done (those of
     // s + 2 may be outstanding); the barrier makes s + 1 complete for every wave and shows
     // that every wave has read k-step s's slot into registers.
-    constexpr int kWaitRead = (T::Ahead - 2) * kStage | (0x7 << 4) | (0xF << 8);
+    // One wave per SIMD: nothing else covers this wave's loads, so they are spread over its
+    // MFMAs (an LDS read of k-step s + 1 after every 3, a global-to-LDS load of k-step s + Ahead
+    // after every 8 or 6), each held in place between empty asm memory fences.
+    constexpr int kWaitRead = waitcnt_vm((T::Ahead - 2) * kStage);
+    constexpr int kReadEvery = 3, kDmaEvery = FW * RW / kStage;
+    static_assert(kReadEvery * (FW + RW) <= FW * RW && kDmaEvery >= 1, "interleave pattern");
     u32x4 wa[FW], xa[RW], wb[FW], xb[RW];
-    auto read = [&](int st, u32x4 (&wd)[FW], u32x4 (&xd)[RW]) {
-      const int sl = st % T::Slots;
-#pragma unroll
-      for (int c = 0; c < FW; ++c) wd[c] = lds[sl][wfrag[c]][lane];
-#pragma unroll
-      for (int nb = 0; nb < RW; ++nb) xd[nb] = lds[sl][kWFrags + RW * wr + nb][lane];
-    };
     auto step = [&](int s, const u32x4 (&wc)[FW], const u32x4 (&xc)[RW], u32x4 (&wn)[FW], u32x4 (&xn)[RW]) {
       __builtin_amdgcn_s_waitcnt(kWaitRead);
       __builtin_amdgcn_s_barrier();
-      dma(s + T::Ahead, (s + T::Ahead) % T::Slots);
-      read(s + 1, wn, xn);  // past the last k-step: the re-read copy of it (never used)
+      const int sl = (s + 1) % T::Slots;  // past the last k-step: the re-read copy of it (never used)
+      const int sc = min(s + T::Ahead, nks - 1), dslot = (s + T::Ahead) % T::Slots;
 #pragma unroll
       for (int c = 0; c < FW; ++c)
 #pragma unroll
-        for (int nb = 0; nb < RW; ++nb)
-          acc[c][nb] = mfma16x16x32(as_bf16x8(wc[c]), as_bf16x8(xc[nb]), acc[c][nb]);
+        for (int nb = 0; nb < RW; ++nb) {
+          mfma_agpr(acc[c][nb], wc[c], xc[nb]);
+          const int i = c * RW + nb;
+          if (i % kReadEvery == kReadEvery - 1 && i / kReadEvery < FW + RW) {
+            const int q = i / kReadEvery;
+            asm volatile("" ::: "memory");
+            if (q < FW) wn[q] = lds[sl][wfrag[q]][lane];
+            else xn[q - FW] = lds[sl][kWFrags + RW * wr + q - FW][lane];
+            asm volatile("" ::: "memory");
+          }
+          if (i % kDmaEvery == kDmaEvery - 1 && i / kDmaEvery < kStage) {
+            const int r = i / kDmaEvery;
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_global_load_lds((const void *)(src[r] + sc * sstep[r]),
+                                             (lds_void *)&lds[dslot][wave + T::Waves * r][0], 16, 0, 0);
+            asm volatile("" ::: "memory");
+          }
+        }
     };
     __builtin_amdgcn_s_waitcnt(kWaitNext);  // k-step 0 is in LDS
     __builtin_amdgcn_s_barrier();
-    read(0, wa, xa);
+#pragma unroll
+    for (int c = 0; c < FW; ++c) wa[c] = lds[0][wfrag[c]][lane];
+#pragma unroll
+    for (int nb = 0; nb < RW; ++nb) xa[nb] = lds[0][kWFrags + RW * wr + nb][lane];
     int s = 0;
     for (; s + 1 < nks; s += 2) {
       step(s, wa, xa, wb, xb);
       step(s + 1, wb, xb, wa, xa);
     }
     if (s < nks) step(s, wa, xa, wb, xb);
+    // the last MFMAs' results are ready 24 wait states later (a 16-pass one needs 19); every
+    // accumulator then passes through an empty asm ordered after the wait, so that no read of
+    // it can be scheduled earlier
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < FW; ++c)
+#pragma unroll
+      for (int nb = 0; nb < RW; ++nb) asm volatile("" : "+a"(acc[c][nb]));
   } else {
   int slot = 0;
   for (int s = 0; s < nks; ++s) {
@@ -217,20 +251,44 @@ prefill_gemm_kernel(PrefillGemmArgs p) {
       }
     }
   } else {
+    // The residual may alias the output, so the compiler keeps each residual load after every
+    // earlier store; loaded one tile at a time, every load is a memory round trip of its own.
+    // Every element is read and written by its lane alone, so the residual tiles of two feature
+    // fragments are loaded together (rows past M clamped: loaded, never stored), then stored.
+    constexpr int kBatch = 2;
+    const bool rows_full = 16 * (T::XFrags * rt + RW * wr + RW) <= M;  // uniform for the wave
 #pragma unroll
-    for (int c = 0; c < FW; ++c) {
-      const int g = ct * kWFrags + FW * wc + c;
-      if (g >= ng) continue;
-      const int col = 16 * g + 4 * j;
+    for (int c0 = 0; c0 < FW; c0 += kBatch) {
+      f32x4 res[kBatch][RW];
+      if (p.residual) {
 #pragma unroll
-      for (int nb = 0; nb < RW; ++nb) {
-        const int row = row0 + 16 * nb;
-        if (row >= M) continue;
-        const int64_t o = (int64_t)row * N + col;
-        f32x4 v = acc[c][nb];
-        if (p.residual) v += *(const f32x4 *)(p.residual + o);
-        *(f32x4 *)((float *)p.y + o) = v;
+        for (int b = 0; b < kBatch; ++b) {
+          const int g = min(ct * kWFrags + FW * wc + c0 + b, ng - 1);
+#pragma unroll
+          for (int nb = 0; nb < RW; ++nb)
+            res[b][nb] = *(const f32x4 *)(p.residual + (int64_t)min(row0 + 16 * nb, M - 1) * N + 16 * g + 4 * j);
+        }
       }
+      // a wave whose rows are all below M stores without per-row branches (the compiler waits
+      // for every load at each divergent store otherwise); only the last row tile checks rows
+      auto store = [&](bool check_rows) {
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const int g = ct * kWFrags + FW * wc + c0 + b;
+          if (g >= ng) continue;
+          const int col = 16 * g + 4 * j;
+#pragma unroll
+          for (int nb = 0; nb < RW; ++nb) {
+            const int row = row0 + 16 * nb;
+            if (check_rows && row >= M) continue;
+            f32x4 v = acc[c0 + b][nb];
+            if (p.residual) v += res[b][nb];
+            *(f32x4 *)((float *)p.y + (int64_t)row * N + col) = v;
+          }
+        }
+      };
+      if (rows_full) store(false);
+      else store(true);
     }
   }
 }
@@ -260,11 +318,11 @@ static int64_t dense_grid(const PrefillGemmArgs &a, bool swiglu) {
 
 hipError_t launch_prefill_gemm(const PrefillGemmArgs &a, bool swiglu, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  // The wide tile runs one work-group per CU. Where its grid ends in a partly filled round of
-  // 256 work-groups (Q/K/V at 4096 rows: 384), the narrow tile was measured faster (231 vs
-  // 243 us); on whole rounds the wide one is (gate/up 876 vs 886 us, W_o and W_down 392 vs
-  // 422 us on average, 4096 rows).
-  if (dense_grid<TileWide>(a, swiglu) % 256 == 0) return launch_dense<TileWide>(a, swiglu, s);
+  // The four-wave tiles run one work-group per CU, so they are taken where their grid fills
+  // whole rounds of 256 work-groups (at 4096 rows: gate/up, W_o and W_down on 256 features,
+  // Q/K/V's 6144 on 192); elsewhere the narrow tile, two work-groups per CU.
+  if (dense_grid<TileQuad>(a, swiglu) % 256 == 0) return launch_dense<TileQuad>(a, swiglu, s);
+  if (!swiglu && dense_grid<TileQuad6>(a, swiglu) % 256 == 0) return launch_dense<TileQuad6>(a, swiglu, s);
   return launch_dense<TileNarrow>(a, swiglu, s);
 }
 

@@ -206,11 +206,14 @@ def kv_step_bound(x, c):
 
 @pytest.mark.parametrize("B,T,shape", [
     # the one-layer workload's shape at the prefill benchmark's chunk: the 256 x 256 projection
-    # tile on gate/up, W_o and W_down, the 256 x 128 one on Q/K/V
+    # tile on gate/up, W_o and W_down, the 192 x 256 one on Q/K/V
     (2, 2048, dict(hidden=4096, num_q_heads=32, num_kv_heads=8, head_dim=128, intermediate=14336, w_std=0.02)),
     # the 256 x 256 tile on every projection, with a ragged last row group (7990 rows) and ragged
     # feature tiles (W_o and W_down 288 features, gate/up 1504; down K = 47 k-steps)
     (2, 3995, dict(hidden=288, num_q_heads=4, num_kv_heads=2, head_dim=64, intermediate=1504, w_std=0.05)),
+    # the 192 x 256 tile on W_o and W_down with a ragged last feature tile (5984 = 31 x 192 + 32)
+    # and a ragged last row group (3980 rows); gate/up on 256 x 256, Q/K/V on 256 x 128
+    (2, 1990, dict(hidden=5984, num_q_heads=8, num_kv_heads=2, head_dim=128, intermediate=1504, w_std=0.02)),
 ])
 def test_prefill_layer_long_chunk_sampled_rows(B, T, shape):
     """A long chunk from position 0: sampled output rows against the oracle's composition for
@@ -410,7 +413,7 @@ def check_prefill_chain(c, x, st, samples, tag):
     (2, 3995, 0, dict(hidden=288, num_q_heads=4, num_kv_heads=2, head_dim=64, intermediate=1504, w_std=0.05),
      "256 x 256, ragged"),
     # the prefill benchmark's shape: 2 x 2048 rows, hidden 4096, 32/8 x 128, SwiGLU 14336 (gate/up,
-    # W_o, W_down on the 256 x 256 tile, Q/K/V on the 256 x 128 one)
+    # W_o, W_down on the 256 x 256 tile, Q/K/V on the 192 x 256 one)
     (2, 2048, 0, dict(hidden=4096, num_q_heads=32, num_kv_heads=8, head_dim=128, intermediate=14336, w_std=0.02),
      "benchmark shape"),
     # rows wider than the norm's 4096 register-resident values (hidden 5120: each row's last
