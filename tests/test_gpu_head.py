@@ -110,6 +110,9 @@ def check_mixture(logits, tok, alpha, pm, noise=None):
 
 
 @pytest.mark.parametrize("F", [2, 1])
+# (batch, hidden, vocab): the first two project in one K split (output-head mode, two 128-logit
+# tiles per work-group) over an odd tile count (9, 157), so the last work-group's second tile lies
+# past the vocabulary; the third splits K (separate statistics pass)
 @pytest.mark.parametrize("shape", [(3, 256, 1040), (40, 512, 20016), (3, 4096, 1040)])
 def test_head_chain_small(F, shape):
     B, H, V = shape
