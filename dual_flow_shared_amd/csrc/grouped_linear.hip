@@ -23,7 +23,7 @@
 // Output-head mode (one split, fp32 logits): after storing its tile a work-group also writes
 // the softmax statistics of every row over its 128 outputs (max, sum of e^(l - max), and for
 // the primary sum of e^(2 (l - max))), which the mixture's apply pass combines; the logits are
-// stored non-temporally.
+// stored non-temporally. Its work-groups hold two 128-output tiles on 8 waves (TW below).
 #include "common.h"
 
 namespace dfx {
