@@ -214,6 +214,9 @@ def kv_step_bound(x, c):
     # the 192 x 256 tile on W_o and W_down with a ragged last feature tile (5984 = 31 x 192 + 32)
     # and a ragged last row group (3980 rows); gate/up on 256 x 256, Q/K/V on 256 x 128
     (2, 1990, dict(hidden=5984, num_q_heads=8, num_kv_heads=2, head_dim=128, intermediate=1504, w_std=0.02)),
+    # hidden 64: Q/K/V's and gate/up's K is 2 k-steps, fewer than the 256 x 256 tile keeps in
+    # flight (its prologue re-reads the last one); every projection on the 256 x 256 tile
+    (2, 3995, dict(hidden=64, num_q_heads=4, num_kv_heads=1, head_dim=64, intermediate=1504, w_std=0.05)),
 ])
 def test_prefill_layer_long_chunk_sampled_rows(B, T, shape):
     """A long chunk from position 0: sampled output rows against the oracle's composition for
