@@ -110,10 +110,10 @@ def check_mixture(logits, tok, alpha, pm, noise=None):
 
 
 @pytest.mark.parametrize("F", [2, 1])
-# (batch, hidden, vocab): the first two project in one K split (output-head mode, two 128-logit
-# tiles per work-group) over an odd tile count (9, 157), so the last work-group's second tile lies
-# past the vocabulary; the third splits K (separate statistics pass)
-@pytest.mark.parametrize("shape", [(3, 256, 1040), (40, 512, 20016), (3, 4096, 1040)])
+# (batch, hidden, vocab): the first three project in one K split (output-head mode, two 128-logit
+# tiles per work-group) over an odd tile count (9, 157, 1), so the last work-group's second tile
+# lies past the vocabulary; the fourth splits K (separate statistics pass)
+@pytest.mark.parametrize("shape", [(3, 256, 1040), (40, 512, 20016), (5, 256, 48), (3, 4096, 1040)])
 def test_head_chain_small(F, shape):
     B, H, V = shape
     c = gen.head_case(900 + B, 2, B, H, V, w_std=0.4)
